@@ -1,0 +1,234 @@
+/*
+ * Q2_K CPU oracle — TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the slow, obviously-correct definition that the HIP path is
+ * checked against. Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load it. The product library never links, calls or
+ * falls back to it, and the two share no code, header, table or helper.
+ *
+ * Source of every rule below: the docs.rs source page of mlx-native 0.10.8,
+ * tests/deepseek_q2_k.rs ("GGML Q2_K loading and Metal execution proofs for
+ * DeepSeek-V4 Q2_K_S"). Functions cite the item on that page they restate:
+ *   - constants QK_K / BLOCK_BYTES and fn block: the 84-byte super-block layout
+ *     (16 scale bytes, 64 code bytes, f16 d, f16 dmin);
+ *   - fn reference_dequant: decode order and arithmetic;
+ *   - fn cpu_dot: the page's f32 dot product;
+ *   - test q2_k_host_decode_rejects_malformed_buffers: length checks;
+ *   - test q2_k_embedding_gather_matches_canonical_rows_and_rejects_bad_ids:
+ *     gather semantics and the id == vocab rejection;
+ *   - fn run_dense: y[m, n] = sum_k x[m, k] * w[n, k], rows of w made of
+ *     K/256 consecutive blocks.
+ *
+ * Precision: the page decodes in f32 (d and dmin widened to f32, products and
+ * the final subtraction in f32), so dequantization is done in f32 here too.
+ * Matmul accumulates in f64 (every f32*f32 product is exact in f64). Build with
+ * -O2 -ffp-contract=off and without fast-math so each f32 operation is one
+ * IEEE-754 operation.
+ *
+ * Parity pins (the tests that tie this file to the page, not to itself):
+ * hand-decoded elements of the page's block(5) fixture, an exhaustive f16
+ * decode check against numpy, format invariants (all-zero codes, all-three
+ * codes, zero scale, zero min, single-bit perturbations), the closed-form
+ * element map, brute-force exact-rational matmuls, and torch's bf16 rounding.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define QK_K 256
+#define BLOCK_BYTES 84
+
+/* IEEE-754 binary16 -> binary32, written from the format definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. Exponent 0 is zero
+ * or subnormal (fraction * 2^-24); exponent 31 is Inf (fraction 0) or NaN.
+ * The page stores d and dmin as little-endian f16 at bytes 80..83 of a block. */
+float oracle_f16_to_f32(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, -24);
+    } else if (expo == 31) {
+        v = frac ? (double)NAN : (double)INFINITY;
+    } else {
+        v = ldexp((double)(1024 + frac), expo - 25);
+    }
+    return (float)(sign ? -v : v);
+}
+
+static float block_d(const uint8_t *blk) {
+    return oracle_f16_to_f32((uint16_t)(blk[80] | (blk[81] << 8)));
+}
+
+static float block_dmin(const uint8_t *blk) {
+    return oracle_f16_to_f32((uint16_t)(blk[82] | (blk[83] << 8)));
+}
+
+/* fn reference_dequant: two halves of 128 weights; within a half the four
+ * 2-bit positions of each code byte (shift 0, 2, 4, 6); within a position two
+ * 16-byte segments; each (half, shift, segment) consumes the next scale byte,
+ * whose low nibble scales the codes and whose high nibble scales dmin.
+ * Outputs are appended in that order, 16 per segment. */
+void oracle_dequant_block(const uint8_t *blk, float *out) {
+    const uint8_t *scales = blk;
+    const uint8_t *qs = blk + 16;
+    const float d = block_d(blk);
+    const float dmin = block_dmin(blk);
+    int scale_index = 0;
+    int o = 0;
+    for (int half = 0; half < 2; ++half) {
+        for (int shift = 0; shift <= 6; shift += 2) {
+            for (int segment = 0; segment < 2; ++segment) {
+                const uint8_t s = scales[scale_index++];
+                const float dl = d * (float)(s & 0x0f);
+                const float ml = dmin * (float)(s >> 4);
+                const uint8_t *q = qs + half * 32 + segment * 16;
+                for (int lane = 0; lane < 16; ++lane) {
+                    const int code = (q[lane] >> shift) & 3;
+                    out[o++] = dl * (float)code - ml;
+                }
+            }
+        }
+    }
+}
+
+/* The same decode, addressed per element instead of in loop order: element e
+ * lies in half e/128, at 2-bit position (e/32)%4, segment (e/16)%2, lane e%16.
+ * So its scale byte is number e/16 and its code byte is 32*(e/128) + e%32.
+ * Kept as an independent cross-check of the loop-order decode. */
+float oracle_dequant_element(const uint8_t *blk, int e) {
+    const uint8_t s = blk[e >> 4];
+    const int byte = 32 * (e >> 7) + (e & 31);
+    const int shift = 2 * ((e >> 5) & 3);
+    const int code = (blk[16 + byte] >> shift) & 3;
+    const float dl = block_d(blk) * (float)(s & 0x0f);
+    const float ml = block_dmin(blk) * (float)(s >> 4);
+    return dl * (float)code - ml;
+}
+
+/* test q2_k_host_decode_rejects_malformed_buffers: a byte length that is not a
+ * whole number of 84-byte blocks, or an output that is not exactly 256 values
+ * per block, is an error. Returns 0 on success, -1 on a rejected length. */
+int oracle_dequantize(const uint8_t *bytes, size_t nbytes, float *out, size_t out_elems) {
+    if (nbytes == 0 || nbytes % BLOCK_BYTES != 0) return -1;
+    const size_t nblocks = nbytes / BLOCK_BYTES;
+    if (out_elems != nblocks * QK_K) return -1;
+    for (size_t b = 0; b < nblocks; ++b)
+        oracle_dequant_block(bytes + b * BLOCK_BYTES, out + b * QK_K);
+    return 0;
+}
+
+/* Round an f32 to the nearest bf16 (8-bit significand), ties to even, returned
+ * widened back to f32. NaN stays NaN. Written from the format definition: keep
+ * the top 16 bits, adding half an ulp plus the parity of the kept lsb. */
+float oracle_bf16_round(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) {
+        u |= 0x00400000u; /* quiet NaN */
+        u &= 0xffff0000u;
+    } else {
+        const uint32_t lsb = (u >> 16) & 1u;
+        u = (u + 0x7fffu + lsb) & 0xffff0000u;
+    }
+    float r;
+    memcpy(&r, &u, 4);
+    return r;
+}
+
+static int matmul_shape_ok(long M, long N, long K) {
+    return M > 0 && N > 0 && K > 0 && K % QK_K == 0;
+}
+
+/* Dequantize row n of w (K/256 consecutive blocks) into wrow[K]. */
+static void dequant_row(const uint8_t *w, long n, long K, float *wrow) {
+    const long nb = K / QK_K;
+    const uint8_t *row = w + (size_t)n * (size_t)nb * BLOCK_BYTES;
+    for (long b = 0; b < nb; ++b)
+        oracle_dequant_block(row + (size_t)b * BLOCK_BYTES, wrow + b * QK_K);
+}
+
+/* fn run_dense: y[m, n] = sum over k of x[m, k] * w[n, k], with x row-major
+ * [M, K] f32, w N rows of K/256 blocks, y row-major [M, N]. Accumulates in f64
+ * in increasing k; also returns a[m, n] = sum over k of |x[m, k] * w[n, k]|,
+ * the scale the tolerances are stated against. bf16_operands = 1 first rounds
+ * both operands to bf16 (ties to even), the operand precision of the matrix-
+ * core path. One thread computes each output, so results do not depend on
+ * nthreads. Returns 0, or -1 for a rejected shape. */
+int oracle_matmul(const float *x, const uint8_t *w, double *y, double *a,
+                  long M, long N, long K, int bf16_operands, int nthreads) {
+    if (!matmul_shape_ok(M, N, K)) return -1;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel num_threads(nthreads)
+    {
+        float *wrow = (float *)malloc(sizeof(float) * (size_t)K);
+        float *xrow = (float *)malloc(sizeof(float) * (size_t)K);
+#pragma omp for schedule(static)
+        for (long n = 0; n < N; ++n) {
+            dequant_row(w, n, K, wrow);
+            if (bf16_operands)
+                for (long k = 0; k < K; ++k) wrow[k] = oracle_bf16_round(wrow[k]);
+            for (long m = 0; m < M; ++m) {
+                const float *xm = x + (size_t)m * (size_t)K;
+                if (bf16_operands) {
+                    for (long k = 0; k < K; ++k) xrow[k] = oracle_bf16_round(xm[k]);
+                    xm = xrow;
+                }
+                double s = 0.0, sa = 0.0;
+                for (long k = 0; k < K; ++k) {
+                    const double p = (double)xm[k] * (double)wrow[k];
+                    s += p;
+                    sa += fabs(p);
+                }
+                y[(size_t)m * (size_t)N + (size_t)n] = s;
+                if (a) a[(size_t)m * (size_t)N + (size_t)n] = sa;
+            }
+        }
+        free(wrow);
+        free(xrow);
+    }
+    return 0;
+}
+
+/* fn cpu_dot: f32 products summed left to right in f32, as the page's test
+ * computes its expected dense outputs. Same shapes as oracle_matmul. */
+int oracle_matmul_f32seq(const float *x, const uint8_t *w, float *y, long M, long N, long K) {
+    if (!matmul_shape_ok(M, N, K)) return -1;
+    float *wrow = (float *)malloc(sizeof(float) * (size_t)K);
+    for (long n = 0; n < N; ++n) {
+        dequant_row(w, n, K, wrow);
+        for (long m = 0; m < M; ++m) {
+            const float *xm = x + (size_t)m * (size_t)K;
+            float s = 0.0f;
+            for (long k = 0; k < K; ++k) s += wrow[k] * xm[k];
+            y[(size_t)m * (size_t)N + (size_t)n] = s;
+        }
+    }
+    free(wrow);
+    return 0;
+}
+
+/* test q2_k_embedding_gather_matches_canonical_rows_and_rejects_bad_ids:
+ * out[t, :] is the decoded table row ids[t]; the table is [vocab, embed_dim]
+ * weights stored as embed_dim/256 blocks per row. Any id >= vocab (the page
+ * tries id == vocab) is an error, detected before anything is written.
+ * Returns 0, -1 for a rejected shape, -2 for an out-of-range id. */
+int oracle_gather(const uint8_t *table, const uint32_t *ids, float *out,
+                  long vocab, long embed_dim, long n_tokens, int nthreads) {
+    if (vocab <= 0 || embed_dim <= 0 || n_tokens <= 0 || embed_dim % QK_K != 0) return -1;
+    for (long t = 0; t < n_tokens; ++t)
+        if ((long)ids[t] >= vocab) return -2;
+    if (nthreads < 1) nthreads = 1;
+    const long nb = embed_dim / QK_K;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (long t = 0; t < n_tokens; ++t) {
+        const uint8_t *row = table + (size_t)ids[t] * (size_t)nb * BLOCK_BYTES;
+        float *o = out + (size_t)t * (size_t)embed_dim;
+        for (long b = 0; b < nb; ++b)
+            oracle_dequant_block(row + (size_t)b * BLOCK_BYTES, o + b * QK_K);
+    }
+    return 0;
+}
