@@ -1,0 +1,386 @@
+// HIP kernels of the Q2_K weight path for gfx950 (MI355X).
+//
+// Block format and decode rule: docs.rs source page of mlx-native 0.10.8,
+// tests/deepseek_q2_k.rs (constants QK_K / BLOCK_BYTES, fn block,
+// fn reference_dequant). An 84-byte super-block holds 256 weights: 16 scale
+// bytes (low nibble sc, high nibble mn), 64 code bytes (four 2-bit codes
+// each), f16 d at byte 80 and f16 dmin at byte 82. Weight e has scale byte
+// e/16 and code (qs[32*(e/128) + e%32] >> 2*((e/32)%4)) & 3, and equals
+// f32(d)*sc*q - f32(dmin)*mn. Because d*sc*q and dmin*mn are exact in f32, the
+// value has one correct f32 rounding; the kernels reproduce it bit for bit.
+//
+// Built with -ffp-contract=off: every FMA below is written as one.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q2k_launch.h"
+
+namespace q2k {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr uint32_t kWave = 64;
+
+// d (bytes 80..81) and dmin (bytes 82..83) arrive together as one dword.
+__device__ __forceinline__ float f16_low(uint32_t v) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v & 0xffffu)));
+}
+__device__ __forceinline__ float f16_high(uint32_t v) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v >> 16)));
+}
+
+__device__ __forceinline__ uint32_t load_u32(const uint8_t *p) {
+    return *reinterpret_cast<const uint32_t *>(p);
+}
+
+// Weights e0..e0+3 (e0 % 4 == 0) of one block. The four share a scale byte and
+// one 2-bit position of four consecutive code bytes.
+__device__ __forceinline__ float4 decode_quad(const uint8_t *blk, uint32_t e0) {
+    const uint32_t sbyte = blk[e0 >> 4];
+    const uint32_t codes = load_u32(blk + 16 + 32 * (e0 >> 7) + (e0 & 31));
+    const uint32_t dd = load_u32(blk + 80);
+    const float dl = f16_low(dd) * static_cast<float>(sbyte & 15u);
+    const float ml = f16_high(dd) * static_cast<float>(sbyte >> 4);
+    const uint32_t c = (codes >> (2 * ((e0 >> 5) & 3))) & 0x03030303u;
+    float4 r;
+    r.x = dl * static_cast<float>(c & 0xffu) - ml;
+    r.y = dl * static_cast<float>((c >> 8) & 0xffu) - ml;
+    r.z = dl * static_cast<float>((c >> 16) & 0xffu) - ml;
+    r.w = dl * static_cast<float>(c >> 24) - ml;
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize: one 16-byte store per thread, a wavefront per block (1 KiB of
+// output), grid-stride over all quads.
+__global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ blocks, float4 *__restrict__ out,
+                                                    uint64_t nquads) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    for (uint64_t g = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < nquads; g += stride) {
+        const uint8_t *blk = blocks + (g >> 6) * kBlockBytes;
+        out[g] = decode_quad(blk, static_cast<uint32_t>(g & 63) << 2);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Embedding gather: grid.y walks tokens, grid.x the 16-byte quads of a row.
+// A token whose id is >= vocab raises the status word and its row is neither
+// read nor written.
+__global__ __launch_bounds__(256) void k_gather(const uint8_t *__restrict__ table, const uint32_t *__restrict__ ids,
+                                                float4 *__restrict__ out, uint32_t vocab, uint32_t blocks_per_row,
+                                                uint32_t n_tokens, int *status) {
+    const uint32_t row_quads = blocks_per_row * 64u;
+    const uint64_t row_bytes = static_cast<uint64_t>(blocks_per_row) * kBlockBytes;
+    for (uint32_t t = blockIdx.y; t < n_tokens; t += gridDim.y) {
+        const uint32_t id = ids[t];
+        if (id >= vocab) {
+            if (blockIdx.x == 0 && threadIdx.x == 0)
+                __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            continue;
+        }
+        const uint8_t *row = table + static_cast<uint64_t>(id) * row_bytes;
+        float4 *orow = out + static_cast<uint64_t>(t) * row_quads;
+        for (uint32_t q = blockIdx.x * blockDim.x + threadIdx.x; q < row_quads; q += gridDim.x * blockDim.x)
+            orow[q] = decode_quad(row + (q >> 6) * kBlockBytes, (q & 63u) << 2);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 GEMV for M <= 8: y[m, n] = sum_k x[m, k] * w[n, k].
+//
+// A wavefront owns ROWS consecutive weight rows and walks K four blocks at a
+// time. Lane l handles sub-block (l % 16) of block (l / 16) of the pass: the
+// 16 weights of one (half, 2-bit position, segment) — they share one scale
+// byte, so the lane accumulates t = sum q*x over its 16 codes and then adds
+// dl*t - ml*sum(x). Activations for the lane's 16 k stay in registers across
+// the ROWS rows. Partial sums are reduced across the 64 lanes at the end.
+// Every output is produced by the same instruction sequence whatever M is, so
+// a row of an M-row call equals an M = 1 call on that row bit for bit.
+template <int M, int ROWS>
+__global__ __launch_bounds__(256) void k_gemv(const float *__restrict__ x, const uint8_t *__restrict__ w,
+                                              float *__restrict__ y, uint32_t N, uint32_t K) {
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t row0 = (blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * ROWS;
+    if (row0 >= N) return;
+    const uint32_t nb = K >> 8;
+    const uint64_t row_bytes = static_cast<uint64_t>(nb) * kBlockBytes;
+    const uint32_t sb = lane & 15u;          // sub-block: scale byte index
+    const uint32_t bsel = lane >> 4;         // block within the pass
+    const uint32_t half = sb >> 3, pos = (sb >> 1) & 3u, seg = sb & 1u;
+    const uint32_t qoff = 16 + 32 * half + 16 * seg;        // the 16 code bytes of the segment
+    const uint32_t shift = 2 * pos;
+    const uint32_t koff = 128 * half + 32 * pos + 16 * seg; // first weight of the sub-block
+
+    float acc[ROWS][M];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+    for (uint32_t kb0 = 0; kb0 < nb; kb0 += 4) {
+        const uint32_t kb = kb0 + bsel;
+        if (kb >= nb) continue;
+        float xv[M][16];
+        float xsum[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float4 *xp = reinterpret_cast<const float4 *>(x + static_cast<uint64_t>(m) * K + kb * 256u + koff);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 v = xp[i];
+                xv[m][4 * i + 0] = v.x;
+                xv[m][4 * i + 1] = v.y;
+                xv[m][4 * i + 2] = v.z;
+                xv[m][4 * i + 3] = v.w;
+            }
+            float s = xv[m][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) s += xv[m][i];
+            xsum[m] = s;
+        }
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const uint32_t n = row0 + r;
+            if (n >= N) break;
+            const uint8_t *blk = w + n * row_bytes + static_cast<uint64_t>(kb) * kBlockBytes;
+            uint32_t qw[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qw[j] = load_u32(blk + qoff + 4 * j);
+            const uint32_t sbyte = blk[sb];
+            const uint32_t dd = load_u32(blk + 80);
+            const float dl = f16_low(dd) * static_cast<float>(sbyte & 15u);
+            const float ml = f16_high(dd) * static_cast<float>(sbyte >> 4);
+            float qf[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t c = (qw[j] >> shift) & 0x03030303u;
+                qf[4 * j + 0] = static_cast<float>(c & 0xffu);
+                qf[4 * j + 1] = static_cast<float>((c >> 8) & 0xffu);
+                qf[4 * j + 2] = static_cast<float>((c >> 16) & 0xffu);
+                qf[4 * j + 3] = static_cast<float>(c >> 24);
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float t = qf[0] * xv[m][0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) t = __builtin_fmaf(qf[i], xv[m][i], t);
+                float a = __builtin_fmaf(dl, t, acc[r][m]);
+                acc[r][m] = __builtin_fmaf(-ml, xsum[m], a);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        const uint32_t n = row0 + r;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float v = acc[r][m];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+            if (lane == 0 && n < N) y[static_cast<uint64_t>(m) * N + n] = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core path for M > 8: y = bf16(x) * bf16(W)^T with fp32 accumulation.
+//
+// A 256-thread workgroup computes a 128 x 128 tile of y. K advances one half
+// super-block (128 weights) at a time: the x tile (f32) is rounded to bf16 and
+// the W tile is decoded and rounded to bf16, both into LDS, then each of the
+// four wavefronts runs a 2 x 2 grid of v_mfma_f32_32x32x16_bf16 on its 64 x 64
+// quadrant. A half super-block is self-contained: its 32 code bytes, its 8
+// scale bytes and the block's d and dmin.
+constexpr uint32_t kTileM = 128, kTileN = 128, kTileK = 128;
+constexpr uint32_t kLdsStride = kTileK + 8;  // bf16 per LDS row; padding spreads banks
+
+__device__ __forceinline__ bf16x8 pack_bf16(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
+                                            float a7) {
+    bf16x8 v;
+    v[0] = static_cast<__bf16>(a0);
+    v[1] = static_cast<__bf16>(a1);
+    v[2] = static_cast<__bf16>(a2);
+    v[3] = static_cast<__bf16>(a3);
+    v[4] = static_cast<__bf16>(a4);
+    v[5] = static_cast<__bf16>(a5);
+    v[6] = static_cast<__bf16>(a6);
+    v[7] = static_cast<__bf16>(a7);
+    return v;
+}
+
+__global__ __launch_bounds__(256) void k_gemm_mfma(const float *__restrict__ x, const uint8_t *__restrict__ w,
+                                                   float *__restrict__ y, uint32_t M, uint32_t N, uint32_t K) {
+    __shared__ __attribute__((aligned(16))) __bf16 xs[kTileM * kLdsStride];
+    __shared__ __attribute__((aligned(16))) __bf16 ws[kTileN * kLdsStride];
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u, wave = tid >> 6;
+    const uint32_t wm = wave >> 1, wn = wave & 1u;
+    const uint32_t tiles_n = (N + kTileN - 1) / kTileN;
+    const uint32_t n0 = (blockIdx.x % tiles_n) * kTileN, m0 = (blockIdx.x / tiles_n) * kTileM;
+    const uint32_t nb = K >> 8;
+    const uint64_t row_bytes = static_cast<uint64_t>(nb) * kBlockBytes;
+
+    // Staging role: tile row r, and which half of it (x: 64 k; W: one segment).
+    const uint32_t r = tid >> 1, part = tid & 1u;
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    for (uint32_t kh = 0; kh < 2 * nb; ++kh) {
+        const uint32_t kb = kh >> 1, half = kh & 1u;
+        {   // x tile: row m0 + r, k = 128*kh + 64*part .. +64
+            const uint32_t m = m0 + r;
+            __bf16 *dst = xs + r * kLdsStride + part * 64;
+            if (m < M) {
+                const float4 *src = reinterpret_cast<const float4 *>(x + static_cast<uint64_t>(m) * K + kh * 128u + part * 64u);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float4 a = src[2 * i], b = src[2 * i + 1];
+                    *reinterpret_cast<bf16x8 *>(dst + 8 * i) = pack_bf16(a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    *reinterpret_cast<bf16x8 *>(dst + 8 * i) = pack_bf16(0, 0, 0, 0, 0, 0, 0, 0);
+            }
+        }
+        {   // W tile: row n0 + r, segment `part` of half `half` of block kb
+            const uint32_t n = n0 + r;
+            __bf16 *dst = ws + r * kLdsStride + 16 * part;
+            if (n < N) {
+                const uint8_t *blk = w + n * row_bytes + static_cast<uint64_t>(kb) * kBlockBytes;
+                uint32_t qw[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) qw[j] = load_u32(blk + 16 + 32 * half + 16 * part + 4 * j);
+                const uint32_t s_lo = load_u32(blk + 8 * half), s_hi = load_u32(blk + 8 * half + 4);
+                const uint32_t dd = load_u32(blk + 80);
+                const float d = f16_low(dd), dmin = f16_high(dd);
+#pragma unroll
+                for (uint32_t pos = 0; pos < 4; ++pos) {
+                    // scale byte 8*half + 2*pos + part
+                    const uint32_t sbyte = ((pos < 2 ? s_lo : s_hi) >> (8 * (2 * (pos & 1) + part))) & 0xffu;
+                    const float dl = d * static_cast<float>(sbyte & 15u);
+                    const float ml = dmin * static_cast<float>(sbyte >> 4);
+                    float wv[16];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t c = (qw[j] >> (2 * pos)) & 0x03030303u;
+                        wv[4 * j + 0] = dl * static_cast<float>(c & 0xffu) - ml;
+                        wv[4 * j + 1] = dl * static_cast<float>((c >> 8) & 0xffu) - ml;
+                        wv[4 * j + 2] = dl * static_cast<float>((c >> 16) & 0xffu) - ml;
+                        wv[4 * j + 3] = dl * static_cast<float>(c >> 24) - ml;
+                    }
+                    *reinterpret_cast<bf16x8 *>(dst + 32 * pos) =
+                        pack_bf16(wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]);
+                    *reinterpret_cast<bf16x8 *>(dst + 32 * pos + 8) =
+                        pack_bf16(wv[8], wv[9], wv[10], wv[11], wv[12], wv[13], wv[14], wv[15]);
+                }
+            } else {
+#pragma unroll
+                for (uint32_t pos = 0; pos < 4; ++pos) {
+                    *reinterpret_cast<bf16x8 *>(dst + 32 * pos) = pack_bf16(0, 0, 0, 0, 0, 0, 0, 0);
+                    *reinterpret_cast<bf16x8 *>(dst + 32 * pos + 8) = pack_bf16(0, 0, 0, 0, 0, 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (uint32_t kk = 0; kk < kTileK / 16; ++kk) {
+            const uint32_t kcol = 16 * kk + 8 * (lane >> 5);
+            bf16x8 a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *reinterpret_cast<const bf16x8 *>(xs + (wm * 64 + 32 * i + (lane & 31)) * kLdsStride + kcol);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[j] = *reinterpret_cast<const bf16x8 *>(ws + (wn * 64 + 32 * j + (lane & 31)) * kLdsStride + kcol);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    // D layout of a 32x32 MFMA tile: lane l holds column l % 32 and, in
+    // register v, row 8*(v/4) + 4*(l/32) + v%4.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t n = n0 + wn * 64 + 32 * j + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const uint32_t m = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (m < M && n < N) y[static_cast<uint64_t>(m) * N + n] = acc[i][j][v];
+            }
+        }
+}
+
+constexpr uint32_t kGemvRows = 2;  // weight rows per wavefront
+
+template <int M>
+hipError_t launch_gemv_m(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, hipStream_t stream) {
+    const uint32_t waves = (N + kGemvRows - 1) / kGemvRows;
+    const uint32_t blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((k_gemv<M, kGemvRows>), dim3(blocks), dim3(256), 0, stream, x, w, y, N, K);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dequantize(const uint8_t *blocks, uint64_t nblocks, float *out, hipStream_t stream) {
+    const uint64_t nquads = nblocks * 64u;
+    const uint64_t want = (nquads + 255) / 256;
+    const uint32_t grid = static_cast<uint32_t>(want < 65536u ? want : 65536u);
+    hipLaunchKernelGGL(k_dequantize, dim3(grid), dim3(256), 0, stream, blocks, reinterpret_cast<float4 *>(out),
+                       nquads);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, uint32_t vocab,
+                         uint32_t blocks_per_row, uint32_t n_tokens, int *status, hipStream_t stream) {
+    const uint64_t row_quads = static_cast<uint64_t>(blocks_per_row) * 64u;
+    const uint64_t gx = (row_quads + 255) / 256;
+    const uint32_t grid_x = static_cast<uint32_t>(gx < 4096u ? gx : 4096u);
+    const uint32_t grid_y = n_tokens < 32768u ? n_tokens : 32768u;
+    hipLaunchKernelGGL(k_gather, dim3(grid_x, grid_y), dim3(256), 0, stream, table, ids,
+                       reinterpret_cast<float4 *>(out), vocab, blocks_per_row, n_tokens, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
+                       hipStream_t stream) {
+    switch (M) {
+        case 1: return launch_gemv_m<1>(x, w, y, N, K, stream);
+        case 2: return launch_gemv_m<2>(x, w, y, N, K, stream);
+        case 3: return launch_gemv_m<3>(x, w, y, N, K, stream);
+        case 4: return launch_gemv_m<4>(x, w, y, N, K, stream);
+        case 5: return launch_gemv_m<5>(x, w, y, N, K, stream);
+        case 6: return launch_gemv_m<6>(x, w, y, N, K, stream);
+        case 7: return launch_gemv_m<7>(x, w, y, N, K, stream);
+        case 8: return launch_gemv_m<8>(x, w, y, N, K, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemm_mfma(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
+                            hipStream_t stream) {
+    const uint64_t tiles = static_cast<uint64_t>((N + kTileN - 1) / kTileN) * ((M + kTileM - 1) / kTileM);
+    if (tiles > 0x7fffffffu) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_gemm_mfma, dim3(static_cast<uint32_t>(tiles)), dim3(256), 0, stream, x, w, y, M, N, K);
+    return hipGetLastError();
+}
+
+}  // namespace q2k

@@ -1,0 +1,27 @@
+// Internal launch interface between the C ABI (q2k_api.cpp) and the HIP
+// kernels (q2k_kernels.hip). Arguments are validated by the caller; these
+// functions only size grids and enqueue kernels on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q2k {
+
+constexpr uint32_t kQK = 256;          // weights per super-block
+constexpr uint32_t kBlockBytes = 84;   // bytes per super-block
+constexpr uint32_t kGemvMaxM = 8;      // largest M the fp32 GEMV handles
+
+hipError_t launch_dequantize(const uint8_t *blocks, uint64_t nblocks, float *out, hipStream_t stream);
+
+hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, uint32_t vocab,
+                         uint32_t blocks_per_row, uint32_t n_tokens, int *status, hipStream_t stream);
+
+hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
+                       hipStream_t stream);
+
+hipError_t launch_gemm_mfma(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
+                            hipStream_t stream);
+
+}  // namespace q2k

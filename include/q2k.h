@@ -1,0 +1,135 @@
+/*
+ * q2k.h — C ABI of libq2k, the MI355X (gfx950) Q2_K weight path.
+ *
+ * Q2_K is GGML's 2-bit k-quant. Its layout and decode rule are those of the
+ * docs.rs source page of mlx-native 0.10.8, tests/deepseek_q2_k.rs
+ * (constants QK_K and BLOCK_BYTES, fn block, fn reference_dequant):
+ *
+ *   one super-block = 256 weights in 84 bytes
+ *     bytes  0..15  scales[16]  low nibble: sub-block scale sc, high nibble: sub-block min mn
+ *     bytes 16..79  qs[64]      2-bit codes, four per byte
+ *     bytes 80..81  d           IEEE f16, little endian
+ *     bytes 82..83  dmin        IEEE f16, little endian
+ *   weight e (0..255): s = scales[e / 16], q = (qs[32*(e/128) + e%32] >> 2*((e/32)%4)) & 3,
+ *                      w = f32(d)*sc*q - f32(dmin)*mn, evaluated in f32.
+ *
+ * A weight matrix W[N, K] (K a multiple of 256) is N rows of K/256 blocks, row
+ * after row, blocks of a row in increasing k (fn run_dense appends the blocks
+ * of each row in turn). An embedding table [vocab, embed_dim] is the same with
+ * vocab rows.
+ *
+ * Conventions shared by every call:
+ *  - Every pointer is caller-owned DEVICE memory on the current HIP device.
+ *    libq2k never frees or retains it.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it;
+ *    q2k_dequantize and q2k_matmul return before the GPU finishes, so the caller
+ *    synchronises before reading outputs (the page's encode / commit_and_wait
+ *    split). q2k_embedding_gather waits for its own kernel (see below).
+ *  - All arguments are validated before anything is enqueued. On any error the
+ *    call returns a non-zero status, enqueues nothing and leaves outputs
+ *    untouched (except the gather's out-of-range case, documented below);
+ *    q2k_last_error_message() then describes the failure.
+ *  - Alignment: float outputs and x must be 16-byte aligned; Q2_K byte buffers
+ *    and ids must be 4-byte aligned (84 is a multiple of 4).
+ *  - An output range may not overlap any input range.
+ *  - Calls on different streams may run concurrently; each call only reads its
+ *    inputs and writes its outputs.
+ */
+#ifndef Q2K_H
+#define Q2K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q2K_QK 256          /* weights per super-block */
+#define Q2K_BLOCK_BYTES 84  /* bytes per super-block */
+
+typedef enum q2k_status {
+    Q2K_OK = 0,
+    Q2K_ERR_INVALID_ARGUMENT = 1, /* bad size, null or misaligned pointer, overlap */
+    Q2K_ERR_ID_OUT_OF_RANGE = 2,  /* q2k_embedding_gather: some id >= vocab */
+    Q2K_ERR_DEVICE = 3            /* a HIP runtime call failed */
+} q2k_status;
+
+/* Matmul kernel choice. Q2K_PATH_AUTO picks the fp32 GEMV for M <= 8 and the
+ * bf16 matrix-core path for M > 8, the switch the page's dense test makes at
+ * more than 8 rows (fn run_dense: its tolerance changes there). The forced
+ * values mirror the page's forced-mm test hooks (dispatch_mm_for_test). */
+typedef enum q2k_path {
+    Q2K_PATH_AUTO = 0,
+    Q2K_PATH_GEMV = 1, /* fp32 GEMV; only valid for 1 <= M <= 8 */
+    Q2K_PATH_MFMA = 2  /* bf16 operands (round to nearest even), fp32 accumulation; any M */
+} q2k_path;
+
+/*
+ * q2k_dequantize — decode whole Q2_K blocks to f32.
+ * Page: test q2_k_host_decode_matches_all_256_canonical_values (values) and
+ * test q2_k_host_decode_rejects_malformed_buffers (length rules).
+ *   blocks       device bytes, blocks_bytes long; 4-byte aligned.
+ *   blocks_bytes must be a positive multiple of 84.
+ *   out          device f32 [out_elems]; 16-byte aligned.
+ *   out_elems    must equal blocks_bytes / 84 * 256.
+ * out[256*b + e] = weight e of block b, bit-identical to the f32 decode rule
+ * above (the value is unique: d*sc*q and dmin*mn are exact in f32, only the
+ * final subtraction rounds). Asynchronous on `stream`.
+ */
+q2k_status q2k_dequantize(const void *blocks, size_t blocks_bytes, float *out, size_t out_elems,
+                          void *stream);
+
+/*
+ * q2k_matmul — y[M, N] = x[M, K] * W[N, K]^T with W in Q2_K.
+ * Page: fn run_dense, which calls quantized_matmul_ggml with (m, n, k).
+ *   x  device f32 [M, K] row-major; 16-byte aligned.
+ *   w  device Q2_K bytes, N * K/256 * 84 long (layout above); 4-byte aligned.
+ *   y  device f32 [M, N] row-major; 16-byte aligned.
+ *   M, N >= 1; K >= 256 and a multiple of 256.
+ * M <= 8 runs the fp32 GEMV: |y - exact| <= 1e-5 * sum_k |x*w| per output,
+ * and every row of y is bit-identical to an M = 1 call on that row of x.
+ * M > 8 runs the matrix-core path on bf16(x) and bf16(w) with fp32
+ * accumulation: |y - exact| <= 4e-3 * sum_k |x*w| + 1e-6.
+ * Asynchronous on `stream`; allocates nothing.
+ */
+q2k_status q2k_matmul(const float *x, const void *w, float *y, uint32_t M, uint32_t N, uint32_t K,
+                      void *stream);
+
+/* q2k_matmul with an explicit kernel choice (see q2k_path). Same arguments,
+ * rules and guarantees; Q2K_PATH_GEMV with M > 8 is Q2K_ERR_INVALID_ARGUMENT. */
+q2k_status q2k_matmul_path(const float *x, const void *w, float *y, uint32_t M, uint32_t N,
+                           uint32_t K, q2k_path path, void *stream);
+
+/*
+ * q2k_embedding_gather — out[t, :] = decoded row ids[t] of a Q2_K table.
+ * Page: test q2_k_embedding_gather_matches_canonical_rows_and_rejects_bad_ids
+ * (EmbeddingQ2KParams { vocab_size, embed_dim, n_tokens }; an id equal to
+ * vocab must make the call fail).
+ *   table     device Q2_K bytes, vocab * embed_dim/256 * 84 long; 4-byte aligned.
+ *   ids       device u32 [n_tokens]; 4-byte aligned. Duplicates are allowed.
+ *   out       device f32 [n_tokens, embed_dim] row-major; 16-byte aligned.
+ *   vocab, n_tokens >= 1; embed_dim >= 256 and a multiple of 256.
+ * Rows are bit-identical to q2k_dequantize of the same blocks. The kernel
+ * checks every id on the GPU and never reads a row at or beyond vocab; the
+ * call then waits for `stream` and returns Q2K_ERR_ID_OUT_OF_RANGE if any id
+ * was >= vocab. In that case rows of valid ids hold their values and rows of
+ * bad ids are left unwritten. Synchronous: it returns after the kernel ends.
+ * Uses one small pinned status word per device, created on first use; calls
+ * from several host threads are serialised on it.
+ */
+q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *out, uint32_t vocab,
+                                uint32_t embed_dim, uint32_t n_tokens, void *stream);
+
+/* Static English name of a status code ("Q2K_OK", ...). Never NULL. */
+const char *q2k_status_string(q2k_status s);
+
+/* Detail of the last failing call on this host thread (empty string if none).
+ * The pointer stays valid until the next libq2k call on the same thread. */
+const char *q2k_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q2K_H */

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device.
+
+The rejection rules restate the docs.rs source page of mlx-native 0.10.8,
+tests/deepseek_q2_k.rs (malformed-buffer test: an 83-byte block and a
+255-value output are errors) plus the header's shape, alignment and overlap
+rules. Every call below fails validation, so no HIP work is ever enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ggml_q2_dequant_amd as q2k
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q2k.h")
+
+# Fake, well-aligned, non-overlapping "device" addresses: validation never
+# dereferences them.
+A = 1 << 32
+B = 2 << 32
+C = 3 << 32
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q2k_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q2k.LIB_PATH):
+        pytest.skip("libq2k.so not built")
+    return q2k.load_library()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert _header_functions() == sorted(q2k.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    names = [lib.q2k_status_string(i).decode() for i in range(4)]
+    assert names == ["Q2K_OK", "Q2K_ERR_INVALID_ARGUMENT", "Q2K_ERR_ID_OUT_OF_RANGE", "Q2K_ERR_DEVICE"]
+    assert lib.q2k_status_string(99).decode() == "Q2K_UNKNOWN_STATUS"
+
+
+def _err(lib, rc, fragment):
+    assert rc == q2k.Q2K_ERR_INVALID_ARGUMENT
+    assert fragment in lib.q2k_last_error_message().decode()
+
+
+@pytest.mark.parametrize("nbytes,nout,frag", [
+    (83, 256, "multiple of 84"),          # the page's short block
+    (84, 255, "need 256 outputs"),        # the page's short output
+    (0, 0, "multiple of 84"),             # empty input
+    (168, 256, "need 512 outputs"),
+])
+def test_dequantize_rejects_malformed_lengths(lib, nbytes, nout, frag):
+    _err(lib, lib.q2k_dequantize(A, nbytes, B, nout, None), frag)
+
+
+def test_dequantize_rejects_null_misaligned_and_overlap(lib):
+    _err(lib, lib.q2k_dequantize(None, 84, B, 256, None), "null")
+    _err(lib, lib.q2k_dequantize(A + 2, 84, B, 256, None), "aligned")
+    _err(lib, lib.q2k_dequantize(A, 84, B + 4, 256, None), "aligned")
+    _err(lib, lib.q2k_dequantize(A, 84, A + 16, 256, None), "overlaps")
+
+
+@pytest.mark.parametrize("M,N,K,frag", [
+    (0, 8, 256, ">= 1"), (1, 0, 256, ">= 1"), (1, 8, 0, ">= 1"),
+    (1, 8, 100, "multiple of 256"), (4, 8, 255, "multiple of 256"),
+])
+def test_matmul_rejects_bad_shapes(lib, M, N, K, frag):
+    _err(lib, lib.q2k_matmul(A, B, C, M, N, K, None), frag)
+
+
+def test_matmul_rejects_null_misaligned_overlap_and_bad_path(lib):
+    _err(lib, lib.q2k_matmul(None, B, C, 1, 8, 256, None), "null")
+    _err(lib, lib.q2k_matmul(A + 4, B, C, 1, 8, 256, None), "aligned")
+    _err(lib, lib.q2k_matmul(A, B + 2, C, 1, 8, 256, None), "aligned")
+    _err(lib, lib.q2k_matmul(A, B, A + 16, 1, 8, 256, None), "overlaps")
+    _err(lib, lib.q2k_matmul(A, B, B + 16, 1, 8, 256, None), "overlaps")
+    _err(lib, lib.q2k_matmul_path(A, B, C, 9, 8, 256, q2k.PATH_GEMV, None), "M <= 8")
+    _err(lib, lib.q2k_matmul_path(A, B, C, 1, 8, 256, 7, None), "unknown path")
+
+
+def test_matmul_rejects_size_overflow(lib):
+    _err(lib, lib.q2k_matmul(A, B, C, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFF00, None), "overflow")
+
+
+@pytest.mark.parametrize("vocab,dim,nt,frag", [
+    (0, 256, 2, ">= 1"), (3, 0, 2, ">= 1"), (3, 256, 0, ">= 1"), (3, 100, 2, "multiple of 256"),
+])
+def test_gather_rejects_bad_shapes(lib, vocab, dim, nt, frag):
+    _err(lib, lib.q2k_embedding_gather(A, B, C, vocab, dim, nt, None), frag)
+
+
+def test_gather_rejects_null_misaligned_and_overlap(lib):
+    _err(lib, lib.q2k_embedding_gather(None, B, C, 3, 256, 2, None), "null")
+    _err(lib, lib.q2k_embedding_gather(A + 1, B, C, 3, 256, 2, None), "aligned")
+    _err(lib, lib.q2k_embedding_gather(A, B + 2, C, 3, 256, 2, None), "aligned")
+    _err(lib, lib.q2k_embedding_gather(A, B, C + 8, 3, 256, 2, None), "aligned")
+    _err(lib, lib.q2k_embedding_gather(A, B, A, 3, 256, 2, None), "overlaps")
+    _err(lib, lib.q2k_embedding_gather(A, C + 4, C, 3, 256, 2, None), "overlaps")
+
+
+def test_python_binding_raises_typed_errors(lib):
+    with pytest.raises(q2k.Q2KInvalidArgument, match="multiple of 256"):
+        q2k.q2k_matmul(A, B, C, 1, 8, 100, stream=0)
+    with pytest.raises(ValueError):
+        q2k.q2k_matmul(A, B, C, 0, 8, 256, stream=0)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        _load_fresh(str(tmp_path / "nope.so"))
+
+
+def _load_fresh(path):
+    saved = q2k._lib
+    q2k._lib = None
+    try:
+        return q2k.load_library(path)
+    finally:
+        q2k._lib = saved
