@@ -89,30 +89,86 @@ __global__ __launch_bounds__(256) void k_gather(const uint8_t *__restrict__ tabl
 }
 
 // ---------------------------------------------------------------------------
+// Cross-lane helpers (DPP, gfx9 encodings).
+constexpr int kDppQuadBcast0 = 0x00;   // quad_perm [0,0,0,0]
+constexpr int kDppQuadBcast1 = 0x55;   // quad_perm [1,1,1,1]
+constexpr int kDppQuadBcast2 = 0xAA;   // quad_perm [2,2,2,2]
+constexpr int kDppQuadBcast3 = 0xFF;   // quad_perm [3,3,3,3]
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wavefront, in a fixed order; the total lands in
+// lanes 48..63 and is returned from lane 63 (uniform).
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<kDppQuadXor1>(v);
+    v += dpp<kDppQuadXor2>(v);
+    v += dpp<kDppRowRor4>(v);
+    v += dpp<kDppRowRor8>(v);          // every lane of a row holds its row sum
+    v += dpp<kDppRowBcast15, 0xA>(v);  // rows 1, 3 += rows 0, 2
+    v += dpp<kDppRowBcast31, 0xC>(v);  // rows 2, 3 += rows 0 + 1
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// The four code bytes of a dword at one 2-bit position, as floats q * 2^-9:
+// masked to 0..3 per byte, each byte is an OCP e4m3 subnormal of that value.
+constexpr float kCodeScale = 512.0f;  // 2^9 undoes the e4m3 subnormal scale exactly
+
+__device__ __forceinline__ void codes4(uint32_t v, uint32_t shift, float *q) {
+    const int c = static_cast<int>((v >> shift) & 0x03030303u);
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
+    q[0] = lo[0];
+    q[1] = lo[1];
+    q[2] = hi[0];
+    q[3] = hi[1];
+}
+
+// ---------------------------------------------------------------------------
 // fp32 GEMV for M <= 8: y[m, n] = sum_k x[m, k] * w[n, k].
 //
-// A wavefront owns ROWS consecutive weight rows and walks K four blocks at a
-// time. Lane l handles sub-block (l % 16) of block (l / 16) of the pass: the
-// 16 weights of one (half, 2-bit position, segment) — they share one scale
-// byte, so the lane accumulates t = sum q*x over its 16 codes and then adds
-// dl*t - ml*sum(x). Activations for the lane's 16 k stay in registers across
-// the ROWS rows. Partial sums are reduced across the 64 lanes at the end.
-// Every output is produced by the same instruction sequence whatever M is, so
-// a row of an M-row call equals an M = 1 call on that row bit for bit.
+// A 256-thread workgroup owns ROWS consecutive weight rows and covers 16
+// blocks (4096 weights) of K per pass. Thread t handles one sub-block: block
+// t / 16 of the pass; within it the segment group g = (t % 16) / 4 (half g/2,
+// segment g%2) and the 2-bit position p = t % 4. Its 16 weights share one
+// scale byte, so it accumulates s = sum q*x over them and adds dl*s - ml*sum(x).
+// The four threads of a quad share the segment's 16 code bytes: each loads one
+// dword and DPP broadcasts hand the other three around.
+//
+// All ROWS rows' loads are issued before any of them is used, so a workgroup
+// keeps ROWS * 21 bytes per thread in flight. Activations for the thread's 16
+// k stay in registers across the rows. Partial sums are reduced in a fixed
+// order (DPP within a wavefront, then the four wavefronts through LDS), and
+// every m runs the same instruction sequence, so a row of an M-row call equals
+// an M = 1 call on that row bit for bit.
 template <int M, int ROWS>
 __global__ __launch_bounds__(256) void k_gemv(const float *__restrict__ x, const uint8_t *__restrict__ w,
                                               float *__restrict__ y, uint32_t N, uint32_t K) {
-    const uint32_t lane = threadIdx.x & (kWave - 1);
-    const uint32_t row0 = (blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * ROWS;
-    if (row0 >= N) return;
+    __shared__ float red[4][ROWS * M];
+    const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const uint32_t nb = K >> 8;
     const uint64_t row_bytes = static_cast<uint64_t>(nb) * kBlockBytes;
-    const uint32_t sb = lane & 15u;          // sub-block: scale byte index
-    const uint32_t bsel = lane >> 4;         // block within the pass
-    const uint32_t half = sb >> 3, pos = (sb >> 1) & 3u, seg = sb & 1u;
-    const uint32_t qoff = 16 + 32 * half + 16 * seg;        // the 16 code bytes of the segment
+    const uint32_t row0 = blockIdx.x * ROWS;
+    const uint32_t bslot = tid >> 4;                  // block within the pass
+    const uint32_t grp = (tid >> 2) & 3u, pos = tid & 3u;
+    const uint32_t half = grp >> 1, seg = grp & 1u;
+    const uint32_t sb = 8 * half + 2 * pos + seg;     // scale byte index
+    const uint32_t koff = 128 * half + 32 * pos + 16 * seg;
+    const uint32_t qoff = 16 + 32 * half + 16 * seg + 4 * pos;  // this thread's dword of the segment
     const uint32_t shift = 2 * pos;
-    const uint32_t koff = 128 * half + 32 * pos + 16 * seg; // first weight of the sub-block
 
     float acc[ROWS][M];
 #pragma unroll
@@ -120,69 +176,80 @@ __global__ __launch_bounds__(256) void k_gemv(const float *__restrict__ x, const
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-    for (uint32_t kb0 = 0; kb0 < nb; kb0 += 4) {
-        const uint32_t kb = kb0 + bsel;
-        if (kb >= nb) continue;
+    for (uint32_t kb0 = 0; kb0 < nb; kb0 += 16) {
+        const uint32_t kb = kb0 + bslot;
+        const bool active = kb < nb;
+
+        uint32_t qd[ROWS], sbyte[ROWS], dd[ROWS];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const uint32_t n = row0 + r;
+            qd[r] = 0;
+            sbyte[r] = 0;
+            dd[r] = 0;
+            if (active && n < N) {
+                const uint8_t *blk = w + n * row_bytes + static_cast<uint64_t>(kb) * kBlockBytes;
+                qd[r] = load_u32(blk + qoff);
+                sbyte[r] = blk[sb];
+                dd[r] = load_u32(blk + 80);
+            }
+        }
+
         float xv[M][16];
         float xsum[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            const float4 *xp = reinterpret_cast<const float4 *>(x + static_cast<uint64_t>(m) * K + kb * 256u + koff);
+            if (active) {
+                const float4 *xp = reinterpret_cast<const float4 *>(x + static_cast<uint64_t>(m) * K + kb * 256u + koff);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 v = xp[i];
-                xv[m][4 * i + 0] = v.x;
-                xv[m][4 * i + 1] = v.y;
-                xv[m][4 * i + 2] = v.z;
-                xv[m][4 * i + 3] = v.w;
+                for (int i = 0; i < 4; ++i) {
+                    const float4 v = xp[i];
+                    xv[m][4 * i + 0] = v.x;
+                    xv[m][4 * i + 1] = v.y;
+                    xv[m][4 * i + 2] = v.z;
+                    xv[m][4 * i + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xv[m][i] = 0.0f;
             }
             float s = xv[m][0];
 #pragma unroll
             for (int i = 1; i < 16; ++i) s += xv[m][i];
             xsum[m] = s;
         }
+
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-            const uint32_t n = row0 + r;
-            if (n >= N) break;
-            const uint8_t *blk = w + n * row_bytes + static_cast<uint64_t>(kb) * kBlockBytes;
-            uint32_t qw[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) qw[j] = load_u32(blk + qoff + 4 * j);
-            const uint32_t sbyte = blk[sb];
-            const uint32_t dd = load_u32(blk + 80);
-            const float dl = f16_low(dd) * static_cast<float>(sbyte & 15u);
-            const float ml = f16_high(dd) * static_cast<float>(sbyte >> 4);
-            float qf[16];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t c = (qw[j] >> shift) & 0x03030303u;
-                qf[4 * j + 0] = static_cast<float>(c & 0xffu);
-                qf[4 * j + 1] = static_cast<float>((c >> 8) & 0xffu);
-                qf[4 * j + 2] = static_cast<float>((c >> 16) & 0xffu);
-                qf[4 * j + 3] = static_cast<float>(c >> 24);
-            }
+            float q[16];
+            codes4(dpp_u32<kDppQuadBcast0>(qd[r]), shift, q + 0);
+            codes4(dpp_u32<kDppQuadBcast1>(qd[r]), shift, q + 4);
+            codes4(dpp_u32<kDppQuadBcast2>(qd[r]), shift, q + 8);
+            codes4(dpp_u32<kDppQuadBcast3>(qd[r]), shift, q + 12);
+            const float dl = f16_low(dd[r]) * static_cast<float>(sbyte[r] & 15u) * kCodeScale;
+            const float ml = f16_high(dd[r]) * static_cast<float>(sbyte[r] >> 4);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                float t = qf[0] * xv[m][0];
+                float t = q[0] * xv[m][0];
 #pragma unroll
-                for (int i = 1; i < 16; ++i) t = __builtin_fmaf(qf[i], xv[m][i], t);
-                float a = __builtin_fmaf(dl, t, acc[r][m]);
+                for (int i = 1; i < 16; ++i) t = __builtin_fmaf(q[i], xv[m][i], t);
+                const float a = __builtin_fmaf(dl, t, acc[r][m]);
                 acc[r][m] = __builtin_fmaf(-ml, xsum[m], a);
             }
         }
     }
 
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-        const uint32_t n = row0 + r;
+    for (int r = 0; r < ROWS; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            float v = acc[r][m];
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-            if (lane == 0 && n < N) y[static_cast<uint64_t>(m) * N + n] = v;
+            const float s = wave_sum(acc[r][m]);
+            if (lane == 0) red[wave][r * M + m] = s;
         }
+    __syncthreads();
+    if (tid < ROWS * M) {
+        const uint32_t r = tid / M, m = tid % M, n = row0 + r;
+        if (n < N) y[static_cast<uint64_t>(m) * N + n] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
     }
 }
 
@@ -328,13 +395,18 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const float *__restrict__ x, 
         }
 }
 
-constexpr uint32_t kGemvRows = 2;  // weight rows per wavefront
+// Weight rows per workgroup: more rows amortise the activation loads, fewer
+// keep more workgroups in flight and bound registers as M grows.
+template <int M>
+constexpr int gemv_rows() {
+    return M <= 2 ? 8 : (M <= 4 ? 8 : 4);
+}
 
 template <int M>
 hipError_t launch_gemv_m(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, hipStream_t stream) {
-    const uint32_t waves = (N + kGemvRows - 1) / kGemvRows;
-    const uint32_t blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((k_gemv<M, kGemvRows>), dim3(blocks), dim3(256), 0, stream, x, w, y, N, K);
+    constexpr int R = gemv_rows<M>();
+    const uint32_t blocks = (N + R - 1) / R;
+    hipLaunchKernelGGL((k_gemv<M, R>), dim3(blocks), dim3(256), 0, stream, x, w, y, N, K);
     return hipGetLastError();
 }
 
