@@ -63,6 +63,7 @@ q2k_status check_matmul(const float *x, const void *w, const float *y, uint32_t 
     if (!x || !w || !y) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul: null pointer");
     if (M == 0 || N == 0 || K == 0) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul: M, N, K must be >= 1 (got %u, %u, %u)", M, N, K);
     if (K % q2k::kQK != 0) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul: K=%u is not a multiple of 256", K);
+    if (K > q2k::kMaxK) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul: K=%u exceeds the limit %u", K, q2k::kMaxK);
     uint64_t xb, wb, yb, t;
     if (!mul_ok(M, K, &t) || !mul_ok(t, 4, &xb) || !mul_ok(N, K / q2k::kQK, &t) || !mul_ok(t, q2k::kBlockBytes, &wb) ||
         !mul_ok(M, N, &t) || !mul_ok(t, 4, &yb))

@@ -254,6 +254,204 @@ __global__ __launch_bounds__(256) void k_gemv(const float *__restrict__ x, const
 }
 
 // ---------------------------------------------------------------------------
+// fp32 GEMV for M <= 2 (decode).
+//
+// A 256-thread workgroup owns 4 * NI consecutive weight rows, taken four at a
+// time (NI iterations), and walks K in chunks of 16 blocks (4096 weights).
+// Wavefront w covers blocks 4w .. 4w+3 of a chunk; lane l of it works on row
+// l / 16 of the current four, block (l / 4) % 4 of the wavefront's four and
+// code segment g = l % 4: the 16 code bytes qs[32h + 16s ..] with h = g / 2,
+// s = g % 2, at all four 2-bit positions p -- that is, all of sub-blocks
+// 8h + 2p + s (64 weights). The lane's 64 activations depend only on
+// (block, segment), so a chunk's activations are loaded once per workgroup
+// and stay in registers for all 4 * NI rows. All of a chunk's loads are issued
+// before any arithmetic, so the workgroup's whole share of the matrix is in
+// flight at once.
+//
+// Codes leave the bytes as e4m3 values four at a time: a byte masked with
+// 0x03 is q * 2^-9 (a subnormal) and a byte masked with 0x0C is 4q * 2^-9 =
+// q * 2^-7, both exact, so positions 0 and 1 need only a mask and positions 2
+// and 3 the same masks after one 4-bit shift. Per sub-block the lane forms
+// T = sum q*x; the row gains d * sc * T - dmin * mn * sum(x). Partial sums are
+// reduced over the 16 lanes of a row with DPP and over the four wavefronts
+// through LDS, in a fixed order.
+#ifndef Q2K_GEMV_SEG_ITERS
+#define Q2K_GEMV_SEG_ITERS 4  // row quadruples per workgroup
+#endif
+
+// Raw buffer resources (gfx9 dword 3): loads past num_records return zero,
+// which is how lanes beyond the end of K read nothing.
+constexpr int kRsrcFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kRsrcFlags);
+}
+
+__device__ __forceinline__ void e4m3x4(uint32_t c, float *q) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c), false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c), true);
+    q[0] = lo[0];
+    q[1] = lo[1];
+    q[2] = hi[0];
+    q[3] = hi[1];
+}
+
+// Sum over each 16-lane DPP row; every lane of the row receives the total.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<kDppQuadXor1>(v);
+    v += dpp<kDppQuadXor2>(v);
+    v += dpp<kDppRowRor4>(v);
+    v += dpp<kDppRowRor8>(v);
+    return v;
+}
+
+struct SegLoads {
+    uint32_t q[4];   // the 16 code bytes of the segment
+    uint32_t sc[2];  // the 8 scale bytes of the segment's half
+    uint32_t dd;     // d, dmin
+};
+
+__device__ __forceinline__ SegLoads load_seg(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t g, uint32_t h) {
+    SegLoads t;
+    const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 + 16 * g, 0, 0);
+    const auto sc = __builtin_amdgcn_raw_buffer_load_b64(rs, off + 8 * h, 0, 0);
+    t.dd = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 80, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t.q[j] = q[j];
+    t.sc[0] = sc[0];
+    t.sc[1] = sc[1];
+    return t;
+}
+
+template <int M, int NI>
+__global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, const uint8_t *__restrict__ w,
+                                                  float *__restrict__ y, uint32_t N, uint32_t K) {
+    __shared__ float red[4][NI * 4 * M];
+    const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint32_t rr = lane >> 4, bq = (lane >> 2) & 3u, g = lane & 3u, h = g >> 1, s = g & 1u;
+    const uint32_t row0 = blockIdx.x * (4 * NI);
+    const uint32_t nb = K >> 8;
+    const uint32_t row_bytes = nb * kBlockBytes;
+
+    // One descriptor spans the workgroup's rows; a lane addresses its row with
+    // a 32-bit offset (rows past N reread row N-1 and are never stored). The
+    // host guarantees 4 * NI * row_bytes < 2^31.
+    const uint32_t nrows = min(4u * NI, N - row0);
+    const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(w + static_cast<uint64_t>(row0) * row_bytes, nrows * row_bytes);
+    uint32_t wrow[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) wrow[i] = min(4u * i + rr, nrows - 1) * row_bytes;
+    __amdgpu_buffer_rsrc_t xr[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) xr[m] = buffer_rsrc(x + static_cast<uint64_t>(m) * K, K * 4u);
+
+    float acc[NI][M];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[i][m] = 0.0f;
+
+    for (uint32_t kb0 = 0; kb0 < nb; kb0 += 16) {
+        const uint32_t kb = kb0 + 4 * wave + bq;
+        // Lanes past the end of K aim every weight load beyond the descriptor
+        // (they read zeros) and their activation loads beyond K (zeros too).
+        const uint32_t boff = kb < nb ? kb * kBlockBytes : 0x80000000u;
+
+        // Activations first (L2-resident, needed by every row), then each row
+        // quadruple's weights in the order they are used, so the arithmetic on
+        // the first rows overlaps the arrival of the later ones.
+        const uint32_t xoff = 4 * (kb * 256u + 128 * h + 16 * s);
+        float xv[M][4][16], xs[M][4];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr[m], xoff + 128 * p + 16 * i, 0, 0);
+                    // (Element copies go through a named temporary: this compiler folds
+                    // __builtin_bit_cast of a vector subscript to element 0.)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint32_t e = v[c];
+                        xv[m][p][4 * i + c] = __builtin_bit_cast(float, e);
+                    }
+                }
+        SegLoads wl[NI];
+#pragma unroll
+        for (int it = 0; it < NI; ++it) wl[it] = load_seg(wrs, wrow[it] + boff, g, h);
+        // Keep the scheduler from sinking these loads towards their uses.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                float t = xv[m][p][0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) t += xv[m][p][i];
+                xs[m][p] = t;
+            }
+
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+            const SegLoads &cur = wl[it];
+            // q[p][i]: code of byte i at position p, as q * 2^-9 (p even) or q * 2^-7 (p odd).
+            float q[4][16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t v = cur.q[j], u = v >> 4;
+                e4m3x4(v & 0x03030303u, &q[0][4 * j]);
+                e4m3x4(v & 0x0C0C0C0Cu, &q[1][4 * j]);
+                e4m3x4(u & 0x03030303u, &q[2][4 * j]);
+                e4m3x4(u & 0x0C0C0C0Cu, &q[3][4 * j]);
+            }
+            // Scale bytes 8h + 2p + s: bytes s and 2 + s of each scale dword.
+            const uint32_t u0 = cur.sc[0] >> (8 * s), u1 = cur.sc[1] >> (8 * s);
+            const uint32_t lo0 = u0 & 0x000F000Fu, hi0 = (u0 >> 4) & 0x000F000Fu;
+            const uint32_t lo1 = u1 & 0x000F000Fu, hi1 = (u1 >> 4) & 0x000F000Fu;
+            const float sc[4] = {static_cast<float>(lo0 & 0xffu), static_cast<float>(lo0 >> 16),
+                                 static_cast<float>(lo1 & 0xffu), static_cast<float>(lo1 >> 16)};
+            const float mn[4] = {static_cast<float>(hi0 & 0xffu), static_cast<float>(hi0 >> 16),
+                                 static_cast<float>(hi1 & 0xffu), static_cast<float>(hi1 >> 16)};
+            const float d = f16_low(cur.dd), dmin = f16_high(cur.dd);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float t[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    float a = q[p][0] * xv[m][p][0];
+#pragma unroll
+                    for (int i = 1; i < 16; ++i) a = __builtin_fmaf(q[p][i], xv[m][p][i], a);
+                    t[p] = a;
+                }
+                const float even = __builtin_fmaf(sc[2], t[2], sc[0] * t[0]);  // scaled by 2^-9
+                const float odd = __builtin_fmaf(sc[3], t[3], sc[1] * t[1]);   // scaled by 2^-7
+                const float codes = __builtin_fmaf(even, 512.0f, odd * 128.0f);
+                float mins = mn[0] * xs[m][0];
+#pragma unroll
+                for (int p = 1; p < 4; ++p) mins = __builtin_fmaf(mn[p], xs[m][p], mins);
+                const float a = __builtin_fmaf(d, codes, acc[it][m]);
+                acc[it][m] = __builtin_fmaf(-dmin, mins, a);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int it = 0; it < NI; ++it)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float v = row16_sum(acc[it][m]);
+            if ((lane & 15u) == 0) red[wave][(it * 4 + rr) * M + m] = v;
+        }
+    __syncthreads();
+    if (tid < NI * 4 * M) {
+        const uint32_t r = tid / M, m = tid % M, n = row0 + r;
+        if (n < N) y[static_cast<uint64_t>(m) * N + n] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Matrix-core path for M > 8: y = bf16(x) * bf16(W)^T with fp32 accumulation.
 //
 // A 256-thread workgroup computes a 128 x 128 tile of y. K advances one half
@@ -403,6 +601,14 @@ constexpr int gemv_rows() {
 }
 
 template <int M>
+hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, hipStream_t stream) {
+    constexpr int NI = Q2K_GEMV_SEG_ITERS;
+    const uint32_t blocks = (N + 4 * NI - 1) / (4 * NI);
+    hipLaunchKernelGGL((k_gemv_seg<M, NI>), dim3(blocks), dim3(256), 0, stream, x, w, y, N, K);
+    return hipGetLastError();
+}
+
+template <int M>
 hipError_t launch_gemv_m(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, hipStream_t stream) {
     constexpr int R = gemv_rows<M>();
     const uint32_t blocks = (N + R - 1) / R;
@@ -435,8 +641,8 @@ hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, 
 hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
                        hipStream_t stream) {
     switch (M) {
-        case 1: return launch_gemv_m<1>(x, w, y, N, K, stream);
-        case 2: return launch_gemv_m<2>(x, w, y, N, K, stream);
+        case 1: return launch_gemv_seg<1>(x, w, y, N, K, stream);
+        case 2: return launch_gemv_seg<2>(x, w, y, N, K, stream);
         case 3: return launch_gemv_m<3>(x, w, y, N, K, stream);
         case 4: return launch_gemv_m<4>(x, w, y, N, K, stream);
         case 5: return launch_gemv_m<5>(x, w, y, N, K, stream);

@@ -12,6 +12,7 @@ namespace q2k {
 constexpr uint32_t kQK = 256;          // weights per super-block
 constexpr uint32_t kBlockBytes = 84;   // bytes per super-block
 constexpr uint32_t kGemvMaxM = 8;      // largest M the fp32 GEMV handles
+constexpr uint32_t kMaxK = 1u << 24;   // keeps every per-workgroup byte offset below 2^31
 
 hipError_t launch_dequantize(const uint8_t *blocks, uint64_t nblocks, float *out, hipStream_t stream);
 
