@@ -11,7 +11,9 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <map>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "q2k_launch.h"
@@ -113,6 +115,39 @@ q2k_status status_word(StatusWord **out) {
     return Q2K_OK;
 }
 
+// The matrix-core path stages bf16(x) in a device workspace. One grow-only
+// workspace is kept per (device, stream); growth frees and reallocates it in
+// stream order, so work already queued on that stream keeps its buffer, and
+// calls on different streams never share one.
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+q2k_status stream_workspace(hipStream_t st, size_t bytes, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_error("hipGetDevice", e);
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    Workspace &w = g_ws[{dev, st}];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            e = hipFreeAsync(w.ptr, st);
+            if (e != hipSuccess) return device_error("hipFreeAsync(workspace)", e);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        e = hipMallocAsync(&w.ptr, bytes, st);
+        if (e != hipSuccess) return device_error("hipMallocAsync(workspace)", e);
+        w.bytes = bytes;
+    }
+    *out = w.ptr;
+    return Q2K_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,7 +197,10 @@ q2k_status q2k_matmul_path(const float *x, const void *w, float *y, uint32_t M, 
         if (M > q2k::kGemvMaxM) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul: the GEMV path takes M <= 8 (got %u)", M);
         e = q2k::launch_gemv(x, wb, y, M, N, K, st);
     } else if (path == Q2K_PATH_MFMA) {
-        e = q2k::launch_gemm_mfma(x, wb, y, M, N, K, st);
+        void *ws = nullptr;
+        s = stream_workspace(st, static_cast<size_t>(M) * K * 2, &ws);
+        if (s != Q2K_OK) return s;
+        e = q2k::launch_gemm_mfma(x, wb, y, M, N, K, ws, st);
     } else {
         return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul: unknown path %d", static_cast<int>(path));
     }

@@ -454,14 +454,18 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
 // ---------------------------------------------------------------------------
 // Matrix-core path for M > 8: y = bf16(x) * bf16(W)^T with fp32 accumulation.
 //
-// A 256-thread workgroup computes a 128 x 128 tile of y. K advances one half
-// super-block (128 weights) at a time: the x tile (f32) is rounded to bf16 and
-// the W tile is decoded and rounded to bf16, both into LDS, then each of the
-// four wavefronts runs a 2 x 2 grid of v_mfma_f32_32x32x16_bf16 on its 64 x 64
-// quadrant. A half super-block is self-contained: its 32 code bytes, its 8
-// scale bytes and the block's d and dmin.
-constexpr uint32_t kTileM = 128, kTileN = 128, kTileK = 128;
-constexpr uint32_t kLdsStride = kTileK + 8;  // bf16 per LDS row; padding spreads banks
+// k_x_to_bf16 rounds the activations to bf16 (nearest even) once, into a
+// workspace. k_gemm_q2k then computes a 256 (M) x 128 (N) tile of y per
+// 512-thread workgroup whose wavefronts specialise: four consumers each own a
+// 128 x 64 quadrant held as a 4 x 2 grid of v_mfma_f32_32x32x16_bf16
+// accumulators; four producers (one per SIMD beside a consumer) fetch, decode
+// and stage tiles, so decode arithmetic runs beside the matrix cores instead
+// of between their instructions. K advances 64 weights per step -- a quarter
+// super-block: 16 code bytes of each segment of one half, at two of the four
+// 2-bit positions, plus two scale bytes per segment -- through double-buffered
+// LDS tiles, with one workgroup barrier per step.
+constexpr uint32_t kGM = 256, kGN = 128, kGK = 64;
+constexpr uint32_t kGLd = kGK + 8;  // bf16 per LDS row (144 B): a fragment's 32 rows hit distinct banks
 
 __device__ __forceinline__ bf16x8 pack_bf16(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
                                             float a7) {
@@ -477,118 +481,202 @@ __device__ __forceinline__ bf16x8 pack_bf16(float a0, float a1, float a2, float 
     return v;
 }
 
-__global__ __launch_bounds__(256) void k_gemm_mfma(const float *__restrict__ x, const uint8_t *__restrict__ w,
-                                                   float *__restrict__ y, uint32_t M, uint32_t N, uint32_t K) {
-    __shared__ __attribute__((aligned(16))) __bf16 xs[kTileM * kLdsStride];
-    __shared__ __attribute__((aligned(16))) __bf16 ws[kTileN * kLdsStride];
+__global__ __launch_bounds__(256) void k_x_to_bf16(const float4 *__restrict__ x, bf16x8 *__restrict__ xb,
+                                                   uint64_t n8) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n8; i += stride) {
+        const float4 a = x[2 * i], b = x[2 * i + 1];
+        xb[i] = pack_bf16(a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w);
+    }
+}
 
-    const uint32_t tid = threadIdx.x;
-    const uint32_t lane = tid & 63u, wave = tid >> 6;
-    const uint32_t wm = wave >> 1, wn = wave & 1u;
-    const uint32_t tiles_n = (N + kTileN - 1) / kTileN;
-    const uint32_t n0 = (blockIdx.x % tiles_n) * kTileN, m0 = (blockIdx.x / tiles_n) * kTileM;
-    const uint32_t nb = K >> 8;
-    const uint64_t row_bytes = static_cast<uint64_t>(nb) * kBlockBytes;
+// Workgroups are dealt to the eight XCDs in turn (XCD = id % 8). When the tile
+// count allows, each XCD gets a contiguous band of N tiles with all their M
+// tiles, so the W rows its workgroups share stay in that XCD's L2.
+__device__ __forceinline__ void gemm_tile(uint32_t b, uint32_t tiles_m, uint32_t tiles_n, uint32_t *tm,
+                                          uint32_t *tn) {
+    const uint32_t total = tiles_m * tiles_n;
+    uint32_t idx = b;
+    if (total % 8 == 0) idx = (b / 8) + (b % 8) * (total / 8);
+    *tn = idx / tiles_m;
+    *tm = idx % tiles_m;
+}
 
-    // Staging role: tile row r, and which half of it (x: 64 k; W: one segment).
-    const uint32_t r = tid >> 1, part = tid & 1u;
+__global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb, const uint8_t *__restrict__ w,
+                                                  float *__restrict__ y, uint32_t M, uint32_t N, uint32_t K) {
+    __shared__ __attribute__((aligned(16))) __bf16 xs[2][kGM * kGLd];
+    __shared__ __attribute__((aligned(16))) __bf16 ws[2][kGN * kGLd];
 
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const bool producer = wave >= 4;  // waves 4..7 stage tiles, waves 0..3 run the MFMAs
+    uint32_t tm, tn;
+    gemm_tile(blockIdx.x, (M + kGM - 1) / kGM, (N + kGN - 1) / kGN, &tm, &tn);
+    const uint32_t m0 = tm * kGM, n0 = tn * kGN;
+    const uint32_t nb = K >> 8, row_bytes = nb * kBlockBytes;
+    const uint32_t steps = K / kGK;  // a multiple of 4
 
-    for (uint32_t kh = 0; kh < 2 * nb; ++kh) {
-        const uint32_t kb = kh >> 1, half = kh & 1u;
-        {   // x tile: row m0 + r, k = 128*kh + 64*part .. +64
-            const uint32_t m = m0 + r;
-            __bf16 *dst = xs + r * kLdsStride + part * 64;
-            if (m < M) {
-                const float4 *src = reinterpret_cast<const float4 *>(x + static_cast<uint64_t>(m) * K + kh * 128u + part * 64u);
+    if (producer) {
+        // ------------------------------------------------------------ producers
+        // Rows past M or N lie beyond these descriptors and load as zeros.
+        const __amdgpu_buffer_rsrc_t xr =
+            buffer_rsrc(xb + static_cast<uint64_t>(m0) * K, min(kGM, M - m0) * K * 2u);
+        const __amdgpu_buffer_rsrc_t wrs =
+            buffer_rsrc(w + static_cast<uint64_t>(n0) * row_bytes, min(kGN, N - n0) * row_bytes);
+        // Roles: activation chunk c = pt + 256 i of the 256 x 64 tile (row c / 8,
+        // bf16 column 8 (c % 8)); weights: row pt / 2, code segment pt % 2.
+        const uint32_t pt = threadIdx.x - 256u;
+        const uint32_t wrow = pt >> 1, seg = pt & 1u;
+
+        struct Stage {
+            uint32_t xq[8][4];  // eight 16-byte activation chunks
+            uint32_t qd[4];     // the segment's 16 code bytes
+            uint32_t sd;        // the two scale bytes of each position (one dword)
+            uint32_t dd;        // d, dmin
+        };
+        auto load_stage = [&](Stage &st, uint32_t step) {
+            const uint32_t k0 = step * kGK;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float4 a = src[2 * i], b = src[2 * i + 1];
-                    *reinterpret_cast<bf16x8 *>(dst + 8 * i) = pack_bf16(a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w);
-                }
-            } else {
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t c = pt + 256u * i;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, ((c >> 3) * K + k0 + 8 * (c & 7u)) * 2u, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    *reinterpret_cast<bf16x8 *>(dst + 8 * i) = pack_bf16(0, 0, 0, 0, 0, 0, 0, 0);
+                for (int e = 0; e < 4; ++e) st.xq[i][e] = v[e];
             }
-        }
-        {   // W tile: row n0 + r, segment `part` of half `half` of block kb
-            const uint32_t n = n0 + r;
-            __bf16 *dst = ws + r * kLdsStride + 16 * part;
-            if (n < N) {
-                const uint8_t *blk = w + n * row_bytes + static_cast<uint64_t>(kb) * kBlockBytes;
-                uint32_t qw[4];
+            const uint32_t kb = step >> 2, j = step & 3u, half = j >> 1;
+            const uint32_t off = wrow * row_bytes + kb * kBlockBytes;
+            const auto q = __builtin_amdgcn_raw_buffer_load_b128(wrs, off + 16 + 32 * half + 16 * seg, 0, 0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) qw[j] = load_u32(blk + 16 + 32 * half + 16 * part + 4 * j);
-                const uint32_t s_lo = load_u32(blk + 8 * half), s_hi = load_u32(blk + 8 * half + 4);
-                const uint32_t dd = load_u32(blk + 80);
-                const float d = f16_low(dd), dmin = f16_high(dd);
+            for (int e = 0; e < 4; ++e) st.qd[e] = q[e];
+            st.sd = __builtin_amdgcn_raw_buffer_load_b32(wrs, off + 8 * half + 4 * (j & 1u), 0, 0);
+            st.dd = __builtin_amdgcn_raw_buffer_load_b32(wrs, off + 80, 0, 0);
+        };
+        // Store a stage to LDS buffer `buf`: the activation chunks as they are,
+        // and 32 decoded, bf16-rounded weights. Quarter j of the block covers
+        // weights 64j..64j+63: half j/2, 2-bit positions p = 2(j%2) + pl
+        // (pl = 0, 1); local column 32 pl + 16 seg + i.
+        auto store_stage = [&](const Stage &st, uint32_t buf, uint32_t step) {
 #pragma unroll
-                for (uint32_t pos = 0; pos < 4; ++pos) {
-                    // scale byte 8*half + 2*pos + part
-                    const uint32_t sbyte = ((pos < 2 ? s_lo : s_hi) >> (8 * (2 * (pos & 1) + part))) & 0xffu;
-                    const float dl = d * static_cast<float>(sbyte & 15u);
-                    const float ml = dmin * static_cast<float>(sbyte >> 4);
-                    float wv[16];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t c = (qw[j] >> (2 * pos)) & 0x03030303u;
-                        wv[4 * j + 0] = dl * static_cast<float>(c & 0xffu) - ml;
-                        wv[4 * j + 1] = dl * static_cast<float>((c >> 8) & 0xffu) - ml;
-                        wv[4 * j + 2] = dl * static_cast<float>((c >> 16) & 0xffu) - ml;
-                        wv[4 * j + 3] = dl * static_cast<float>(c >> 24) - ml;
-                    }
-                    *reinterpret_cast<bf16x8 *>(dst + 32 * pos) =
-                        pack_bf16(wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]);
-                    *reinterpret_cast<bf16x8 *>(dst + 32 * pos + 8) =
-                        pack_bf16(wv[8], wv[9], wv[10], wv[11], wv[12], wv[13], wv[14], wv[15]);
-                }
-            } else {
-#pragma unroll
-                for (uint32_t pos = 0; pos < 4; ++pos) {
-                    *reinterpret_cast<bf16x8 *>(dst + 32 * pos) = pack_bf16(0, 0, 0, 0, 0, 0, 0, 0);
-                    *reinterpret_cast<bf16x8 *>(dst + 32 * pos + 8) = pack_bf16(0, 0, 0, 0, 0, 0, 0, 0);
-                }
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t c = pt + 256u * i;
+                uint4 v;
+                v.x = st.xq[i][0];
+                v.y = st.xq[i][1];
+                v.z = st.xq[i][2];
+                v.w = st.xq[i][3];
+                *reinterpret_cast<uint4 *>(&xs[buf][(c >> 3) * kGLd + 8 * (c & 7u)]) = v;
             }
-        }
+            const uint32_t j = step & 3u;
+            const float d = f16_low(st.dd), dmin = f16_high(st.dd);
+#pragma unroll
+            for (uint32_t pl = 0; pl < 2; ++pl) {
+                const uint32_t sbyte = (st.sd >> (8 * (2 * pl + seg))) & 0xffu;  // scale byte 8h + 2p + seg
+                // Codes arrive as e4m3 subnormals q * 2^-9; 2^9 is folded into dl (exact).
+                const float dl = d * static_cast<float>(sbyte & 15u) * kCodeScale;
+                const float ml = dmin * static_cast<float>(sbyte >> 4);
+                const uint32_t shift = 2 * (2 * (j & 1u) + pl);
+                float wv[16];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float q[4];
+                    e4m3x4((st.qd[e] >> shift) & 0x03030303u, q);
+                    // dl * q is exact, so the fused form rounds once, like dl * q - ml.
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) wv[4 * e + t] = __builtin_fmaf(dl, q[t], -ml);
+                }
+                __bf16 *dst = &ws[buf][wrow * kGLd + 32 * pl + 16 * seg];
+                *reinterpret_cast<bf16x8 *>(dst) = pack_bf16(wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]);
+                *reinterpret_cast<bf16x8 *>(dst + 8) =
+                    pack_bf16(wv[8], wv[9], wv[10], wv[11], wv[12], wv[13], wv[14], wv[15]);
+            }
+        };
+
+        // Step s: store stage s + 1 into buffer (s + 1) % 2 and request the raw
+        // bytes of step s + 3, from a ring of four register stages -- three
+        // steps of lead time for loads that mostly hit L2 at ~1 us latency.
+        Stage s0, s1, s2, s3;
+        auto step_body = [&](Stage &ld, uint32_t ld_step, const Stage &st, uint32_t st_step) {
+            if (ld_step < steps) load_stage(ld, ld_step);
+            if (st_step < steps) store_stage(st, st_step & 1u, st_step);
+            __syncthreads();
+        };
+        load_stage(s0, 0);
+        load_stage(s1, 1);
+        load_stage(s2, 2);
+        store_stage(s0, 0, 0);
         __syncthreads();
-#pragma unroll
-        for (uint32_t kk = 0; kk < kTileK / 16; ++kk) {
-            const uint32_t kcol = 16 * kk + 8 * (lane >> 5);
-            bf16x8 a[2], b[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                a[i] = *reinterpret_cast<const bf16x8 *>(xs + (wm * 64 + 32 * i + (lane & 31)) * kLdsStride + kcol);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                b[j] = *reinterpret_cast<const bf16x8 *>(ws + (wn * 64 + 32 * j + (lane & 31)) * kLdsStride + kcol);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (uint32_t step = 0; step < steps; step += 4) {
+            step_body(s3, step + 3, s1, step + 1);
+            step_body(s0, step + 4, s2, step + 2);
+            step_body(s1, step + 5, s3, step + 3);
+            step_body(s2, step + 6, s0, step + 4);
         }
+        return;
+    }
+
+    // ---------------------------------------------------------------- consumers
+    const uint32_t wm = wave >> 1, wn = wave & 1u;
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
+
+    // Fragments of one k16 slice: four 32 x 16 activation blocks and two
+    // 16 x 32 weight blocks (8 consecutive k per lane).
+    struct Frags {
+        bf16x8 a[4], b[2];
+    };
+    auto read_frags = [&](Frags &f, uint32_t buf, uint32_t kk) {
+        const uint32_t kcol = 16 * kk + 8 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            f.a[i] = *reinterpret_cast<const bf16x8 *>(&xs[buf][(128 * wm + 32 * i + (lane & 31u)) * kGLd + kcol]);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+            f.b[jj] = *reinterpret_cast<const bf16x8 *>(&ws[buf][(64 * wn + 32 * jj + (lane & 31u)) * kGLd + kcol]);
+    };
+    auto mfma_frags = [&](const Frags &f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[jj], acc[i][jj], 0, 0, 0);
+    };
+    // One step on buffer `buf`; each slice's fragments are read while the
+    // previous slice's MFMAs run.
+    auto mfma_step = [&](uint32_t buf) {
+        Frags f0, f1;
+        read_frags(f0, buf, 0);
+        read_frags(f1, buf, 1);
+        mfma_frags(f0);
+        read_frags(f0, buf, 2);
+        mfma_frags(f1);
+        read_frags(f1, buf, 3);
+        mfma_frags(f0);
+        mfma_frags(f1);
+    };
+
+    __syncthreads();  // stage 0 is in buffer 0
+    for (uint32_t step = 0; step < steps; step += 2) {
+        mfma_step(0);
+        __syncthreads();
+        mfma_step(1);
         __syncthreads();
     }
 
-    // D layout of a 32x32 MFMA tile: lane l holds column l % 32 and, in
-    // register v, row 8*(v/4) + 4*(l/32) + v%4.
+    // D layout of a 32x32 tile: lane l holds column l % 32, rows 8(v/4) + 4(l/32) + v%4.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t n = n0 + wn * 64 + 32 * j + (lane & 31);
+        for (int jj = 0; jj < 2; ++jj) {
+            const uint32_t n = n0 + 64 * wn + 32 * jj + (lane & 31u);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const uint32_t m = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (m < M && n < N) y[static_cast<uint64_t>(m) * N + n] = acc[i][j][v];
+                const uint32_t m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (m < M && n < N) y[static_cast<uint64_t>(m) * N + n] = acc[i][jj][v];
             }
         }
 }
@@ -654,10 +742,15 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, u
 }
 
 hipError_t launch_gemm_mfma(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
-                            hipStream_t stream) {
-    const uint64_t tiles = static_cast<uint64_t>((N + kTileN - 1) / kTileN) * ((M + kTileM - 1) / kTileM);
+                            void *x_bf16, hipStream_t stream) {
+    const uint64_t n8 = static_cast<uint64_t>(M) * K / 8;
+    const uint64_t want = (n8 + 255) / 256;
+    hipLaunchKernelGGL(k_x_to_bf16, dim3(static_cast<uint32_t>(want < 8192u ? want : 8192u)), dim3(256), 0, stream,
+                       reinterpret_cast<const float4 *>(x), static_cast<bf16x8 *>(x_bf16), n8);
+    const uint64_t tiles = static_cast<uint64_t>((N + kGN - 1) / kGN) * ((M + kGM - 1) / kGM);
     if (tiles > 0x7fffffffu) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_gemm_mfma, dim3(static_cast<uint32_t>(tiles)), dim3(256), 0, stream, x, w, y, M, N, K);
+    hipLaunchKernelGGL(k_gemm_q2k, dim3(static_cast<uint32_t>(tiles)), dim3(512), 0, stream,
+                       static_cast<const __bf16 *>(x_bf16), w, y, M, N, K);
     return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ namespace q2k {
 constexpr uint32_t kQK = 256;          // weights per super-block
 constexpr uint32_t kBlockBytes = 84;   // bytes per super-block
 constexpr uint32_t kGemvMaxM = 8;      // largest M the fp32 GEMV handles
-constexpr uint32_t kMaxK = 1u << 24;   // keeps every per-workgroup byte offset below 2^31
+constexpr uint32_t kMaxK = 1u << 21;   // keeps every per-workgroup byte offset below 2^31
 
 hipError_t launch_dequantize(const uint8_t *blocks, uint64_t nblocks, float *out, hipStream_t stream);
 
@@ -22,7 +22,9 @@ hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, 
 hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
                        hipStream_t stream);
 
+// Matrix-core path. x_bf16 is a device workspace of at least M * K * 2 bytes
+// (16-byte aligned) that receives bf16(x) before the GEMM reads it.
 hipError_t launch_gemm_mfma(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
-                            hipStream_t stream);
+                            void *x_bf16, hipStream_t stream);
 
 }  // namespace q2k

@@ -86,14 +86,17 @@ q2k_status q2k_dequantize(const void *blocks, size_t blocks_bytes, float *out, s
  *   x  device f32 [M, K] row-major; 16-byte aligned.
  *   w  device Q2_K bytes, N * K/256 * 84 long (layout above); 4-byte aligned.
  *   y  device f32 [M, N] row-major; 16-byte aligned.
- *   M, N >= 1; K a multiple of 256 with 256 <= K <= 2^24.
+ *   M, N >= 1; K a multiple of 256 with 256 <= K <= 2^21.
  * M <= 8 runs the fp32 GEMV: |y - exact| <= 1e-5 * sum_k |x*w| per output.
  * A row of y depends only on its own row of x: calls with the same M give it
  * bit-identical values whatever the other rows hold (M <= 2 and 3 <= M <= 8
  * run different kernels and may differ in the last bits).
  * M > 8 runs the matrix-core path on bf16(x) and bf16(w) with fp32
- * accumulation: |y - exact| <= 4e-3 * sum_k |x*w| + 1e-6.
- * Asynchronous on `stream`; allocates nothing.
+ * accumulation: |y - exact| <= 4e-3 * sum_k |x*w| + 1e-6. That path stages
+ * bf16(x) (2 * M * K bytes) in a device workspace that libq2k keeps per
+ * (device, stream): allocated in stream order on the first call that needs
+ * more, reused afterwards, never freed before the process ends.
+ * Asynchronous on `stream`.
  */
 q2k_status q2k_matmul(const float *x, const void *w, float *y, uint32_t M, uint32_t N, uint32_t K,
                       void *stream);

@@ -76,7 +76,7 @@ def test_dequantize_rejects_null_misaligned_and_overlap(lib):
 
 @pytest.mark.parametrize("M,N,K,frag", [
     (0, 8, 256, ">= 1"), (1, 0, 256, ">= 1"), (1, 8, 0, ">= 1"),
-    (1, 8, 100, "multiple of 256"), (4, 8, 255, "multiple of 256"), (1, 1, (1 << 24) + 256, "exceeds the limit"),
+    (1, 8, 100, "multiple of 256"), (4, 8, 255, "multiple of 256"), (1, 1, (1 << 21) + 256, "exceeds the limit"),
 ])
 def test_matmul_rejects_bad_shapes(lib, M, N, K, frag):
     _err(lib, lib.q2k_matmul(A, B, C, M, N, K, None), frag)
@@ -93,7 +93,7 @@ def test_matmul_rejects_null_misaligned_overlap_and_bad_path(lib):
 
 
 def test_matmul_rejects_size_overflow(lib):
-    _err(lib, lib.q2k_matmul(A, B, C, 0xFFFFFFFF, 0xFFFFFFFF, 1 << 24, None), "overflow")
+    _err(lib, lib.q2k_matmul(A, B, C, 0xFFFFFFFF, 0xFFFFFFFF, 1 << 21, None), "overflow")
 
 
 @pytest.mark.parametrize("vocab,dim,nt,frag", [
