@@ -455,17 +455,24 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
 // Matrix-core path for M > 8: y = bf16(x) * bf16(W)^T with fp32 accumulation.
 //
 // k_x_to_bf16 rounds the activations to bf16 (nearest even) once, into a
-// workspace. k_gemm_q2k then computes a 256 (M) x 128 (N) tile of y per
-// 512-thread workgroup whose wavefronts specialise: four consumers each own a
-// 128 x 64 quadrant held as a 4 x 2 grid of v_mfma_f32_32x32x16_bf16
-// accumulators; four producers (one per SIMD beside a consumer) fetch, decode
-// and stage tiles, so decode arithmetic runs beside the matrix cores instead
-// of between their instructions. K advances 64 weights per step -- a quarter
-// super-block: 16 code bytes of each segment of one half, at two of the four
-// 2-bit positions, plus two scale bytes per segment -- through double-buffered
-// LDS tiles, with one workgroup barrier per step.
-constexpr uint32_t kGM = 256, kGN = 128, kGK = 64;
-constexpr uint32_t kGLd = kGK + 8;  // bf16 per LDS row (144 B): a fragment's 32 rows hit distinct banks
+// workspace. k_gemm_q2k then computes a 128 (M) x 256 (N) tile of y per
+// 256-thread workgroup. Wavefront w owns columns 64w .. 64w+63 of the tile for
+// all 128 rows, as a 4 x 2 grid of v_mfma_f32_32x32x16_bf16 accumulators.
+// K advances 64 weights per step (a quarter super-block). The activation tile
+// (128 x 64 bf16) is staged through double-buffered LDS and shared by the four
+// wavefronts; the weights never touch LDS: each wavefront decodes its own 64
+// columns straight into MFMA B fragments, one step ahead of the MFMAs that
+// use them, so the decode arithmetic overlaps the matrix cores and LDS carries
+// only activations. One workgroup barrier per step.
+//
+// Inside a step the 64 k are taken in an order that suits the code bytes: the
+// k-chunk of 8 that MFMA slice kk gives to lane half kh (lanes 32kh .. 32kh+31)
+// is chunk 4 (kk / 2) + 2 kh + kk % 2 of the step, i.e. 2-bit position
+// 2 (j % 2) + kk / 2 (j = quarter of the block), code segment kh, code bytes
+// 8 (kk % 2) .. +7 of that segment. Activations are read from LDS in the same
+// order, so every product pairs x[m, k] with w[n, k].
+constexpr uint32_t kGM = 128, kGN = 256, kGK = 128;
+constexpr uint32_t kGLd = kGK + 8;  // bf16 per LDS row (144 B): a fragment's rows spread over the banks
 
 __device__ __forceinline__ bf16x8 pack_bf16(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
                                             float a7) {
@@ -481,10 +488,30 @@ __device__ __forceinline__ bf16x8 pack_bf16(float a0, float a1, float a2, float 
     return v;
 }
 
+// Each thread converts kXU chunks of 8 values per round, all loads first, so a
+// few hundred workgroups keep the whole 8 MB in flight (launching thousands of
+// small workgroups costs more than the copy itself at this size).
+constexpr uint32_t kXU = 4;
+
 __global__ __launch_bounds__(256) void k_x_to_bf16(const float4 *__restrict__ x, bf16x8 *__restrict__ xb,
                                                    uint64_t n8) {
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
-    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const uint64_t t = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    uint64_t base = 0;
+    // Whole rounds: every thread's kXU chunks are in range.
+    for (; base + kXU * stride <= n8; base += kXU * stride) {
+        float4 a[kXU], b[kXU];
+#pragma unroll
+        for (uint32_t u = 0; u < kXU; ++u) {
+            const uint64_t i = base + u * stride + t;
+            a[u] = x[2 * i];
+            b[u] = x[2 * i + 1];
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < kXU; ++u)
+            xb[base + u * stride + t] = pack_bf16(a[u].x, a[u].y, a[u].z, a[u].w, b[u].x, b[u].y, b[u].z, b[u].w);
+    }
+    for (uint64_t i = base + t; i < n8; i += stride) {
         const float4 a = x[2 * i], b = x[2 * i + 1];
         xb[i] = pack_bf16(a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w);
     }
@@ -502,120 +529,112 @@ __device__ __forceinline__ void gemm_tile(uint32_t b, uint32_t tiles_m, uint32_t
     *tm = idx % tiles_m;
 }
 
+// Raw bytes of one half super-block for one lane: for each of its two columns
+// the lane's 16-byte code segment and the half's 8 scale bytes, plus d, dmin.
+struct GemmRaw {
+    uint32_t q[2][4];
+    uint32_t sc[2][2];
+    uint32_t dd[2];
+};
+
 __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb, const uint8_t *__restrict__ w,
                                                   float *__restrict__ y, uint32_t M, uint32_t N, uint32_t K) {
-    __shared__ __attribute__((aligned(16))) __bf16 xs[2][kGM * kGLd];
-    __shared__ __attribute__((aligned(16))) __bf16 ws[2][kGN * kGLd];
+    // Eight wavefronts, two per SIMD: group g = wave / 4 runs the MFMAs of K
+    // half g for the whole 128 x 256 tile (wavefront wave % 4 owns columns
+    // 64 (wave % 4) .. +63), so while one wavefront of a SIMD waits on a
+    // barrier, LDS or memory, the other keeps the matrix core busy. Each group
+    // has two activation buffers of 128 x 64 bf16 (rows padded to 72); at the
+    // end the same memory carries the partial sums the groups exchange.
+    constexpr uint32_t kStepK = 64;
+    constexpr uint32_t kLd = kStepK + 8;
+    constexpr uint32_t kBuf = kGM * kLd;
+    constexpr uint32_t kXBytes = 2 * 2 * kBuf * 2;
+    constexpr uint32_t kSwapBytes = 8 * 64 * 64 * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kXBytes > kSwapBytes ? kXBytes : kSwapBytes];
+    __bf16 *xs = reinterpret_cast<__bf16 *>(smem);
 
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const bool producer = wave >= 4;  // waves 4..7 stage tiles, waves 0..3 run the MFMAs
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint32_t grp = wave >> 2, wq = wave & 3u;
+    const uint32_t gtid = tid & 255u;
+    const uint32_t kh = lane >> 5, col = lane & 31u;
     uint32_t tm, tn;
     gemm_tile(blockIdx.x, (M + kGM - 1) / kGM, (N + kGN - 1) / kGN, &tm, &tn);
     const uint32_t m0 = tm * kGM, n0 = tn * kGN;
     const uint32_t nb = K >> 8, row_bytes = nb * kBlockBytes;
-    const uint32_t steps = K / kGK;  // a multiple of 4
+    // Group g takes half-blocks [g nb, (g + 1) nb): 2 nb steps of 64 k each.
+    const uint32_t hb0 = grp * nb, s0 = 2 * hb0, steps = 2 * nb;
 
-    if (producer) {
-        // ------------------------------------------------------------ producers
-        // Rows past M or N lie beyond these descriptors and load as zeros.
-        const __amdgpu_buffer_rsrc_t xr =
-            buffer_rsrc(xb + static_cast<uint64_t>(m0) * K, min(kGM, M - m0) * K * 2u);
-        const __amdgpu_buffer_rsrc_t wrs =
-            buffer_rsrc(w + static_cast<uint64_t>(n0) * row_bytes, min(kGN, N - n0) * row_bytes);
-        // Roles: activation chunk c = pt + 256 i of the 256 x 64 tile (row c / 8,
-        // bf16 column 8 (c % 8)); weights: row pt / 2, code segment pt % 2.
-        const uint32_t pt = threadIdx.x - 256u;
-        const uint32_t wrow = pt >> 1, seg = pt & 1u;
+    // Rows past M or N lie beyond these descriptors and load as zeros.
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(xb + static_cast<uint64_t>(m0) * K, min(kGM, M - m0) * K * 2u);
+    const __amdgpu_buffer_rsrc_t wr =
+        buffer_rsrc(w + static_cast<uint64_t>(n0) * row_bytes, min(kGN, N - n0) * row_bytes);
 
-        struct Stage {
-            uint32_t xq[8][4];  // eight 16-byte activation chunks
-            uint32_t qd[4];     // the segment's 16 code bytes
-            uint32_t sd;        // the two scale bytes of each position (one dword)
-            uint32_t dd;        // d, dmin
-        };
-        auto load_stage = [&](Stage &st, uint32_t step) {
-            const uint32_t k0 = step * kGK;
+    // Activation staging: chunk c = gtid + 256 i (i < 4) of the group's 128 x 64
+    // tile is row c / 8, bf16 columns 8 (c % 8) .. +7; step s adds 128 bytes.
+    const uint32_t xg = ((gtid >> 3) * K + 8u * (gtid & 7u)) * 2u;  // + i * 32 rows
+    const uint32_t xl = grp * 2 * kBuf + (gtid >> 3) * kLd + 8u * (gtid & 7u);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 xq[4];
+    auto load_x = [&](uint32_t step) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t c = pt + 256u * i;
-                const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, ((c >> 3) * K + k0 + 8 * (c & 7u)) * 2u, 0, 0);
+        for (int i = 0; i < 4; ++i)
+            xq[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xg + i * 32u * K * 2u + step * 128u, 0, 0);
+    };
+    auto store_x = [&](uint32_t buf) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) st.xq[i][e] = v[e];
-            }
-            const uint32_t kb = step >> 2, j = step & 3u, half = j >> 1;
-            const uint32_t off = wrow * row_bytes + kb * kBlockBytes;
-            const auto q = __builtin_amdgcn_raw_buffer_load_b128(wrs, off + 16 + 32 * half + 16 * seg, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) st.qd[e] = q[e];
-            st.sd = __builtin_amdgcn_raw_buffer_load_b32(wrs, off + 8 * half + 4 * (j & 1u), 0, 0);
-            st.dd = __builtin_amdgcn_raw_buffer_load_b32(wrs, off + 80, 0, 0);
-        };
-        // Store a stage to LDS buffer `buf`: the activation chunks as they are,
-        // and 32 decoded, bf16-rounded weights. Quarter j of the block covers
-        // weights 64j..64j+63: half j/2, 2-bit positions p = 2(j%2) + pl
-        // (pl = 0, 1); local column 32 pl + 16 seg + i.
-        auto store_stage = [&](const Stage &st, uint32_t buf, uint32_t step) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t c = pt + 256u * i;
-                uint4 v;
-                v.x = st.xq[i][0];
-                v.y = st.xq[i][1];
-                v.z = st.xq[i][2];
-                v.w = st.xq[i][3];
-                *reinterpret_cast<uint4 *>(&xs[buf][(c >> 3) * kGLd + 8 * (c & 7u)]) = v;
-            }
-            const uint32_t j = step & 3u;
-            const float d = f16_low(st.dd), dmin = f16_high(st.dd);
-#pragma unroll
-            for (uint32_t pl = 0; pl < 2; ++pl) {
-                const uint32_t sbyte = (st.sd >> (8 * (2 * pl + seg))) & 0xffu;  // scale byte 8h + 2p + seg
-                // Codes arrive as e4m3 subnormals q * 2^-9; 2^9 is folded into dl (exact).
-                const float dl = d * static_cast<float>(sbyte & 15u) * kCodeScale;
-                const float ml = dmin * static_cast<float>(sbyte >> 4);
-                const uint32_t shift = 2 * (2 * (j & 1u) + pl);
-                float wv[16];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float q[4];
-                    e4m3x4((st.qd[e] >> shift) & 0x03030303u, q);
-                    // dl * q is exact, so the fused form rounds once, like dl * q - ml.
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) wv[4 * e + t] = __builtin_fmaf(dl, q[t], -ml);
-                }
-                __bf16 *dst = &ws[buf][wrow * kGLd + 32 * pl + 16 * seg];
-                *reinterpret_cast<bf16x8 *>(dst) = pack_bf16(wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]);
-                *reinterpret_cast<bf16x8 *>(dst + 8) =
-                    pack_bf16(wv[8], wv[9], wv[10], wv[11], wv[12], wv[13], wv[14], wv[15]);
-            }
-        };
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4 *>(&xs[buf * kBuf + xl + i * 32u * kLd]) = xq[i];
+    };
 
-        // Step s: store stage s + 1 into buffer (s + 1) % 2 and request the raw
-        // bytes of step s + 3, from a ring of four register stages -- three
-        // steps of lead time for loads that mostly hit L2 at ~1 us latency.
-        Stage s0, s1, s2, s3;
-        auto step_body = [&](Stage &ld, uint32_t ld_step, const Stage &st, uint32_t st_step) {
-            if (ld_step < steps) load_stage(ld, ld_step);
-            if (st_step < steps) store_stage(st, st_step & 1u, st_step);
-            __syncthreads();
-        };
-        load_stage(s0, 0);
-        load_stage(s1, 1);
-        load_stage(s2, 2);
-        store_stage(s0, 0, 0);
-        __syncthreads();
-        for (uint32_t step = 0; step < steps; step += 4) {
-            step_body(s3, step + 3, s1, step + 1);
-            step_body(s0, step + 4, s2, step + 2);
-            step_body(s1, step + 5, s3, step + 3);
-            step_body(s2, step + 6, s0, step + 4);
+    uint32_t wrow[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) wrow[jj] = (64u * wq + 32u * jj + col) * row_bytes;
+    auto load_raw = [&](GemmRaw &r, uint32_t hb) {
+        const uint32_t kb = hb >> 1, h = hb & 1u;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const uint32_t base = wrow[jj] + kb * kBlockBytes;
+            const auto q = __builtin_amdgcn_raw_buffer_load_b128(wr, base + 16u + 32u * h + 16u * kh, 0, 0);
+            const auto sc = __builtin_amdgcn_raw_buffer_load_b64(wr, base + 8u * h, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r.q[jj][e] = q[e];
+            r.sc[jj][0] = sc[0];
+            r.sc[jj][1] = sc[1];
+            r.dd[jj] = __builtin_amdgcn_raw_buffer_load_b32(wr, base + 80u, 0, 0);
         }
-        return;
-    }
+    };
+    // B fragments of MFMA slice kk (0..7) of a half-block, both columns: 2-bit
+    // position p = kk / 2, code bytes 8 (kk % 2) .. +7 of segment kh. The code
+    // bits become floats with the e4m3 trick: masked with 0x03 a byte is
+    // q * 2^-9, masked with 0x0C it is q * 2^-7 (positions 2 and 3 after a
+    // 4-bit shift). The power of two is folded into d * sc, so
+    // fma(dl, code, -ml) rounds d*sc*q - dmin*mn once, exactly as the decode
+    // rule, before the bf16 rounding.
+    auto decode = [&](const GemmRaw &r, int kk, bf16x8 (&b)[2]) {
+        const int p = kk >> 1, ih = kk & 1;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const float d = f16_low(r.dd[jj]), dmin = f16_high(r.dd[jj]);
+            const uint32_t sbyte = (r.sc[jj][p >> 1] >> (8u * kh + 16u * (p & 1))) & 0xffu;  // scale byte 2p + kh
+            const float dl = d * static_cast<float>(sbyte & 15u) * ((p & 1) == 0 ? 512.0f : 128.0f);
+            const float ml = dmin * static_cast<float>(sbyte >> 4);
+            const uint32_t mask = (p & 1) == 0 ? 0x03030303u : 0x0C0C0C0Cu;
+            float wv[8];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t v = r.q[jj][2 * ih + t];
+                const int c = static_cast<int>((p >= 2 ? (v >> 4) : v) & mask);
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
+                wv[4 * t + 0] = __builtin_fmaf(dl, lo[0], -ml);
+                wv[4 * t + 1] = __builtin_fmaf(dl, lo[1], -ml);
+                wv[4 * t + 2] = __builtin_fmaf(dl, hi[0], -ml);
+                wv[4 * t + 3] = __builtin_fmaf(dl, hi[1], -ml);
+            }
+            b[jj] = pack_bf16(wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]);
+        }
+    };
 
-    // ---------------------------------------------------------------- consumers
-    const uint32_t wm = wave >> 1, wn = wave & 1u;
     f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -624,61 +643,121 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
 
-    // Fragments of one k16 slice: four 32 x 16 activation blocks and two
-    // 16 x 32 weight blocks (8 consecutive k per lane).
-    struct Frags {
-        bf16x8 a[4], b[2];
+    // A fragment of slice kq (0..3 within a 64-k step), row block i: row
+    // 32 i + col, 8-element chunk 4 (kq / 2) + 2 kh + kq % 2 of the step.
+    const uint32_t a_lane = grp * 2 * kBuf + col * kLd + 16u * kh;
+    auto read_a = [&](bf16x8 (&a)[4], uint32_t buf, int kq) {
+        const uint32_t off = buf * kBuf + a_lane + 32u * (kq >> 1) + 8u * (kq & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(&xs[off + 32u * kLd * i]);
     };
-    auto read_frags = [&](Frags &f, uint32_t buf, uint32_t kk) {
-        const uint32_t kcol = 16 * kk + 8 * (lane >> 5);
+
+    // One 64-k step = slices 4 odd .. 4 odd + 3 of half-block rc (odd = which
+    // quarter of the half). Slice kq's MFMAs run while slice kq + 1 is read and
+    // decoded; during the last slice, the next step's slice 0 is decoded (from
+    // rn when the next step starts a new half-block) and read after the
+    // barrier that opens it.
+    bf16x8 af[2][4], bf[2][2];
+    auto step = [&](uint32_t buf, const GemmRaw &rc, int odd, const GemmRaw &rn) {
+        read_a(af[0], buf, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            f.a[i] = *reinterpret_cast<const bf16x8 *>(&xs[buf][(128 * wm + 32 * i + (lane & 31u)) * kGLd + kcol]);
+        for (int kq = 0; kq < 4; ++kq) {
+            if (kq < 3) {
+                read_a(af[(kq + 1) & 1], buf, kq + 1);
+                decode(rc, 4 * odd + kq + 1, bf[(kq + 1) & 1]);
+            } else if (odd == 0) {
+                decode(rc, 4, bf[0]);
+            } else {
+                decode(rn, 0, bf[0]);
+            }
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-            f.b[jj] = *reinterpret_cast<const bf16x8 *>(&ws[buf][(64 * wn + 32 * jj + (lane & 31u)) * kGLd + kcol]);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kq & 1][i], bf[kq & 1][jj], acc[i][jj], 0, 0, 0);
+        }
     };
-    auto mfma_frags = [&](const Frags &f) {
+
+    // Step s of the group (K step s0 + s): the barrier means every wavefront
+    // has finished step s - 1, so buffer (s + 1) % 2 is free for step s + 1's
+    // tile and buffer s % 2 holds step s's. Half-block hb + 1's bytes are
+    // requested at the start of half-block hb, two steps before their first
+    // use. Loads past the group's range read beyond it (the other group's
+    // columns, the next row, or zeros past the descriptors) and are never
+    // used; the store after the last step lands in a buffer nobody reads.
+    GemmRaw raw[2];
+    load_raw(raw[0], hb0);
+    load_x(s0);
+    store_x(0);
+    load_x(s0 + 1);
+    decode(raw[0], 0, bf[0]);
+    auto half = [&](uint32_t hl, GemmRaw &rc, GemmRaw &rn) {
+        // quarter 0 of the half
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        load_raw(rn, hb0 + hl + 1);
+        store_x(1);
+        load_x(s0 + 2 * hl + 2);
+        step(0, rc, 0, rn);
+        __builtin_amdgcn_sched_barrier(0);
+        // quarter 1 of the half
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        store_x(0);
+        load_x(s0 + 2 * hl + 3);
+        step(1, rc, 1, rn);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    uint32_t hl = 0;
+    for (; hl + 2 <= nb; hl += 2) {
+        half(hl, raw[0], raw[1]);
+        half(hl + 1, raw[1], raw[0]);
+    }
+    if (hl < nb) half(hl, raw[0], raw[1]);
+    (void)steps;
+
+    // The two K halves meet: group 1 hands over row blocks 0 and 1, group 0
+    // row blocks 2 and 3, lane-major (one dword per lane, rows of 64 lanes).
+    // Both groups add (lower half) + (upper half) in that order. The group
+    // index selects register blocks only through uniform branches, so the
+    // accumulators are never indexed at run time.
+    __syncthreads();
+    float *swap = reinterpret_cast<float *>(smem);
+    auto give = [&](int base) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[jj], acc[i][jj], 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    swap[((wave * 64u) + 32u * ii + 16u * jj + v) * 64u + lane] = acc[base + ii][jj][v];
     };
-    // One step on buffer `buf`; each slice's fragments are read while the
-    // previous slice's MFMAs run.
-    auto mfma_step = [&](uint32_t buf) {
-        Frags f0, f1;
-        read_frags(f0, buf, 0);
-        read_frags(f1, buf, 1);
-        mfma_frags(f0);
-        read_frags(f0, buf, 2);
-        mfma_frags(f1);
-        read_frags(f1, buf, 3);
-        mfma_frags(f0);
-        mfma_frags(f1);
-    };
-
-    __syncthreads();  // stage 0 is in buffer 0
-    for (uint32_t step = 0; step < steps; step += 2) {
-        mfma_step(0);
-        __syncthreads();
-        mfma_step(1);
-        __syncthreads();
-    }
-
+    if (grp == 0) give(2);
+    else give(0);
+    __syncthreads();
+    const uint32_t partner = wave ^ 4u;
     // D layout of a 32x32 tile: lane l holds column l % 32, rows 8(v/4) + 4(l/32) + v%4.
+    const bool full = m0 + kGM <= M && n0 + kGN <= N;
+    auto finish = [&](int base, bool lower_is_mine) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const uint32_t n = n0 + 64 * wn + 32 * jj + (lane & 31u);
+            for (int jj = 0; jj < 2; ++jj) {
+                const uint32_t i = base + ii;
+                const uint32_t n = n0 + 64u * wq + 32u * jj + col;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const uint32_t m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (m < M && n < N) y[static_cast<uint64_t>(m) * N + n] = acc[i][jj][v];
+                for (int v = 0; v < 16; ++v) {
+                    const float other = swap[((partner * 64u) + 32u * ii + 16u * jj + v) * 64u + lane];
+                    const float mine = acc[base + ii][jj][v];
+                    const float sum = lower_is_mine ? mine + other : other + mine;
+                    const uint32_t m = m0 + 32u * i + 8u * (v >> 2) + 4u * kh + (v & 3);
+                    if (full || (m < M && n < N)) y[static_cast<uint64_t>(m) * N + n] = sum;
+                }
+                __builtin_amdgcn_sched_barrier(0);  // one 16-value group live at a time
             }
-        }
+    };
+    if (grp == 0) finish(0, true);
+    else finish(2, false);
 }
 
 // Weight rows per workgroup: more rows amortise the activation loads, fewer
@@ -744,8 +823,8 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, u
 hipError_t launch_gemm_mfma(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
                             void *x_bf16, hipStream_t stream) {
     const uint64_t n8 = static_cast<uint64_t>(M) * K / 8;
-    const uint64_t want = (n8 + 255) / 256;
-    hipLaunchKernelGGL(k_x_to_bf16, dim3(static_cast<uint32_t>(want < 8192u ? want : 8192u)), dim3(256), 0, stream,
+    const uint64_t want = (n8 + 256 * kXU - 1) / (256 * kXU);
+    hipLaunchKernelGGL(k_x_to_bf16, dim3(static_cast<uint32_t>(want < 1024u ? want : 1024u)), dim3(256), 0, stream,
                        reinterpret_cast<const float4 *>(x), static_cast<bf16x8 *>(x_bf16), n8);
     const uint64_t tiles = static_cast<uint64_t>((N + kGN - 1) / kGN) * ((M + kGM - 1) / kGM);
     if (tiles > 0x7fffffffu) return hipErrorInvalidValue;
