@@ -98,8 +98,6 @@ constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
-constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> next row
-constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
 
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp(float v) {
@@ -109,18 +107,6 @@ __device__ __forceinline__ float dpp(float v) {
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
     return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the 64 lanes of a wavefront, in a fixed order; the total lands in
-// lanes 48..63 and is returned from lane 63 (uniform).
-__device__ __forceinline__ float wave_sum(float v) {
-    v += dpp<kDppQuadXor1>(v);
-    v += dpp<kDppQuadXor2>(v);
-    v += dpp<kDppRowRor4>(v);
-    v += dpp<kDppRowRor8>(v);          // every lane of a row holds its row sum
-    v += dpp<kDppRowBcast15, 0xA>(v);  // rows 1, 3 += rows 0, 2
-    v += dpp<kDppRowBcast31, 0xC>(v);  // rows 2, 3 += rows 0 + 1
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // The four code bytes of a dword at one 2-bit position, as floats q * 2^-9:
@@ -135,122 +121,6 @@ __device__ __forceinline__ void codes4(uint32_t v, uint32_t shift, float *q) {
     q[1] = lo[1];
     q[2] = hi[0];
     q[3] = hi[1];
-}
-
-// ---------------------------------------------------------------------------
-// fp32 GEMV for M <= 8: y[m, n] = sum_k x[m, k] * w[n, k].
-//
-// A 256-thread workgroup owns ROWS consecutive weight rows and covers 16
-// blocks (4096 weights) of K per pass. Thread t handles one sub-block: block
-// t / 16 of the pass; within it the segment group g = (t % 16) / 4 (half g/2,
-// segment g%2) and the 2-bit position p = t % 4. Its 16 weights share one
-// scale byte, so it accumulates s = sum q*x over them and adds dl*s - ml*sum(x).
-// The four threads of a quad share the segment's 16 code bytes: each loads one
-// dword and DPP broadcasts hand the other three around.
-//
-// All ROWS rows' loads are issued before any of them is used, so a workgroup
-// keeps ROWS * 21 bytes per thread in flight. Activations for the thread's 16
-// k stay in registers across the rows. Partial sums are reduced in a fixed
-// order (DPP within a wavefront, then the four wavefronts through LDS), and
-// every m runs the same instruction sequence, so a row of an M-row call equals
-// an M = 1 call on that row bit for bit.
-template <int M, int ROWS>
-__global__ __launch_bounds__(256) void k_gemv(const float *__restrict__ x, const uint8_t *__restrict__ w,
-                                              float *__restrict__ y, uint32_t N, uint32_t K) {
-    __shared__ float red[4][ROWS * M];
-    const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const uint32_t nb = K >> 8;
-    const uint64_t row_bytes = static_cast<uint64_t>(nb) * kBlockBytes;
-    const uint32_t row0 = blockIdx.x * ROWS;
-    const uint32_t bslot = tid >> 4;                  // block within the pass
-    const uint32_t grp = (tid >> 2) & 3u, pos = tid & 3u;
-    const uint32_t half = grp >> 1, seg = grp & 1u;
-    const uint32_t sb = 8 * half + 2 * pos + seg;     // scale byte index
-    const uint32_t koff = 128 * half + 32 * pos + 16 * seg;
-    const uint32_t qoff = 16 + 32 * half + 16 * seg + 4 * pos;  // this thread's dword of the segment
-    const uint32_t shift = 2 * pos;
-
-    float acc[ROWS][M];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-
-    for (uint32_t kb0 = 0; kb0 < nb; kb0 += 16) {
-        const uint32_t kb = kb0 + bslot;
-        const bool active = kb < nb;
-
-        uint32_t qd[ROWS], sbyte[ROWS], dd[ROWS];
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-            const uint32_t n = row0 + r;
-            qd[r] = 0;
-            sbyte[r] = 0;
-            dd[r] = 0;
-            if (active && n < N) {
-                const uint8_t *blk = w + n * row_bytes + static_cast<uint64_t>(kb) * kBlockBytes;
-                qd[r] = load_u32(blk + qoff);
-                sbyte[r] = blk[sb];
-                dd[r] = load_u32(blk + 80);
-            }
-        }
-
-        float xv[M][16];
-        float xsum[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            if (active) {
-                const float4 *xp = reinterpret_cast<const float4 *>(x + static_cast<uint64_t>(m) * K + kb * 256u + koff);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float4 v = xp[i];
-                    xv[m][4 * i + 0] = v.x;
-                    xv[m][4 * i + 1] = v.y;
-                    xv[m][4 * i + 2] = v.z;
-                    xv[m][4 * i + 3] = v.w;
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) xv[m][i] = 0.0f;
-            }
-            float s = xv[m][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) s += xv[m][i];
-            xsum[m] = s;
-        }
-
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-            float q[16];
-            codes4(dpp_u32<kDppQuadBcast0>(qd[r]), shift, q + 0);
-            codes4(dpp_u32<kDppQuadBcast1>(qd[r]), shift, q + 4);
-            codes4(dpp_u32<kDppQuadBcast2>(qd[r]), shift, q + 8);
-            codes4(dpp_u32<kDppQuadBcast3>(qd[r]), shift, q + 12);
-            const float dl = f16_low(dd[r]) * static_cast<float>(sbyte[r] & 15u) * kCodeScale;
-            const float ml = f16_high(dd[r]) * static_cast<float>(sbyte[r] >> 4);
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float t = q[0] * xv[m][0];
-#pragma unroll
-                for (int i = 1; i < 16; ++i) t = __builtin_fmaf(q[i], xv[m][i], t);
-                const float a = __builtin_fmaf(dl, t, acc[r][m]);
-                acc[r][m] = __builtin_fmaf(-ml, xsum[m], a);
-            }
-        }
-    }
-
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float s = wave_sum(acc[r][m]);
-            if (lane == 0) red[wave][r * M + m] = s;
-        }
-    __syncthreads();
-    if (tid < ROWS * M) {
-        const uint32_t r = tid / M, m = tid % M, n = row0 + r;
-        if (n < N) y[static_cast<uint64_t>(m) * N + n] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -452,6 +322,161 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
 }
 
 // ---------------------------------------------------------------------------
+// fp32 GEMV for 3 <= M <= 8 (batched decode).
+//
+// A 512-thread workgroup owns a run of consecutive weight rows and walks K in
+// chunks of 16 blocks (4096 weights). Lane l of wavefront w owns one
+// sub-block of the chunk: block 4 (w % 4) + l / 16, half h = (l / 8) % 2, code
+// segment s = (l / 4) % 2 and 2-bit position p = l % 4, i.e. the 16 weights
+// 128 h + 32 p + 16 s + i that share scale byte 8h + 2p + s. Its 16 * M
+// activations stay in registers while the workgroup sweeps its rows in
+// batches of R; wavefronts 0-3 take the even batches and 4-7 the odd ones,
+// two wavefronts per SIMD, so one's latency hides under the other's FMAs.
+// For each row the lane forms T_m = sum_i q_i x[m, i] and the partial
+// dl * T_m - ml * sum_i x[m, i]; the four lanes of a quad share the
+// segment's 16 code bytes (one dword each, passed around with DPP). A batch's
+// partials are summed over its four wavefronts through LDS in a fixed order
+// (lanes, then wavefronts) and added to per-row totals chunk by chunk, so each
+// output row depends only on its own activation row.
+constexpr uint32_t kGemvMaxBatches = 16;  // rows per workgroup <= 16 batches (host-checked)
+
+template <int M>
+struct GemvRowsCfg {
+    static constexpr int kR = M <= 5 ? 8 : 4;  // rows per batch (register budget)
+    static constexpr int kV = kR * M;          // partial sums per lane per batch
+};
+
+template <int M>
+__global__ __launch_bounds__(512) void k_gemv_rows(const float *__restrict__ x, const uint8_t *__restrict__ w,
+                                                   float *__restrict__ y, uint32_t N, uint32_t K, uint32_t rows_per_wg) {
+    constexpr int R = GemvRowsCfg<M>::kR, V = GemvRowsCfg<M>::kV;
+    __shared__ float red[2][4][V][kWave];
+    __shared__ float tot[kGemvMaxBatches][V];
+    const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint32_t par = wave >> 2, wq = wave & 3u;  // batch parity, block group
+    const uint32_t bq = lane >> 4, h = (lane >> 3) & 1u, sg = (lane >> 2) & 1u, p = lane & 3u;
+    const uint32_t nb = K >> 8, row_bytes = nb * kBlockBytes;
+    const uint32_t row0 = blockIdx.x * rows_per_wg;
+    const uint32_t nrows = min(rows_per_wg, N - row0);
+    const uint32_t batches = (nrows + R - 1) / R, pairs = (batches + 1) / 2;
+
+    // One descriptor over the workgroup's rows; rows past the end re-read the
+    // last row (never stored). The host keeps rows_per_wg * row_bytes below 2^31.
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(w + static_cast<uint64_t>(row0) * row_bytes, nrows * row_bytes);
+    __amdgpu_buffer_rsrc_t xr[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) xr[m] = buffer_rsrc(x + static_cast<uint64_t>(m) * K, K * 4u);
+
+    // Output (batch 2 i + par, value v) is finished by thread 256 par + 4 v + q;
+    // the thread with q = 0 keeps the running total over K chunks in tot.
+    const uint32_t ot = tid & 255u, ov = ot >> 2, oq = ot & 3u;
+
+    for (uint32_t kb0 = 0; kb0 < nb; kb0 += 16) {
+        const uint32_t kb = kb0 + 4 * wq + bq;
+        // Lanes past the end of K read zeros (activations beyond K, weights
+        // beyond the descriptor) and add nothing.
+        const uint32_t boff = kb < nb ? kb * kBlockBytes : 0x80000000u;
+        const uint32_t xoff = kb < nb ? 4u * (kb * 256u + 128u * h + 32u * p + 16u * sg) : 0x80000000u;
+        float xv[M][16], xs[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr[m], xoff + 16u * i, 0, 0);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t e = v[c];
+                    xv[m][4 * i + c] = __builtin_bit_cast(float, e);
+                }
+            }
+            float t = xv[m][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) t += xv[m][i];
+            xs[m] = t;
+        }
+
+        // Per row: the lane's dword of the segment's code bytes, the dword
+        // holding its scale byte, and the block's d, dmin.
+        struct RowLoads {
+            uint32_t q, sc, dd;
+        };
+        auto load_row = [&](uint32_t r) {
+            const uint32_t off = min(r, nrows - 1) * row_bytes + boff;
+            RowLoads t;
+            t.q = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 16u + 32u * h + 16u * sg + 4u * p, 0, 0);
+            t.sc = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 8u * h + 4u * (p >> 1), 0, 0);
+            t.dd = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 80u, 0, 0);
+            return t;
+        };
+        RowLoads cur[R], nxt[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) cur[r] = load_row(par * R + r);
+
+        for (uint32_t i = 0; i < pairs; ++i) {
+            const uint32_t g = 2 * i + par;
+#pragma unroll
+            for (int r = 0; r < R; ++r) nxt[r] = load_row((g + 2) * R + r);
+            float part[R][M];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t qd[4] = {dpp_u32<kDppQuadBcast0>(cur[r].q), dpp_u32<kDppQuadBcast1>(cur[r].q),
+                                        dpp_u32<kDppQuadBcast2>(cur[r].q), dpp_u32<kDppQuadBcast3>(cur[r].q)};
+                float q[16];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) codes4(qd[j], 2 * p, q + 4 * j);
+                // scale byte 8h + 2p + s is byte 2 (p % 2) + s of the dword loaded
+                const uint32_t sbyte = (cur[r].sc >> (8u * (2u * (p & 1u) + sg))) & 0xffu;
+                const float dl = f16_low(cur[r].dd) * static_cast<float>(sbyte & 15u) * kCodeScale;
+                const float ml = f16_high(cur[r].dd) * static_cast<float>(sbyte >> 4);
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    float t = q[0] * xv[m][0];
+#pragma unroll
+                    for (int k = 1; k < 16; ++k) t = __builtin_fmaf(q[k], xv[m][k], t);
+                    part[r][m] = __builtin_fmaf(dl, t, -(ml * xs[m]));
+                }
+            }
+            // Sum each batch over its four wavefronts: lanes 16 q .. 16 q + 15 of
+            // every wavefront by thread 4 v + q, in order, then the four q by DPP.
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m) red[par][wq][r * M + m][lane] = part[r][m];
+            __syncthreads();
+            float s = 0.0f;
+            if (ov < static_cast<uint32_t>(V)) {
+#pragma unroll
+                for (int wv = 0; wv < 4; ++wv) {
+                    const float4 *src = reinterpret_cast<const float4 *>(&red[par][wv][ov][16u * oq]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float4 a = src[j];
+                        s += a.x;
+                        s += a.y;
+                        s += a.z;
+                        s += a.w;
+                    }
+                }
+            }
+            s += dpp<kDppQuadXor1>(s);
+            s += dpp<kDppQuadXor2>(s);
+            if (oq == 0 && ov < static_cast<uint32_t>(V) && g < batches)
+                tot[g][ov] = (kb0 == 0 ? 0.0f : tot[g][ov]) + s;
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < R; ++r) cur[r] = nxt[r];
+        }
+    }
+
+    if (oq == 0 && ov < static_cast<uint32_t>(V)) {
+        const uint32_t r = ov / M, m = ov % M;
+        for (uint32_t g = par; g < batches; g += 2)
+            if (g * R + r < nrows) y[static_cast<uint64_t>(m) * N + row0 + g * R + r] = tot[g][ov];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Matrix-core path for M > 8: y = bf16(x) * bf16(W)^T with fp32 accumulation.
 //
 // k_x_to_bf16 rounds the activations to bf16 (nearest even) once, into a
@@ -472,7 +497,6 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
 // 8 (kk % 2) .. +7 of that segment. Activations are read from LDS in the same
 // order, so every product pairs x[m, k] with w[n, k].
 constexpr uint32_t kGM = 128, kGN = 256, kGK = 128;
-constexpr uint32_t kGLd = kGK + 8;  // bf16 per LDS row (144 B): a fragment's rows spread over the banks
 
 __device__ __forceinline__ bf16x8 pack_bf16(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
                                             float a7) {
@@ -760,13 +784,6 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
     else finish(2, false);
 }
 
-// Weight rows per workgroup: more rows amortise the activation loads, fewer
-// keep more workgroups in flight and bound registers as M grows.
-template <int M>
-constexpr int gemv_rows() {
-    return M <= 2 ? 8 : (M <= 4 ? 8 : 4);
-}
-
 template <int M>
 hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, hipStream_t stream) {
     constexpr int NI = Q2K_GEMV_SEG_ITERS;
@@ -775,11 +792,16 @@ hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t 
     return hipGetLastError();
 }
 
+// Rows per workgroup: enough workgroups to cover the 256 CUs once, each
+// sweeping whole batches of rows, at most kGemvMaxBatches of them.
 template <int M>
-hipError_t launch_gemv_m(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, hipStream_t stream) {
-    constexpr int R = gemv_rows<M>();
-    const uint32_t blocks = (N + R - 1) / R;
-    hipLaunchKernelGGL((k_gemv<M, R>), dim3(blocks), dim3(256), 0, stream, x, w, y, N, K);
+hipError_t launch_gemv_rows(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, hipStream_t stream) {
+    constexpr uint32_t R = GemvRowsCfg<M>::kR;
+    uint32_t rows = (N + 255) / 256;
+    rows = (rows + R - 1) / R * R;
+    if (rows > kGemvMaxBatches * R) rows = kGemvMaxBatches * R;
+    const uint32_t blocks = (N + rows - 1) / rows;
+    hipLaunchKernelGGL((k_gemv_rows<M>), dim3(blocks), dim3(512), 0, stream, x, w, y, N, K, rows);
     return hipGetLastError();
 }
 
@@ -810,12 +832,12 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, u
     switch (M) {
         case 1: return launch_gemv_seg<1>(x, w, y, N, K, stream);
         case 2: return launch_gemv_seg<2>(x, w, y, N, K, stream);
-        case 3: return launch_gemv_m<3>(x, w, y, N, K, stream);
-        case 4: return launch_gemv_m<4>(x, w, y, N, K, stream);
-        case 5: return launch_gemv_m<5>(x, w, y, N, K, stream);
-        case 6: return launch_gemv_m<6>(x, w, y, N, K, stream);
-        case 7: return launch_gemv_m<7>(x, w, y, N, K, stream);
-        case 8: return launch_gemv_m<8>(x, w, y, N, K, stream);
+        case 3: return launch_gemv_rows<3>(x, w, y, N, K, stream);
+        case 4: return launch_gemv_rows<4>(x, w, y, N, K, stream);
+        case 5: return launch_gemv_rows<5>(x, w, y, N, K, stream);
+        case 6: return launch_gemv_rows<6>(x, w, y, N, K, stream);
+        case 7: return launch_gemv_rows<7>(x, w, y, N, K, stream);
+        case 8: return launch_gemv_rows<8>(x, w, y, N, K, stream);
         default: return hipErrorInvalidValue;
     }
 }
