@@ -7,14 +7,25 @@ quoted on. Each step reads a different one of R byte-identical weight replicas
 (R * 5.5 MB >= 512 MiB, twice the 256 MiB Infinity Cache), so every step
 streams its weights from HBM. The other rows of the path (dequantize, gather,
 M = 8 GEMV, M = 512 matrix-core GEMM) are timed after the headline region and
-reported under "rows". The CPU oracle is timed on the host cores on a bounded
-sample and reported as "cpu_baseline".
+reported under "rows", each against the roofline that bounds it. The CPU
+oracle is timed on the host cores on a bounded sample and reported as
+"cpu_baseline".
+
+Other modes (used to collect rocprofv3 counters; they print one short JSON line):
+  --only ROW         run only one row's timed loop (gemv1, dequant, gather, gemv8, mfma)
+  --copy-probe       also run a device-to-device copy of COPY_BYTES (counter calibration)
+  --derive-traffic FETCH_CSV WRITE_CSV
+                     turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
+                     `--only gemv1 --copy-probe` into profiles/traffic.json: HBM bytes
+                     per GEMV launch, each counter scaled by known bytes / what it
+                     reads for the copy.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import math
@@ -30,8 +41,12 @@ BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 matrix (no sparsity)
 FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
 METRIC = "Q2_K matmul: GEMV HBM GB/s (M=1) and TFLOP/s at M=512, % of roofline"
 COLD_BYTES = 512 << 20          # rotate replicas over at least this many bytes
+COPY_BYTES = 256 << 20          # size of the calibration copy
 KERNEL_SRC = os.path.join(ROOT, "ggml_q2_dequant_amd", "csrc", "q2k_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GEMV_KERNEL = "k_gemv_seg<1"    # name prefix of the M = 1 GEMV kernel in rocprofv3 output
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+ROWS = ("gemv1", "dequant", "gather", "gemv8", "mfma")
 
 
 def log(msg: str) -> None:
@@ -57,7 +72,7 @@ def measured_traffic(kernel: str):
 
 
 def time_launches(torch, launch, n: int, warmup: int):
-    """Average device time per launch over n back-to-back launches (events on the launch stream)."""
+    """Average time per launch over n back-to-back launches, from events on the launch stream."""
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -86,6 +101,165 @@ def cpu_baseline(inp, budget_s: float):
     return el / reps, threads, reps
 
 
+# --------------------------------------------------------------------------- rocprofv3 counters
+
+def _per_dispatch(path: str, counter: str):
+    """{kernel name: [per-dispatch value]} for one counter of a rocprofv3 counter_collection.csv."""
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _pick(vals: dict, prefix: str):
+    got = [v for name, v in vals.items() if prefix in name]
+    if not got:
+        raise SystemExit("no dispatches of %r in the counter file" % prefix)
+    return [x for lst in got for x in lst]
+
+
+def derive_traffic(fetch_csv: str, write_csv: str) -> int:
+    fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(write_csv, "WRITE_SIZE")
+    copy_f = max(_pick(fetch, COPY_KERNEL))   # the calibration copy is the largest copy dispatch
+    copy_w = max(_pick(write, COPY_KERNEL))
+    known_kib = COPY_BYTES / 1024.0
+    rs, ws = known_kib / copy_f, known_kib / copy_w
+    gf, gw = _pick(fetch, GEMV_KERNEL), _pick(write, GEMV_KERNEL)
+    f_kib, w_kib = sum(gf) / len(gf), sum(gw) / len(gw)
+    hbm = (f_kib * rs + w_kib * ws) * 1024.0
+    rec = {}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        pass
+    rec["k_gemv_m1"] = {
+        "kernel_source_sha256": kernel_source_hash(),
+        "hbm_bytes_per_launch": round(hbm),
+        "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
+        "copy_bytes": COPY_BYTES, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+        "read_scale": rs, "write_scale": ws, "launches": len(gf),
+        "how": "rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE of `bench.py --only gemv1 --copy-probe`; "
+               "each counter scaled by known bytes / its reading for a %d-byte device copy" % COPY_BYTES,
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec["k_gemv_m1"]))
+    return 0
+
+
+# --------------------------------------------------------------------------- workloads
+
+class Bench:
+    def __init__(self, torch, q2k, synth, np):
+        self.torch, self.q2k, self.synth, self.np = torch, q2k, synth, np
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def gemv1_setup(self):
+        inp = self.synth.make_inputs(1)
+        c = inp.config
+        reps = max(1, math.ceil(COLD_BYTES / inp.blocks.size))
+        w_host = self.torch.from_numpy(inp.blocks)
+        self.g1 = dict(inp=inp, reps=reps, replicas=[w_host.to(self.dev) for _ in range(reps)],
+                       x=self.torch.from_numpy(inp.x).to(self.dev),
+                       y=self.torch.empty((c.M, c.N), dtype=self.torch.float32, device=self.dev),
+                       bytes=inp.blocks.size + c.M * c.K * 4 + c.M * c.N * 4)
+        lib = self.q2k.load_library()
+        g, st = self.g1, self.stream
+
+        def step(i):
+            rc = lib.q2k_matmul(g["x"].data_ptr(), g["replicas"][i % reps].data_ptr(), g["y"].data_ptr(),
+                                c.M, c.N, c.K, st)
+            if rc:
+                raise RuntimeError(lib.q2k_last_error_message().decode())
+        return step
+
+    def dequant(self, n=200):
+        g = self.g1
+        w_bytes = g["inp"].blocks.size
+        out = self.torch.empty(w_bytes // 84 * 256, dtype=self.torch.float32, device=self.dev)
+        b = w_bytes + out.numel() * 4
+        t = time_launches(self.torch, lambda i: self.q2k.q2k_dequantize(g["replicas"][i % g["reps"]], out,
+                                                                        stream=self.stream), n, 20)
+        gbs = b / t / 1e9
+        log("dequantize: %.2f us, %.1f GB/s" % (t * 1e6, gbs))
+        return {"workload": "%d blocks (the decode GEMV weights), cold replicas" % (w_bytes // 84),
+                "us": t * 1e6, "algorithmic_bytes": b, "GB/s": gbs, "bound": "hbm",
+                "frac_hbm": gbs / HBM_PEAK_GBS}
+
+    def gather(self, n=200):
+        np, torch = self.np, self.torch
+        log("generating gather inputs")
+        inp = self.synth.make_inputs(2)
+        c = inp.config
+        table = torch.from_numpy(inp.blocks).to(self.dev)
+        rng = np.random.Generator(np.random.PCG64(2000))
+        id_sets = [torch.from_numpy(rng.integers(0, c.vocab, c.n_tokens).astype(np.int32)).to(self.dev)
+                   for _ in range(64)]
+        outs = [torch.empty((c.n_tokens, c.embed_dim), dtype=torch.float32, device=self.dev) for _ in range(8)]
+        b = c.n_tokens * (c.embed_dim // 256) * 84 + c.n_tokens * c.embed_dim * 4 + c.n_tokens * 4
+        t = time_launches(torch, lambda i: self.q2k.q2k_embedding_gather(table, id_sets[i % 64], outs[i % 8],
+                                                                         c.vocab, c.embed_dim, c.n_tokens,
+                                                                         stream=self.stream), n, 20)
+        gbs = b / t / 1e9
+        log("gather: %.2f us/call (synchronous), %.1f GB/s" % (t * 1e6, gbs))
+        return {"workload": "512 ids into a 262144 x 4096 table (64 rotating id sets); the call waits for "
+                            "its id check", "us_per_call_incl_sync": t * 1e6, "algorithmic_bytes": b,
+                "GB/s": gbs, "bound": "hbm", "frac_hbm": gbs / HBM_PEAK_GBS}
+
+    def gemv8(self, n=300):
+        torch = self.torch
+        log("generating M=8 GEMV inputs")
+        inp = self.synth.make_inputs(3)
+        c = inp.config
+        w3 = torch.from_numpy(inp.blocks)
+        reps = max(1, math.ceil(COLD_BYTES / inp.blocks.size))
+        wr = [w3.to(self.dev) for _ in range(reps)]
+        x = torch.from_numpy(inp.x).to(self.dev)
+        y = torch.empty((c.M, c.N), dtype=torch.float32, device=self.dev)
+        t = time_launches(torch, lambda i: self.q2k.q2k_matmul(x, wr[i % reps], y, c.M, c.N, c.K,
+                                                               stream=self.stream), n, 30)
+        b = inp.blocks.size + c.M * c.K * 4 + c.M * c.N * 4
+        f = 2.0 * c.M * c.N * c.K
+        log("GEMV M=8: %.2f us, %.1f GB/s, %.2f TFLOP/s" % (t * 1e6, b / t / 1e9, f / t / 1e12))
+        return {"workload": "M=8 N=14336 K=4096 (%d cold weight replicas)" % reps, "us": t * 1e6,
+                "algorithmic_bytes": b, "flop": f, "GB/s": b / t / 1e9, "TFLOP/s": f / t / 1e12,
+                "bound": "alu", "frac_fp32": f / t / 1e12 / FP32_PEAK_TFLOPS,
+                "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
+
+    def mfma(self, n=50):
+        torch = self.torch
+        log("generating M=512 inputs")
+        inp = self.synth.make_inputs(4)
+        c = inp.config
+        w = torch.from_numpy(inp.blocks).to(self.dev)
+        x = torch.from_numpy(inp.x).to(self.dev)
+        y = torch.empty((c.M, c.N), dtype=torch.float32, device=self.dev)
+        t = time_launches(torch, lambda i: self.q2k.q2k_matmul(x, w, y, c.M, c.N, c.K, stream=self.stream), n, 5)
+        f = 2.0 * c.M * c.N * c.K
+        log("MFMA M=512: %.2f us, %.1f TFLOP/s" % (t * 1e6, f / t / 1e12))
+        return {"workload": "M=512 N=14336 K=4096 (one call: bf16(x) pre-pass + GEMM)", "us": t * 1e6,
+                "flop": f, "TFLOP/s": f / t / 1e12, "bound": "mfma",
+                "frac_bf16_mfma": f / t / 1e12 / BF16_PEAK_TFLOPS}
+
+    def copy_probe(self):
+        torch = self.torch
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=self.dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: %d bytes" % COPY_BYTES)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,7 +267,13 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
+    ap.add_argument("--only", choices=ROWS, help="run only this row's timed loop")
+    ap.add_argument("--copy-probe", action="store_true", help="also run the calibration copy")
+    ap.add_argument("--derive-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+
+    if args.derive_traffic:
+        return derive_traffic(*args.derive_traffic)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -107,110 +287,55 @@ def main() -> int:
     import synth
 
     q2k.load_library()
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream().cuda_stream
+    b = Bench(torch, q2k, synth, np)
 
-    # ---------------------------------------------------------------- headline: decode GEMV
+    if args.only:
+        out = {"only": args.only}
+        if args.copy_probe:
+            b.copy_probe()
+        if args.only in ("gemv1", "dequant"):
+            step = b.gemv1_setup()
+            if args.only == "gemv1":
+                t = time_launches(torch, step, args.steps, args.warmup)
+                out.update(us=t * 1e6, GBs=b.g1["bytes"] / t / 1e9)
+            else:
+                out.update(b.dequant(args.steps))
+        else:
+            out.update(getattr(b, args.only)(args.steps))
+        print(json.dumps(out), flush=True)
+        return 0
+
+    # ------------------------------------------------------------------- headline: decode GEMV
     log("generating decode GEMV inputs")
-    inp1 = synth.make_inputs(1)
-    c1 = inp1.config
-    w_bytes = inp1.blocks.size
-    algo_bytes = w_bytes + c1.M * c1.K * 4 + c1.M * c1.N * 4
-    reps = max(1, math.ceil(COLD_BYTES / w_bytes))
-    w_host = torch.from_numpy(inp1.blocks)
-    replicas = [w_host.to(dev) for _ in range(reps)]
-    x1 = torch.from_numpy(inp1.x).to(dev)
-    y1 = torch.empty((c1.M, c1.N), dtype=torch.float32, device=dev)
-    lib = q2k.load_library()
-
-    def gemv_step(i):
-        rc = lib.q2k_matmul(x1.data_ptr(), replicas[i % reps].data_ptr(), y1.data_ptr(), c1.M, c1.N, c1.K, stream)
-        if rc:
-            raise RuntimeError(lib.q2k_last_error_message().decode())
-
-    log("timing %d GEMV steps (%d warmup) over %d weight replicas" % (args.steps, args.warmup, reps))
+    step = b.gemv1_setup()
+    g = b.g1
+    c1 = g["inp"].config
+    log("timing %d GEMV steps (%d warmup) over %d weight replicas" % (args.steps, args.warmup, g["reps"]))
     for i in range(args.warmup):
-        gemv_step(i)
+        step(i)
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record()
     for i in range(args.steps):
-        gemv_step(i)
+        step(i)
     t_end.record()
     torch.cuda.synchronize()
     sec_per_step = t_start.elapsed_time(t_end) * 1e-3 / args.steps
-    gbs = algo_bytes / sec_per_step / 1e9
+    gbs = g["bytes"] / sec_per_step / 1e9
     log("GEMV M=1: %.3f us/step, %.1f GB/s" % (sec_per_step * 1e6, gbs))
 
     rows = {}
     if not args.no_rows:
-        # ------------------------------------------------------------ dequantize (write-bound stream)
-        out_dq = torch.empty(w_bytes // 84 * 256, dtype=torch.float32, device=dev)
-        dq_bytes = w_bytes + out_dq.numel() * 4
-        t = time_launches(torch, lambda i: q2k.q2k_dequantize(replicas[i % reps], out_dq, stream=stream), 200, 20)
-        rows["dequantize"] = {"workload": "%d blocks (the decode GEMV weights)" % (w_bytes // 84),
-                              "us": t * 1e6, "GB/s": dq_bytes / t / 1e9,
-                              "frac_hbm": dq_bytes / t / 1e9 / HBM_PEAK_GBS}
-        log("dequantize: %.2f us, %.1f GB/s" % (t * 1e6, dq_bytes / t / 1e9))
-        del out_dq
+        rows["dequantize"] = b.dequant()
+        rows["gather"] = b.gather()
+        rows["gemv_m8"] = b.gemv8()
+        rows["mfma_m512"] = b.mfma()
 
-        # ------------------------------------------------------------ gather
-        log("generating gather inputs")
-        inp2 = synth.make_inputs(2)
-        c2 = inp2.config
-        table = torch.from_numpy(inp2.blocks).to(dev)
-        rng = np.random.Generator(np.random.PCG64(2000))
-        id_sets = [torch.from_numpy(rng.integers(0, c2.vocab, c2.n_tokens).astype(np.int32)).to(dev)
-                   for _ in range(64)]
-        outs = [torch.empty((c2.n_tokens, c2.embed_dim), dtype=torch.float32, device=dev) for _ in range(8)]
-        g_bytes = c2.n_tokens * (c2.embed_dim // 256) * 84 + c2.n_tokens * c2.embed_dim * 4 + c2.n_tokens * 4
-        t = time_launches(torch, lambda i: q2k.q2k_embedding_gather(table, id_sets[i % 64], outs[i % 8], c2.vocab,
-                                                                    c2.embed_dim, c2.n_tokens, stream=stream),
-                          200, 20)
-        rows["gather"] = {"workload": "512 ids into a 262144 x 4096 table (64 rotating id sets)",
-                          "us_per_call_incl_sync": t * 1e6, "GB/s": g_bytes / t / 1e9,
-                          "frac_hbm": g_bytes / t / 1e9 / HBM_PEAK_GBS}
-        log("gather: %.2f us/call (synchronous), %.1f GB/s" % (t * 1e6, g_bytes / t / 1e9))
-        del table, outs, id_sets, inp2
-
-        # ------------------------------------------------------------ M = 8 GEMV
-        log("generating M=8 GEMV inputs")
-        inp3 = synth.make_inputs(3)
-        c3 = inp3.config
-        w3 = torch.from_numpy(inp3.blocks)
-        reps3 = max(1, math.ceil(COLD_BYTES / inp3.blocks.size))
-        w3r = [w3.to(dev) for _ in range(reps3)]
-        x3 = torch.from_numpy(inp3.x).to(dev)
-        y3 = torch.empty((c3.M, c3.N), dtype=torch.float32, device=dev)
-        t = time_launches(torch, lambda i: q2k.q2k_matmul(x3, w3r[i % reps3], y3, c3.M, c3.N, c3.K, stream=stream),
-                          300, 30)
-        b3 = inp3.blocks.size + c3.M * c3.K * 4 + c3.M * c3.N * 4
-        f3 = 2.0 * c3.M * c3.N * c3.K
-        rows["gemv_m8"] = {"workload": "M=8 N=14336 K=4096 (%d weight replicas)" % reps3, "us": t * 1e6,
-                           "GB/s": b3 / t / 1e9, "TFLOP/s": f3 / t / 1e12,
-                           "frac_hbm": b3 / t / 1e9 / HBM_PEAK_GBS, "frac_fp32": f3 / t / 1e12 / FP32_PEAK_TFLOPS}
-        log("GEMV M=8: %.2f us, %.1f GB/s, %.2f TFLOP/s" % (t * 1e6, b3 / t / 1e9, f3 / t / 1e12))
-        del w3r
-
-        # ------------------------------------------------------------ M = 512 matrix-core path
-        log("generating M=512 inputs")
-        inp4 = synth.make_inputs(4)
-        c4 = inp4.config
-        w4 = torch.from_numpy(inp4.blocks).to(dev)
-        x4 = torch.from_numpy(inp4.x).to(dev)
-        y4 = torch.empty((c4.M, c4.N), dtype=torch.float32, device=dev)
-        t = time_launches(torch, lambda i: q2k.q2k_matmul(x4, w4, y4, c4.M, c4.N, c4.K, stream=stream), 50, 5)
-        f4 = 2.0 * c4.M * c4.N * c4.K
-        rows["mfma_m512"] = {"workload": "M=512 N=14336 K=4096", "us": t * 1e6, "TFLOP/s": f4 / t / 1e12,
-                             "frac_bf16_mfma": f4 / t / 1e12 / BF16_PEAK_TFLOPS}
-        log("MFMA M=512: %.2f us, %.1f TFLOP/s" % (t * 1e6, f4 / t / 1e12))
-        del w4, x4, y4
-
-    # ---------------------------------------------------------------- CPU oracle baseline
+    # ------------------------------------------------------------------- CPU oracle baseline
     log("timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
-    sec_cpu, threads, cpu_reps = cpu_baseline(inp1, args.cpu_seconds)
-    cpu_gbs = algo_bytes / sec_cpu / 1e9
+    sec_cpu, threads, cpu_reps = cpu_baseline(g["inp"], args.cpu_seconds)
+    cpu_gbs = g["bytes"] / sec_cpu / 1e9
 
     result = {
         "metric": METRIC,
@@ -226,15 +351,15 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": c1.name + " (Q2_K weights, f32 activations, cold weights)",
-                   "M": c1.M, "N": c1.N, "K": c1.K, "weight_replicas": reps,
-                   "algorithmic_bytes_per_step": algo_bytes, "parallelism": "single GPU"},
+                   "M": c1.M, "N": c1.N, "K": c1.K, "weight_replicas": g["reps"],
+                   "algorithmic_bytes_per_step": g["bytes"], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("k_gemv_m1")},
         "cpu_baseline": {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
                          "sample": "the whole decode GEMV workload (M=1, N=K=4096), %d calls of the f64 "
-                                   "oracle matmul, %.3f s per call" % (cpu_reps, sec_cpu)},
+                                   "oracle matmul, %.4f s per call" % (cpu_reps, sec_cpu)},
         "rows": rows,
-        "input_sha256": inp1.hashes,
+        "input_sha256": g["inp"].hashes,
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -496,7 +496,7 @@ __global__ __launch_bounds__(512) void k_gemv_rows(const float *__restrict__ x, 
 // 2 (j % 2) + kk / 2 (j = quarter of the block), code segment kh, code bytes
 // 8 (kk % 2) .. +7 of that segment. Activations are read from LDS in the same
 // order, so every product pairs x[m, k] with w[n, k].
-constexpr uint32_t kGM = 128, kGN = 256, kGK = 128;
+constexpr uint32_t kGM = 128, kGN = 256;
 
 __device__ __forceinline__ bf16x8 pack_bf16(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
                                             float a7) {
