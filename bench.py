@@ -6,13 +6,13 @@ Timed step: one q2k_matmul call on the decode GEMV workload (M = 1, N = K =
 quoted on. Each step reads a different one of R byte-identical weight replicas
 (R * 5.5 MB >= 512 MiB, twice the 256 MiB Infinity Cache), so every step
 streams its weights from HBM. The other rows of the path (dequantize, gather,
-M = 8 GEMV, M = 512 matrix-core GEMM) are timed after the headline region and
+M = 8 GEMV, M = 512 matrix-core GEMM, batched mat-vec) are timed after the headline region and
 reported under "rows", each against the roofline that bounds it. The CPU
 oracle is timed on the host cores on a bounded sample and reported as
 "cpu_baseline".
 
 Other modes (used to collect rocprofv3 counters; they print one short JSON line):
-  --only ROW         run only one row's timed loop (gemv1, dequant, gather, gemv8, mfma)
+  --only ROW         run only one row's timed loop (gemv1, dequant, gather, gemv8, mfma, batched)
   --copy-probe       also run a device-to-device copy of COPY_BYTES (counter calibration)
   --derive-traffic FETCH_CSV WRITE_CSV
                      turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
@@ -46,7 +46,7 @@ KERNEL_SRC = os.path.join(ROOT, "ggml_q2_dequant_amd", "csrc", "q2k_kernels.hip"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMV_KERNEL = "k_gemv_seg<1"    # name prefix of the M = 1 GEMV kernel in rocprofv3 output
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-ROWS = ("gemv1", "dequant", "gather", "gemv8", "mfma")
+ROWS = ("gemv1", "dequant", "gather", "gemv8", "mfma", "batched")
 
 
 def log(msg: str) -> None:
@@ -249,6 +249,25 @@ class Bench:
                 "flop": f, "TFLOP/s": f / t / 1e12, "bound": "mfma",
                 "frac_bf16_mfma": f / t / 1e12 / BF16_PEAK_TFLOPS}
 
+    def batched(self, n=200):
+        """Batched mat-vec: 8 independent decode GEMVs (M=1, N=K=4096) in one call, cold weights."""
+        torch, np = self.torch, self.np
+        bt, M, N, K = 8, 1, 4096, 4096
+        rng = np.random.Generator(np.random.PCG64(3000))
+        blocks = self.synth.random_blocks(rng, bt * N * K // 256)
+        x = torch.from_numpy(rng.standard_normal((bt, M, K), dtype=np.float32)).to(self.dev)
+        reps = max(1, math.ceil(COLD_BYTES / blocks.size))
+        wh = torch.from_numpy(blocks)
+        wr = [wh.to(self.dev) for _ in range(reps)]
+        y = torch.empty((bt, M, N), dtype=torch.float32, device=self.dev)
+        t = time_launches(torch, lambda i: self.q2k.q2k_matmul_batched(x, wr[i % reps], y, bt, M, N, K,
+                                                                       stream=self.stream), n, 20)
+        b = blocks.size + bt * M * K * 4 + bt * M * N * 4
+        log("batched mat-vec 8 x (M=1, N=K=4096): %.2f us, %.1f GB/s" % (t * 1e6, b / t / 1e9))
+        return {"workload": "8 matrices x (M=1, N=K=4096) in one call, %d cold weight replicas" % reps,
+                "us": t * 1e6, "algorithmic_bytes": b, "GB/s": b / t / 1e9, "bound": "hbm",
+                "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
+
     def copy_probe(self):
         torch = self.torch
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=self.dev)
@@ -331,6 +350,7 @@ def main() -> int:
         rows["gather"] = b.gather()
         rows["gemv_m8"] = b.gemv8()
         rows["mfma_m512"] = b.mfma()
+        rows["batched_mv"] = b.batched()
 
     # ------------------------------------------------------------------- CPU oracle baseline
     log("timing the CPU oracle (~%.0f s)" % args.cpu_seconds)

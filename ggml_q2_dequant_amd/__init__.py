@@ -10,6 +10,8 @@ Functions carry the C names:
 * ``q2k_dequantize(blocks, out)`` — decode whole 84-byte blocks to f32.
 * ``q2k_matmul(x, w, y, M, N, K)`` — y[M, N] = x[M, K] * W[N, K]^T, W in Q2_K.
 * ``q2k_matmul_path(x, w, y, M, N, K, path)`` — same with a forced kernel.
+* ``q2k_matmul_batched(x, w, y, batches, M, N, K)`` — independent products, one
+  per matrix of a batch-major stack (1 <= M <= 8).
 * ``q2k_embedding_gather(table, ids, out, vocab, embed_dim, n_tokens)`` — rows
   of a Q2_K table; raises ``Q2KIdOutOfRange`` for an id >= vocab.
 
@@ -41,6 +43,7 @@ EXPORTS = (
     "q2k_dequantize",
     "q2k_matmul",
     "q2k_matmul_path",
+    "q2k_matmul_batched",
     "q2k_embedding_gather",
     "q2k_status_string",
     "q2k_last_error_message",
@@ -83,8 +86,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.q2k_dequantize.argtypes = [P, SZ, P, SZ, P]
     lib.q2k_matmul.argtypes = [P, P, P, U32, U32, U32, P]
     lib.q2k_matmul_path.argtypes = [P, P, P, U32, U32, U32, ctypes.c_int, P]
+    lib.q2k_matmul_batched.argtypes = [P, P, P, U32, U32, U32, U32, P]
     lib.q2k_embedding_gather.argtypes = [P, P, P, U32, U32, U32, P]
-    for name in ("q2k_dequantize", "q2k_matmul", "q2k_matmul_path", "q2k_embedding_gather"):
+    for name in ("q2k_dequantize", "q2k_matmul", "q2k_matmul_path", "q2k_matmul_batched", "q2k_embedding_gather"):
         getattr(lib, name).restype = ctypes.c_int
     lib.q2k_status_string.argtypes = [ctypes.c_int]
     lib.q2k_status_string.restype = ctypes.c_char_p
@@ -147,6 +151,11 @@ def q2k_matmul(x, w, y, M: int, N: int, K: int, stream=None) -> None:
 def q2k_matmul_path(x, w, y, M: int, N: int, K: int, path: int, stream=None) -> None:
     """q2k_matmul with a forced kernel: PATH_AUTO, PATH_GEMV (M <= 8) or PATH_MFMA."""
     _check(load_library().q2k_matmul_path(_ptr(x), _ptr(w), _ptr(y), M, N, K, int(path), _stream(stream)))
+
+
+def q2k_matmul_batched(x, w, y, batches: int, M: int, N: int, K: int, stream=None) -> None:
+    """y[b] = x[b] * W[b]^T for each of ``batches`` stacked problems (1 <= M <= 8)."""
+    _check(load_library().q2k_matmul_batched(_ptr(x), _ptr(w), _ptr(y), batches, M, N, K, _stream(stream)))
 
 
 def q2k_embedding_gather(table, ids, out, vocab: int, embed_dim: int, n_tokens: int, stream=None) -> None:

@@ -195,7 +195,7 @@ q2k_status q2k_matmul_path(const float *x, const void *w, float *y, uint32_t M, 
     const auto st = static_cast<hipStream_t>(stream);
     if (path == Q2K_PATH_GEMV) {
         if (M > q2k::kGemvMaxM) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul: the GEMV path takes M <= 8 (got %u)", M);
-        e = q2k::launch_gemv(x, wb, y, M, N, K, st);
+        e = q2k::launch_gemv(x, wb, y, M, N, K, 1, st);
     } else if (path == Q2K_PATH_MFMA) {
         void *ws = nullptr;
         s = stream_workspace(st, static_cast<size_t>(M) * K * 2, &ws);
@@ -210,6 +210,35 @@ q2k_status q2k_matmul_path(const float *x, const void *w, float *y, uint32_t M, 
 
 q2k_status q2k_matmul(const float *x, const void *w, float *y, uint32_t M, uint32_t N, uint32_t K, void *stream) {
     return q2k_matmul_path(x, w, y, M, N, K, Q2K_PATH_AUTO, stream);
+}
+
+q2k_status q2k_matmul_batched(const float *x, const void *w, float *y, uint32_t batches, uint32_t M, uint32_t N,
+                              uint32_t K, void *stream) {
+    if (!x || !w || !y) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul_batched: null pointer");
+    if (batches == 0 || M == 0 || N == 0 || K == 0)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul_batched: batches, M, N, K must be >= 1 (got %u, %u, %u, %u)",
+                    batches, M, N, K);
+    if (M > q2k::kGemvMaxM)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul_batched: M=%u; batched mat-vec takes 1 <= M <= 8", M);
+    if (K % q2k::kQK != 0) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul_batched: K=%u is not a multiple of 256", K);
+    if (K > q2k::kMaxK) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul_batched: K=%u exceeds the limit %u", K, q2k::kMaxK);
+    uint64_t xe, we, ye, t, xb, wbb, yb;
+    if (!mul_ok(M, K, &xe) || !mul_ok(N, K / q2k::kQK, &t) || !mul_ok(t, q2k::kBlockBytes, &we) || !mul_ok(M, N, &ye) ||
+        !mul_ok(xe, batches, &t) || !mul_ok(t, 4, &xb) || !mul_ok(we, batches, &wbb) || !mul_ok(ye, batches, &t) ||
+        !mul_ok(t, 4, &yb))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul_batched: size overflow");
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 4))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul_batched: x and y must be 16-byte aligned, w 4-byte aligned");
+    if (overlap(y, yb, x, xb) || overlap(y, yb, w, wbb))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul_batched: y overlaps an input");
+    const auto st = static_cast<hipStream_t>(stream);
+    const auto *wp = static_cast<const uint8_t *>(w);
+    for (uint64_t b0 = 0; b0 < batches; b0 += q2k::kMaxGridY) {
+        const uint32_t nbat = static_cast<uint32_t>(batches - b0 < q2k::kMaxGridY ? batches - b0 : q2k::kMaxGridY);
+        hipError_t e = q2k::launch_gemv(x + b0 * xe, wp + b0 * we, y + b0 * ye, M, N, K, nbat, st);
+        if (e != hipSuccess) return device_error("q2k_matmul_batched launch", e);
+    }
+    return ok();
 }
 
 q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *out, uint32_t vocab,

@@ -123,6 +123,14 @@ __device__ __forceinline__ void codes4(uint32_t v, uint32_t shift, float *q) {
     q[3] = hi[1];
 }
 
+// Batched GEMV: grid.y walks independent problems laid out batch-major;
+// problem b reads x + b * x_elems and w + b * w_bytes and writes y + b * y_elems.
+// Every problem runs exactly the instructions of a single call, so a batched
+// result is bit-identical to separate calls on the same slices.
+struct GemvBatch {
+    uint64_t x_elems, w_bytes, y_elems;
+};
+
 // ---------------------------------------------------------------------------
 // fp32 GEMV for M <= 2 (decode).
 //
@@ -195,8 +203,11 @@ __device__ __forceinline__ SegLoads load_seg(__amdgpu_buffer_rsrc_t rs, uint32_t
 
 template <int M, int NI>
 __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, const uint8_t *__restrict__ w,
-                                                  float *__restrict__ y, uint32_t N, uint32_t K) {
+                                                  float *__restrict__ y, uint32_t N, uint32_t K, GemvBatch bt) {
     __shared__ float red[4][NI * 4 * M];
+    x += blockIdx.y * bt.x_elems;
+    w += blockIdx.y * bt.w_bytes;
+    y += blockIdx.y * bt.y_elems;
     const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const uint32_t rr = lane >> 4, bq = (lane >> 2) & 3u, g = lane & 3u, h = g >> 1, s = g & 1u;
@@ -348,8 +359,12 @@ struct GemvRowsCfg {
 
 template <int M>
 __global__ __launch_bounds__(512) void k_gemv_rows(const float *__restrict__ x, const uint8_t *__restrict__ w,
-                                                   float *__restrict__ y, uint32_t N, uint32_t K, uint32_t rows_per_wg) {
+                                                   float *__restrict__ y, uint32_t N, uint32_t K, uint32_t rows_per_wg,
+                                                   GemvBatch bt) {
     constexpr int R = GemvRowsCfg<M>::kR, V = GemvRowsCfg<M>::kV;
+    x += blockIdx.y * bt.x_elems;
+    w += blockIdx.y * bt.w_bytes;
+    y += blockIdx.y * bt.y_elems;
     __shared__ float red[2][4][V][kWave];
     __shared__ float tot[kGemvMaxBatches][V];
     const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -785,23 +800,25 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
 }
 
 template <int M>
-hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, hipStream_t stream) {
+hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, uint32_t batches,
+                           GemvBatch bt, hipStream_t stream) {
     constexpr int NI = Q2K_GEMV_SEG_ITERS;
     const uint32_t blocks = (N + 4 * NI - 1) / (4 * NI);
-    hipLaunchKernelGGL((k_gemv_seg<M, NI>), dim3(blocks), dim3(256), 0, stream, x, w, y, N, K);
+    hipLaunchKernelGGL((k_gemv_seg<M, NI>), dim3(blocks, batches), dim3(256), 0, stream, x, w, y, N, K, bt);
     return hipGetLastError();
 }
 
 // Rows per workgroup: enough workgroups to cover the 256 CUs once, each
 // sweeping whole batches of rows, at most kGemvMaxBatches of them.
 template <int M>
-hipError_t launch_gemv_rows(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, hipStream_t stream) {
+hipError_t launch_gemv_rows(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, uint32_t batches,
+                            GemvBatch bt, hipStream_t stream) {
     constexpr uint32_t R = GemvRowsCfg<M>::kR;
     uint32_t rows = (N + 255) / 256;
     rows = (rows + R - 1) / R * R;
     if (rows > kGemvMaxBatches * R) rows = kGemvMaxBatches * R;
     const uint32_t blocks = (N + rows - 1) / rows;
-    hipLaunchKernelGGL((k_gemv_rows<M>), dim3(blocks), dim3(512), 0, stream, x, w, y, N, K, rows);
+    hipLaunchKernelGGL((k_gemv_rows<M>), dim3(blocks, batches), dim3(512), 0, stream, x, w, y, N, K, rows, bt);
     return hipGetLastError();
 }
 
@@ -828,16 +845,19 @@ hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, 
 }
 
 hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
-                       hipStream_t stream) {
+                       uint32_t batches, hipStream_t stream) {
+    if (batches == 0 || batches > kMaxGridY) return hipErrorInvalidValue;
+    const GemvBatch bt{static_cast<uint64_t>(M) * K, static_cast<uint64_t>(N) * (K / kQK) * kBlockBytes,
+                       static_cast<uint64_t>(M) * N};
     switch (M) {
-        case 1: return launch_gemv_seg<1>(x, w, y, N, K, stream);
-        case 2: return launch_gemv_seg<2>(x, w, y, N, K, stream);
-        case 3: return launch_gemv_rows<3>(x, w, y, N, K, stream);
-        case 4: return launch_gemv_rows<4>(x, w, y, N, K, stream);
-        case 5: return launch_gemv_rows<5>(x, w, y, N, K, stream);
-        case 6: return launch_gemv_rows<6>(x, w, y, N, K, stream);
-        case 7: return launch_gemv_rows<7>(x, w, y, N, K, stream);
-        case 8: return launch_gemv_rows<8>(x, w, y, N, K, stream);
+        case 1: return launch_gemv_seg<1>(x, w, y, N, K, batches, bt, stream);
+        case 2: return launch_gemv_seg<2>(x, w, y, N, K, batches, bt, stream);
+        case 3: return launch_gemv_rows<3>(x, w, y, N, K, batches, bt, stream);
+        case 4: return launch_gemv_rows<4>(x, w, y, N, K, batches, bt, stream);
+        case 5: return launch_gemv_rows<5>(x, w, y, N, K, batches, bt, stream);
+        case 6: return launch_gemv_rows<6>(x, w, y, N, K, batches, bt, stream);
+        case 7: return launch_gemv_rows<7>(x, w, y, N, K, batches, bt, stream);
+        case 8: return launch_gemv_rows<8>(x, w, y, N, K, batches, bt, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -13,14 +13,17 @@ constexpr uint32_t kQK = 256;          // weights per super-block
 constexpr uint32_t kBlockBytes = 84;   // bytes per super-block
 constexpr uint32_t kGemvMaxM = 8;      // largest M the fp32 GEMV handles
 constexpr uint32_t kMaxK = 1u << 21;   // keeps every per-workgroup byte offset below 2^31
+constexpr uint32_t kMaxGridY = 65535;  // largest batch count one GEMV launch takes
 
 hipError_t launch_dequantize(const uint8_t *blocks, uint64_t nblocks, float *out, hipStream_t stream);
 
 hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, uint32_t vocab,
                          uint32_t blocks_per_row, uint32_t n_tokens, int *status, hipStream_t stream);
 
+// 1 <= M <= 8; batches problems laid out batch-major (x [batches, M, K],
+// w [batches, N, K/256 blocks], y [batches, M, N]), 1 <= batches <= kMaxGridY.
 hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
-                       hipStream_t stream);
+                       uint32_t batches, hipStream_t stream);
 
 // Matrix-core path. x_bf16 is a device workspace of at least M * K * 2 bytes
 // (16-byte aligned) that receives bf16(x) before the GEMM reads it.

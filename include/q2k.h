@@ -107,6 +107,24 @@ q2k_status q2k_matmul_path(const float *x, const void *w, float *y, uint32_t M, 
                            uint32_t K, q2k_path path, void *stream);
 
 /*
+ * q2k_matmul_batched — a batch of independent small products,
+ *   y[b][M, N] = x[b][M, K] * W[b][N, K]^T for b = 0 .. batches-1.
+ * Page: test q2_k_batched_mv_is_byte_identical_to_independent_dispatches
+ * (quantized_matmul_q2_k_batched_mv with (batches, m, n, k); its result must
+ * equal, byte for byte, separate single-matrix calls on slice views).
+ *   x  device f32 [batches, M, K] row-major; 16-byte aligned.
+ *   w  device Q2_K bytes, batches * N * K/256 * 84 long: matrix b follows
+ *      matrix b-1, each laid out as for q2k_matmul; 4-byte aligned.
+ *   y  device f32 [batches, M, N] row-major; 16-byte aligned.
+ *   batches, N >= 1; 1 <= M <= 8 (the fp32 mat-vec path); K as for q2k_matmul.
+ * Slice b of y is bit-identical to q2k_matmul(x + b*M*K, w + b*N*K/256*84,
+ * y + b*M*N, M, N, K), whatever the other slices hold. Asynchronous on
+ * `stream`; allocates nothing.
+ */
+q2k_status q2k_matmul_batched(const float *x, const void *w, float *y, uint32_t batches, uint32_t M, uint32_t N,
+                              uint32_t K, void *stream);
+
+/*
  * q2k_embedding_gather — out[t, :] = decoded row ids[t] of a Q2_K table.
  * Page: test q2_k_embedding_gather_matches_canonical_rows_and_rejects_bad_ids
  * (EmbeddingQ2KParams { vocab_size, embed_dim, n_tokens }; an id equal to

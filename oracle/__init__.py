@@ -157,6 +157,24 @@ def matmul(x, w, M: int, N: int, K: int, bf16_operands: bool = False, nthreads: 
     return y, a
 
 
+def matmul_batched(x, w, batches: int, M: int, N: int, K: int, nthreads: int = 1):
+    """The page's batched mat-vec (test q2_k_batched_mv_is_byte_identical_to_independent_dispatches):
+    problem b multiplies x[b] (M x K) by the b-th weight matrix of a batch-major stack (N rows of K/256
+    blocks each). Defined there as separate single-matrix products; returns (y, a) stacked [batches, M, N].
+    """
+    xa = np.ascontiguousarray(x, dtype=np.float32).reshape(batches, M, K)
+    wa = _u8(w)
+    per = N * (K // QK_K) * BLOCK_BYTES
+    if K % QK_K or wa.size != batches * per:
+        raise OracleError("batched matmul shape mismatch")
+    ys, as_ = [], []
+    for b in range(batches):
+        y, a = matmul(xa[b], wa[b * per:(b + 1) * per], M, N, K, nthreads=nthreads)
+        ys.append(y)
+        as_.append(a)
+    return np.stack(ys), np.stack(as_)
+
+
 def matmul_f32seq(x, w, M: int, N: int, K: int) -> np.ndarray:
     """The page's cpu_dot: f32 products summed left to right in f32."""
     xa = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)

@@ -96,6 +96,24 @@ def test_matmul_rejects_size_overflow(lib):
     _err(lib, lib.q2k_matmul(A, B, C, 0xFFFFFFFF, 0xFFFFFFFF, 1 << 21, None), "overflow")
 
 
+@pytest.mark.parametrize("bt,M,N,K,frag", [
+    (0, 1, 8, 256, ">= 1"), (2, 0, 8, 256, ">= 1"), (2, 1, 0, 256, ">= 1"), (2, 1, 8, 0, ">= 1"),
+    (2, 9, 8, 256, "1 <= M <= 8"), (2, 1, 8, 300, "multiple of 256"), (2, 1, 8, (1 << 21) + 256, "exceeds"),
+    (0xFFFFFFFF, 8, 0xFFFFFFFF, 1 << 21, "overflow"),
+])
+def test_matmul_batched_rejects_bad_shapes(lib, bt, M, N, K, frag):
+    _err(lib, lib.q2k_matmul_batched(A, B, C, bt, M, N, K, None), frag)
+
+
+def test_matmul_batched_rejects_null_misaligned_and_overlap(lib):
+    _err(lib, lib.q2k_matmul_batched(None, B, C, 3, 1, 8, 256, None), "null")
+    _err(lib, lib.q2k_matmul_batched(A + 4, B, C, 3, 1, 8, 256, None), "aligned")
+    _err(lib, lib.q2k_matmul_batched(A, B + 1, C, 3, 1, 8, 256, None), "aligned")
+    # y of 3 batches x 8 floats ends 96 bytes after C: it overlaps an x that starts inside it
+    _err(lib, lib.q2k_matmul_batched(C + 64, B, C, 3, 1, 8, 256, None), "overlaps")
+    _err(lib, lib.q2k_matmul_batched(A, C + 80, C, 3, 1, 8, 256, None), "overlaps")
+
+
 @pytest.mark.parametrize("vocab,dim,nt,frag", [
     (0, 256, 2, ">= 1"), (3, 0, 2, ">= 1"), (3, 256, 0, ">= 1"), (3, 100, 2, "multiple of 256"),
 ])

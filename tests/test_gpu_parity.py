@@ -271,6 +271,65 @@ def test_gemv_is_deterministic():
     assert bits_equal(a, b)
 
 
+# ----------------------------------------------------------------- batched mat-vec
+
+def gpu_matmul_batched(x, blocks, batches, M, N, K):
+    xd, wd = dev(np.ascontiguousarray(x, dtype=np.float32)), dev(blocks)
+    y = torch.full((batches, M, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    q2k.q2k_matmul_batched(xd, wd, y, batches, M, N, K)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def test_batched_page_fixture_equals_independent_calls_bytewise():
+    # The page's batched mat-vec test: 3 matrices of 8 rows, K = 256, block(b*8 + row + 1),
+    # input(3) split one row per matrix; batched output equals serial M = 1 calls byte for byte.
+    batches, n = 3, 8
+    blocks = np.concatenate([synth.page_block(b * n + r + 1) for b in range(batches) for r in range(n)])
+    x = synth.page_input(batches).reshape(batches, 1, QK_K)
+    yb = gpu_matmul_batched(x, blocks, batches, 1, n, QK_K)
+    per = n * BB
+    for b in range(batches):
+        ys = gpu_matmul(x[b], blocks[b * per:(b + 1) * per], 1, n, QK_K)
+        assert bits_equal(yb[b], ys)
+    ref, a = oracle.matmul_batched(x, blocks, batches, 1, n, QK_K)
+    assert np.all(np.abs(yb - ref) <= GEMV_REL * a)
+    for b in range(batches):
+        assert np.all(np.abs(yb[b] - oracle.matmul_f32seq(x[b], blocks[b * per:(b + 1) * per], 1, n, QK_K)) <= 2e-4)
+
+
+@pytest.mark.parametrize("batches,M,N,K", [(2, 1, 130, 768), (5, 2, 33, 256), (3, 3, 70, 1280), (4, 8, 257, 512),
+                                           (1, 5, 4097, 256), (6, 7, 9, 4352)])
+def test_batched_equals_independent_calls_and_oracle(batches, M, N, K):
+    rng = np.random.Generator(np.random.PCG64(batches * 100003 + M * 1009 + N * 31 + K))
+    blocks = synth.random_blocks(rng, batches * N * K // QK_K)
+    x = rng.standard_normal((batches, M, K), dtype=np.float32)
+    yb = gpu_matmul_batched(x, blocks, batches, M, N, K)
+    per = N * K // QK_K * BB
+    for b in range(batches):
+        assert bits_equal(yb[b], gpu_matmul(x[b], blocks[b * per:(b + 1) * per], M, N, K))
+    ref, a = oracle.matmul_batched(x, blocks, batches, M, N, K, nthreads=oracle.host_threads())
+    assert np.all(np.abs(yb.astype(np.float64) - ref) <= GEMV_REL * a)
+
+
+def test_batched_more_problems_than_one_launch_covers():
+    # 65 537 one-row problems: the library splits them over two launches.
+    batches, M, N, K = 65537, 1, 1, 256
+    rng = np.random.Generator(np.random.PCG64(41))
+    blocks = synth.random_blocks(rng, batches)
+    x = rng.uniform(-1, 1, (batches, M, K)).astype(np.float32)
+    yb = gpu_matmul_batched(x, blocks, batches, M, N, K)
+    ref, a = oracle.matmul_batched(x, blocks, batches, M, N, K)
+    assert np.all(np.abs(yb.astype(np.float64) - ref) <= GEMV_REL * a)
+    for b in (0, 1, 65534, 65535, 65536):
+        assert bits_equal(yb[b], gpu_matmul(x[b], blocks[b * BB:(b + 1) * BB], M, N, K))
+
+
+def test_batched_rejects_m_above_eight_on_device():
+    with pytest.raises(q2k.Q2KInvalidArgument):
+        gpu_matmul_batched(np.zeros((2, 9, QK_K), np.float32), np.zeros(2 * BB, np.uint8), 2, 9, 1, QK_K)
+
+
 # ----------------------------------------------------------------- matrix-core path (M > 8)
 
 def test_mfma_page_run_dense_rows9_relative_rule():

@@ -356,3 +356,20 @@ def test_gather_duplicates_and_multi_block_rows():
     out = oracle.gather(table, ids, vocab, dim, len(ids), nthreads=3)
     dense = oracle.dequantize(table).reshape(vocab, dim)
     assert np.array_equal(out, dense[ids])
+
+
+def test_batched_matmul_is_independent_products_with_exact_rationals():
+    # The page defines the batched mat-vec as separate single-matrix products; check the
+    # oracle's stacking against exact rational arithmetic on a tiny case.
+    rng = _rng(43)
+    batches, M, N, K = 3, 2, 2, 256
+    blocks = synth.random_blocks(rng, batches * N)
+    x = rng.standard_normal((batches, M, K)).astype(np.float32)
+    y, a = oracle.matmul_batched(x, blocks, batches, M, N, K)
+    for b in range(batches):
+        for n in range(N):
+            blk = blocks[(b * N + n) * BB:(b * N + n + 1) * BB]
+            w = oracle.dequant_block(blk)
+            for m in range(M):
+                exact = sum(Fraction(float(x[b, m, k])) * Fraction(float(w[k])) for k in range(K))
+                assert abs(Fraction(float(y[b, m, n])) - exact) <= Fraction(1, 10**12) * (1 + abs(exact))
