@@ -14,6 +14,8 @@ Functions carry the C names:
   per matrix of a batch-major stack (1 <= M <= 8).
 * ``q2k_embedding_gather(table, ids, out, vocab, embed_dim, n_tokens)`` — rows
   of a Q2_K table; raises ``Q2KIdOutOfRange`` for an id >= vocab.
+* ``GGUFFile(path)`` — the GGUF tensor directory (``q2k_gguf_*``): names,
+  ``tensor_info(name)`` and ``tensor_bytes(name)`` (host side, no GPU work).
 
 The library is built in-tree by ``ggml_q2_dequant_amd.build``; importing this
 package never builds or falls back to anything, and a call fails loudly when
@@ -32,6 +34,9 @@ Q2K_ERR_INVALID_ARGUMENT = 1
 Q2K_ERR_ID_OUT_OF_RANGE = 2
 Q2K_ERR_DEVICE = 3
 
+GGML_TYPE_Q2_K = 10
+GGUF_MAX_DIMS = 4
+
 PATH_AUTO = 0
 PATH_GEMV = 1
 PATH_MFMA = 2
@@ -45,6 +50,12 @@ EXPORTS = (
     "q2k_matmul_path",
     "q2k_matmul_batched",
     "q2k_embedding_gather",
+    "q2k_gguf_open",
+    "q2k_gguf_close",
+    "q2k_gguf_tensor_count",
+    "q2k_gguf_tensor_name",
+    "q2k_gguf_tensor_info",
+    "q2k_gguf_tensor_data",
     "q2k_status_string",
     "q2k_last_error_message",
 )
@@ -70,6 +81,13 @@ class Q2KDeviceError(Q2KError):
     pass
 
 
+class GGUFInfo(ctypes.Structure):
+    """q2k_gguf_info: one tensor record of a GGUF file."""
+    _fields_ = [("ggml_type", ctypes.c_uint32), ("n_dims", ctypes.c_uint32),
+                ("dims", ctypes.c_uint64 * GGUF_MAX_DIMS), ("file_offset", ctypes.c_uint64),
+                ("byte_len", ctypes.c_uint64)]
+
+
 _lib = None
 
 
@@ -90,6 +108,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.q2k_embedding_gather.argtypes = [P, P, P, U32, U32, U32, P]
     for name in ("q2k_dequantize", "q2k_matmul", "q2k_matmul_path", "q2k_matmul_batched", "q2k_embedding_gather"):
         getattr(lib, name).restype = ctypes.c_int
+    lib.q2k_gguf_open.argtypes = [ctypes.c_char_p, ctypes.POINTER(P)]
+    lib.q2k_gguf_open.restype = ctypes.c_int
+    lib.q2k_gguf_close.argtypes = [P]
+    lib.q2k_gguf_close.restype = None
+    lib.q2k_gguf_tensor_count.argtypes = [P]
+    lib.q2k_gguf_tensor_count.restype = ctypes.c_uint64
+    lib.q2k_gguf_tensor_name.argtypes = [P, ctypes.c_uint64]
+    lib.q2k_gguf_tensor_name.restype = ctypes.c_char_p
+    lib.q2k_gguf_tensor_info.argtypes = [P, ctypes.c_char_p, ctypes.POINTER(GGUFInfo)]
+    lib.q2k_gguf_tensor_info.restype = ctypes.c_int
+    lib.q2k_gguf_tensor_data.argtypes = [P, ctypes.c_char_p, ctypes.POINTER(P), ctypes.POINTER(ctypes.c_uint64)]
+    lib.q2k_gguf_tensor_data.restype = ctypes.c_int
     lib.q2k_status_string.argtypes = [ctypes.c_int]
     lib.q2k_status_string.restype = ctypes.c_char_p
     lib.q2k_last_error_message.argtypes = []
@@ -108,7 +138,7 @@ def _status_name(status: int) -> str:
 def _check(status: int) -> None:
     if status == Q2K_OK:
         return
-    msg = load_library().q2k_last_error_message().decode()
+    msg = load_library().q2k_last_error_message().decode(errors="replace")
     cls = {Q2K_ERR_INVALID_ARGUMENT: Q2KInvalidArgument, Q2K_ERR_ID_OUT_OF_RANGE: Q2KIdOutOfRange,
            Q2K_ERR_DEVICE: Q2KDeviceError}.get(status, Q2KError)
     raise cls(status, msg)
@@ -162,3 +192,48 @@ def q2k_embedding_gather(table, ids, out, vocab: int, embed_dim: int, n_tokens: 
     """out[t, :] = decoded row ids[t] of ``table``; raises Q2KIdOutOfRange for any id >= vocab."""
     _check(load_library().q2k_embedding_gather(_ptr(table), _ptr(ids), _ptr(out), vocab, embed_dim, n_tokens,
                                                _stream(stream)))
+
+
+class GGUFFile:
+    """A GGUF file's tensor directory, read by libq2k (q2k_gguf_*). Use as a context manager or call close()."""
+
+    def __init__(self, path: str):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check(lib.q2k_gguf_open(os.fsencode(path), ctypes.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if self._h:
+            load_library().q2k_gguf_close(self._h)
+            self._h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def tensor_names(self) -> list:
+        lib = load_library()
+        return [lib.q2k_gguf_tensor_name(self._h, i).decode(errors="replace")
+                for i in range(lib.q2k_gguf_tensor_count(self._h))]
+
+    def tensor_info(self, name: str) -> dict:
+        info = GGUFInfo()
+        _check(load_library().q2k_gguf_tensor_info(self._h, name.encode(), ctypes.byref(info)))
+        return {"ggml_type": info.ggml_type, "n_dims": info.n_dims, "dims": list(info.dims)[:info.n_dims],
+                "file_offset": info.file_offset, "byte_len": info.byte_len}
+
+    def tensor_bytes(self, name: str):
+        """A numpy uint8 copy of the tensor's data."""
+        import numpy as np
+        ptr, n = ctypes.c_void_p(), ctypes.c_uint64()
+        _check(load_library().q2k_gguf_tensor_data(self._h, name.encode(), ctypes.byref(ptr), ctypes.byref(n)))
+        return np.frombuffer(ctypes.string_at(ptr.value, n.value), dtype=np.uint8).copy()

@@ -1,7 +1,7 @@
 """Build step for libq2k.so: hipcc for gfx950, in-tree.
 
 Produces ``ggml_q2_dequant_amd/libq2k.so`` from ``csrc/q2k_kernels.hip`` and
-``csrc/q2k_api.cpp`` with the public header in ``include/``. Run
+``csrc/q2k_api.cpp`` and ``csrc/q2k_gguf.cpp`` with the public header in ``include/``. Run
 ``python -m ggml_q2_dequant_amd.build`` (or ``__graft_entry__.build()``).
 """
 from __future__ import annotations
@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libq2k.so")
-SOURCES = [os.path.join(CSRC, "q2k_kernels.hip"), os.path.join(CSRC, "q2k_api.cpp")]
+SOURCES = [os.path.join(CSRC, "q2k_kernels.hip"), os.path.join(CSRC, "q2k_api.cpp"), os.path.join(CSRC, "q2k_gguf.cpp")]
 ARCH = os.environ.get("Q2K_OFFLOAD_ARCH", "gfx950")
 
 # -ffp-contract=off: only FMAs written as such are fused, so every kernel's

@@ -150,6 +150,17 @@ q2k_status stream_workspace(hipStream_t st, size_t bytes, void **out) {
 
 }  // namespace
 
+namespace q2k {
+
+q2k_status set_error_v(q2k_status s, const char *fmt, va_list ap) {
+    std::vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+    return s;
+}
+
+void clear_error() { g_msg[0] = '\0'; }
+
+}  // namespace q2k
+
 extern "C" {
 
 const char *q2k_status_string(q2k_status s) {

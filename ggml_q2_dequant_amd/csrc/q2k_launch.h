@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "q2k_error.h"
+
 namespace q2k {
 
 constexpr uint32_t kQK = 256;          // weights per super-block

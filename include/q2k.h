@@ -144,6 +144,50 @@ q2k_status q2k_matmul_batched(const float *x, const void *w, float *y, uint32_t 
 q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *out, uint32_t vocab,
                                 uint32_t embed_dim, uint32_t n_tokens, void *stream);
 
+/*
+ * GGUF tensor directory (host only; no GPU work).
+ * Page: test q2_k_gguf_type_10_parses_with_exact_block_size (GgufFile::open,
+ * tensor_info(name) -> ggml_type, byte_len): a GGUF v3 file whose one tensor
+ * "q2.weight" has one dimension of 256 and type 10 must report type Q2_K and
+ * 84 bytes.
+ * The file is "GGUF", u32 version (2 or 3), u64 tensor count, u64 metadata
+ * count, the metadata (string key, u32 type, value), then per tensor: string
+ * name, u32 n_dims, n_dims u64 extents (fastest first), u32 type, u64 offset
+ * into the data section, which starts at the next multiple of 32 bytes (or of
+ * the u32 metadata value "general.alignment"). Strings are a u64 length and
+ * the bytes; integers are little endian.
+ * q2k_gguf_open maps the file read-only and indexes the tensor records; every
+ * read is bounds-checked, and any malformed or truncated input is
+ * Q2K_ERR_INVALID_ARGUMENT with a message. The handle is caller-owned until
+ * q2k_gguf_close; pointers from q2k_gguf_tensor_name / q2k_gguf_tensor_data
+ * stay valid until then. Handles may be read from several threads at once.
+ */
+#define Q2K_GGUF_MAX_DIMS 4
+#define Q2K_GGML_TYPE_Q2_K 10
+
+typedef struct q2k_gguf q2k_gguf;
+
+typedef struct q2k_gguf_info {
+    uint32_t ggml_type;                /* GGML type code (10 = Q2_K) */
+    uint32_t n_dims;                   /* 1 .. Q2K_GGUF_MAX_DIMS */
+    uint64_t dims[Q2K_GGUF_MAX_DIMS];  /* extents, fastest-varying first; unused ones are 1 */
+    uint64_t file_offset;              /* byte offset of the tensor's data in the file */
+    uint64_t byte_len;                 /* data bytes; 0 when the type's size is unknown here
+                                          (known: F32 = 0, F16 = 1, Q2_K = 10, BF16 = 30) */
+} q2k_gguf_info;
+
+q2k_status q2k_gguf_open(const char *path, q2k_gguf **out);
+void q2k_gguf_close(q2k_gguf *f); /* NULL is ignored */
+uint64_t q2k_gguf_tensor_count(const q2k_gguf *f);
+/* Name of tensor `index` in file order, or NULL if out of range. */
+const char *q2k_gguf_tensor_name(const q2k_gguf *f, uint64_t index);
+/* Unknown name, a row extent that is not a whole number of blocks, or data
+ * outside the file: Q2K_ERR_INVALID_ARGUMENT. */
+q2k_status q2k_gguf_tensor_info(const q2k_gguf *f, const char *name, q2k_gguf_info *info);
+/* Host pointer to the tensor's bytes inside the mapping (for upload with
+ * hipMemcpy); fails if the type's size is unknown. */
+q2k_status q2k_gguf_tensor_data(const q2k_gguf *f, const char *name, const void **data, uint64_t *byte_len);
+
 /* Static English name of a status code ("Q2K_OK", ...). Never NULL. */
 const char *q2k_status_string(q2k_status s);
 
