@@ -12,7 +12,8 @@ oracle is timed on the host cores on a bounded sample and reported as
 "cpu_baseline".
 
 Other modes (used to collect rocprofv3 counters; they print one short JSON line):
-  --only ROW         run only one row's timed loop (gemv1, dequant, gather, gemv8, mfma, batched)
+  --only ROW         run only one row's timed loop (gemv1, dequant, gather, gemv8, mfma, batched,
+                     sample)
   --copy-probe       also run a device-to-device copy of COPY_BYTES (counter calibration)
   --derive-traffic FETCH_CSV WRITE_CSV
                      turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
@@ -46,7 +47,7 @@ KERNEL_SRC = os.path.join(ROOT, "ggml_q2_dequant_amd", "csrc", "q2k_kernels.hip"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMV_KERNEL = "k_gemv_seg<1"    # name prefix of the M = 1 GEMV kernel in rocprofv3 output
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-ROWS = ("gemv1", "dequant", "gather", "gemv8", "mfma", "batched")
+ROWS = ("gemv1", "dequant", "gather", "gemv8", "mfma", "batched", "sample")
 
 
 def log(msg: str) -> None:
@@ -268,6 +269,25 @@ class Bench:
                 "us": t * 1e6, "algorithmic_bytes": b, "GB/s": b / t / 1e9, "bound": "hbm",
                 "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
 
+    def sample(self, n=200):
+        """First-max argmax + threshold candidates over 8 slots x 262144 logits (cap 64)."""
+        torch, np = self.torch, self.np
+        ns, vocab, cap = 8, 262144, 64
+        rng = np.random.Generator(np.random.PCG64(4000))
+        sets = [torch.from_numpy(rng.standard_normal((ns, vocab), dtype=np.float32)).to(self.dev) for _ in range(64)]
+        d = self.dev
+        idx = torch.empty(ns, dtype=torch.int32, device=d)
+        val = torch.empty(ns, dtype=torch.float32, device=d)
+        cnt = torch.empty(ns, dtype=torch.int32, device=d)
+        ovf = torch.empty(ns, dtype=torch.int32, device=d)
+        ids = torch.empty((ns, cap), dtype=torch.int32, device=d)
+        t = time_launches(torch, lambda i: self.q2k.q2k_argmax_candidates(sets[i % 64], ns, vocab, cap, idx, val, cnt,
+                                                                          ovf, ids, stream=self.stream), n, 20)
+        b = ns * vocab * 4 + ns * 16 + ns * cap * 4
+        log("argmax + candidates 8 x 262144: %.2f us, %.1f GB/s" % (t * 1e6, b / t / 1e9))
+        return {"workload": "8 slots x 262144 logits, cap 64 (64 rotating logit sets, 512 MiB)", "us": t * 1e6,
+                "algorithmic_bytes": b, "GB/s": b / t / 1e9, "bound": "hbm", "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
+
     def copy_probe(self):
         torch = self.torch
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=self.dev)
@@ -351,6 +371,7 @@ def main() -> int:
         rows["gemv_m8"] = b.gemv8()
         rows["mfma_m512"] = b.mfma()
         rows["batched_mv"] = b.batched()
+        rows["argmax_candidates"] = b.sample()
 
     # ------------------------------------------------------------------- CPU oracle baseline
     log("timing the CPU oracle (~%.0f s)" % args.cpu_seconds)

@@ -14,6 +14,9 @@ Functions carry the C names:
   per matrix of a batch-major stack (1 <= M <= 8).
 * ``q2k_embedding_gather(table, ids, out, vocab, embed_dim, n_tokens)`` — rows
   of a Q2_K table; raises ``Q2KIdOutOfRange`` for an id >= vocab.
+* ``q2k_argmax_candidates(logits, n_slots, vocab, cap, top1_idx, top1_val,
+  cand_count, overflow, cand_ids)`` — first-max argmax and the logits within
+  0.5 of it, per slot.
 * ``GGUFFile(path)`` — the GGUF tensor directory (``q2k_gguf_*``): names,
   ``tensor_info(name)`` and ``tensor_bytes(name)`` (host side, no GPU work).
 
@@ -50,6 +53,7 @@ EXPORTS = (
     "q2k_matmul_path",
     "q2k_matmul_batched",
     "q2k_embedding_gather",
+    "q2k_argmax_candidates",
     "q2k_gguf_open",
     "q2k_gguf_close",
     "q2k_gguf_tensor_count",
@@ -108,6 +112,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.q2k_embedding_gather.argtypes = [P, P, P, U32, U32, U32, P]
     for name in ("q2k_dequantize", "q2k_matmul", "q2k_matmul_path", "q2k_matmul_batched", "q2k_embedding_gather"):
         getattr(lib, name).restype = ctypes.c_int
+    lib.q2k_argmax_candidates.argtypes = [P, U32, U32, U32, P, P, P, P, P, P]
+    lib.q2k_argmax_candidates.restype = ctypes.c_int
     lib.q2k_gguf_open.argtypes = [ctypes.c_char_p, ctypes.POINTER(P)]
     lib.q2k_gguf_open.restype = ctypes.c_int
     lib.q2k_gguf_close.argtypes = [P]
@@ -192,6 +198,13 @@ def q2k_embedding_gather(table, ids, out, vocab: int, embed_dim: int, n_tokens: 
     """out[t, :] = decoded row ids[t] of ``table``; raises Q2KIdOutOfRange for any id >= vocab."""
     _check(load_library().q2k_embedding_gather(_ptr(table), _ptr(ids), _ptr(out), vocab, embed_dim, n_tokens,
                                                _stream(stream)))
+
+
+def q2k_argmax_candidates(logits, n_slots: int, vocab: int, cap: int, top1_idx, top1_val, cand_count, overflow,
+                          cand_ids, stream=None) -> None:
+    """Per slot: first-max index/value, candidate count (may exceed cap), overflow flag, candidate ids."""
+    _check(load_library().q2k_argmax_candidates(_ptr(logits), n_slots, vocab, cap, _ptr(top1_idx), _ptr(top1_val),
+                                                _ptr(cand_count), _ptr(overflow), _ptr(cand_ids), _stream(stream)))
 
 
 class GGUFFile:

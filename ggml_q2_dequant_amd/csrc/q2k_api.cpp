@@ -115,10 +115,12 @@ q2k_status status_word(StatusWord **out) {
     return Q2K_OK;
 }
 
-// The matrix-core path stages bf16(x) in a device workspace. One grow-only
-// workspace is kept per (device, stream); growth frees and reallocates it in
-// stream order, so work already queued on that stream keeps its buffer, and
-// calls on different streams never share one.
+// The matrix-core path (bf16(x)) and the argmax/candidate call (per-chunk
+// partials) stage data in a device workspace. One grow-only workspace is kept
+// per (device, stream) and used only inside one call; calls on one stream run
+// in order, so they can share it. Growth frees and reallocates it in stream
+// order, so work already queued on that stream keeps its buffer, and calls on
+// different streams never share one.
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
@@ -248,6 +250,45 @@ q2k_status q2k_matmul_batched(const float *x, const void *w, float *y, uint32_t 
         const uint32_t nbat = static_cast<uint32_t>(batches - b0 < q2k::kMaxGridY ? batches - b0 : q2k::kMaxGridY);
         hipError_t e = q2k::launch_gemv(x + b0 * xe, wp + b0 * we, y + b0 * ye, M, N, K, nbat, st);
         if (e != hipSuccess) return device_error("q2k_matmul_batched launch", e);
+    }
+    return ok();
+}
+
+q2k_status q2k_argmax_candidates(const float *logits, uint32_t n_slots, uint32_t vocab, uint32_t cap,
+                                 uint32_t *top1_idx, float *top1_val, uint32_t *cand_count, uint32_t *overflow,
+                                 uint32_t *cand_ids, void *stream) {
+    if (!logits || !top1_idx || !top1_val || !cand_count || !overflow || !cand_ids)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: null pointer");
+    if (n_slots == 0 || vocab == 0 || cap == 0)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: n_slots, vocab, cap must all be > 0 (got %u, %u, %u)",
+                    n_slots, vocab, cap);
+    if (vocab > q2k::kSampleMaxVocab)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: vocab=%u exceeds the limit %u", vocab,
+                    q2k::kSampleMaxVocab);
+    uint64_t lb, cb, t;
+    if (!mul_ok(n_slots, vocab, &t) || !mul_ok(t, 4, &lb) || !mul_ok(n_slots, cap, &t) || !mul_ok(t, 4, &cb))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: size overflow");
+    if (!aligned(logits, 4) || !aligned(top1_idx, 4) || !aligned(top1_val, 4) || !aligned(cand_count, 4) ||
+        !aligned(overflow, 4) || !aligned(cand_ids, 4))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: every buffer must be 4-byte aligned");
+    const Range outs[5] = {{top1_idx, 4ull * n_slots}, {top1_val, 4ull * n_slots}, {cand_count, 4ull * n_slots},
+                           {overflow, 4ull * n_slots}, {cand_ids, cb}};
+    for (int i = 0; i < 5; ++i) {
+        if (overlap(outs[i].p, outs[i].bytes, logits, lb))
+            return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: an output overlaps the logits");
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
+                return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: outputs overlap each other");
+    }
+    const auto st = static_cast<hipStream_t>(stream);
+    for (uint64_t s0 = 0; s0 < n_slots; s0 += q2k::kMaxGridY) {
+        const uint32_t ns = static_cast<uint32_t>(n_slots - s0 < q2k::kMaxGridY ? n_slots - s0 : q2k::kMaxGridY);
+        void *ws = nullptr;
+        q2k_status s = stream_workspace(st, q2k::sample_workspace_bytes(ns, vocab), &ws);
+        if (s != Q2K_OK) return s;
+        hipError_t e = q2k::launch_argmax_candidates(logits + s0 * vocab, ns, vocab, cap, top1_idx + s0, top1_val + s0,
+                                                     cand_count + s0, overflow + s0, cand_ids + s0 * cap, ws, st);
+        if (e != hipSuccess) return device_error("q2k_argmax_candidates launch", e);
     }
     return ok();
 }

@@ -32,4 +32,15 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, u
 hipError_t launch_gemm_mfma(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
                             void *x_bf16, hipStream_t stream);
 
+// First-max argmax + threshold candidates over [n_slots, vocab] logits
+// (q2k_sample.hip). workspace holds sample_workspace_bytes(n_slots, vocab)
+// bytes, 8-byte aligned; 1 <= n_slots <= kMaxGridY, vocab, cap >= 1.
+constexpr uint32_t kSampleMaxChunks = 64;      // chunks (workgroups) per slot
+constexpr uint32_t kSampleMaxVocab = 1u << 29;  // keeps every row's byte offsets below 2^31
+uint32_t sample_chunk(uint32_t vocab);
+uint64_t sample_workspace_bytes(uint32_t n_slots, uint32_t vocab);
+hipError_t launch_argmax_candidates(const float *logits, uint32_t n_slots, uint32_t vocab, uint32_t cap,
+                                    uint32_t *top1_idx, float *top1_val, uint32_t *cand_count, uint32_t *overflow,
+                                    uint32_t *cand_ids, void *workspace, hipStream_t stream);
+
 }  // namespace q2k

@@ -145,6 +145,31 @@ q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *o
                                 uint32_t embed_dim, uint32_t n_tokens, void *stream);
 
 /*
+ * q2k_argmax_candidates — per slot of [n_slots, vocab] f32 logits: the first
+ * maximum and the indices within 0.5 of it.
+ * Page: docs.rs source page of mlx-native 0.9.5, src/mlx_native/ops/gpu_sample.rs
+ * (dispatch_gpu_sample_argmax_candidates: first-max argmax with lower-index
+ * tie-break, candidates are logits >= top1 - 0.5f, the count may exceed cap,
+ * overflow is set when it does; n_slots, vocab and cap must be > 0).
+ *   logits      device f32 [n_slots, vocab] row-major; 4-byte aligned.
+ *   top1_idx    device u32 [n_slots]: the lowest index holding the slot's
+ *               maximum, scanning left to right with strict '>' (NaN never
+ *               wins; a NaN in column 0 is the scan's start and stays the answer).
+ *   top1_val    device f32 [n_slots]: that logit.
+ *   cand_count  device u32 [n_slots]: how many logits are >= top1_val - 0.5f
+ *               (f32 subtraction); may exceed cap; 0 when top1_val is NaN.
+ *   overflow    device u32 [n_slots]: 1 if cand_count > cap, else 0.
+ *   cand_ids    device u32 [n_slots, cap]: the first min(cand_count, cap)
+ *               candidate indices in increasing order; entries past them are
+ *               left unwritten.
+ * 1 <= vocab <= 2^29. Outputs may not overlap the logits or each other. Uses the per-(device,
+ * stream) workspace (about 12 bytes per 8192 logits). Asynchronous on `stream`.
+ */
+q2k_status q2k_argmax_candidates(const float *logits, uint32_t n_slots, uint32_t vocab, uint32_t cap,
+                                 uint32_t *top1_idx, float *top1_val, uint32_t *cand_count, uint32_t *overflow,
+                                 uint32_t *cand_ids, void *stream);
+
+/*
  * GGUF tensor directory (host only; no GPU work).
  * Page: test q2_k_gguf_type_10_parses_with_exact_block_size (GgufFile::open,
  * tensor_info(name) -> ggml_type, byte_len): a GGUF v3 file whose one tensor

@@ -8,7 +8,9 @@ never uses it and shares no code with it.
 Every function restates an item of the docs.rs source page of mlx-native
 0.10.8, tests/deepseek_q2_k.rs: the 84-byte super-block layout (constants and
 fn block), the decode (fn reference_dequant), the dense product (fn run_dense,
-fn cpu_dot) and the embedding gather test. The C file documents each one.
+fn cpu_dot), the batched mat-vec test and the embedding gather test; and, from
+the docs.rs source page of mlx-native 0.9.5, src/mlx_native/ops/gpu_sample.rs,
+the first-max argmax with threshold candidates. The C file documents each one.
 """
 from __future__ import annotations
 
@@ -68,6 +70,8 @@ def _load():
         lib.oracle_matmul_f32seq.restype = ctypes.c_int
         lib.oracle_gather.argtypes = [P, P, P, L, L, L, ctypes.c_int]
         lib.oracle_gather.restype = ctypes.c_int
+        lib.oracle_argmax_candidates.argtypes = [P, L, L, L, P, P, P, P, P]
+        lib.oracle_argmax_candidates.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -200,3 +204,19 @@ def gather(table, ids, vocab: int, embed_dim: int, n_tokens: int, nthreads: int 
     if rc != 0:
         raise OracleError("gather rejected shape")
     return out
+
+
+def argmax_candidates(logits, n_slots: int, vocab: int, cap: int):
+    """gpu_sample.rs: per slot (top1_idx, top1_val, cand_count, overflow, cand_ids[:min(count, cap)])."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32).reshape(-1)
+    if lg.size != n_slots * vocab:
+        raise OracleError("logits shape mismatch")
+    idx = np.empty(n_slots, np.uint32)
+    val = np.empty(n_slots, np.float32)
+    cnt = np.empty(n_slots, np.uint32)
+    ovf = np.empty(n_slots, np.uint32)
+    ids = np.full((n_slots, cap), 0xFFFFFFFF, np.uint32)
+    if _load().oracle_argmax_candidates(_ptr(lg), n_slots, vocab, cap, _ptr(idx), _ptr(val), _ptr(cnt), _ptr(ovf),
+                                        _ptr(ids)) != 0:
+        raise OracleError("argmax_candidates rejected a zero size")
+    return idx, val, cnt, ovf, [ids[s, :min(int(cnt[s]), cap)] for s in range(n_slots)]

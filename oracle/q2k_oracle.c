@@ -232,3 +232,37 @@ int oracle_gather(const uint8_t *table, const uint32_t *ids, float *out,
     }
     return 0;
 }
+
+/* docs.rs source page of mlx-native 0.9.5, src/mlx_native/ops/gpu_sample.rs
+ * (dispatch_gpu_sample_argmax_candidates and its module comment): per slot of
+ * [n_slots, vocab] f32 logits, the first maximum found by a left-to-right scan
+ * with strict '>' (lower index wins ties; NaN never compares greater, so a
+ * NaN in column 0 stays the answer), the count of logits >= top1 - 0.5f
+ * (computed in f32), an overflow flag when that count exceeds cap, and the
+ * first min(count, cap) candidate indices in increasing order (entries past
+ * them are not written). Returns 0, or -1 for a zero size. */
+int oracle_argmax_candidates(const float *logits, long n_slots, long vocab, long cap,
+                             uint32_t *top1_idx, float *top1_val, uint32_t *cand_count,
+                             uint32_t *overflow, uint32_t *cand_ids) {
+    if (n_slots <= 0 || vocab <= 0 || cap <= 0) return -1;
+    for (long s = 0; s < n_slots; ++s) {
+        const float *row = logits + (size_t)s * (size_t)vocab;
+        long best = 0;
+        for (long i = 1; i < vocab; ++i)
+            if (row[i] > row[best]) best = i;
+        const float top = row[best];
+        const float thr = top - 0.5f;
+        uint32_t n = 0;
+        for (long i = 0; i < vocab; ++i) {
+            if (row[i] >= thr) {
+                if ((long)n < cap) cand_ids[(size_t)s * (size_t)cap + n] = (uint32_t)i;
+                ++n;
+            }
+        }
+        top1_idx[s] = (uint32_t)best;
+        top1_val[s] = top;
+        cand_count[s] = n;
+        overflow[s] = (long)n > cap ? 1u : 0u;
+    }
+    return 0;
+}

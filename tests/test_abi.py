@@ -130,6 +130,26 @@ def test_gather_rejects_null_misaligned_and_overlap(lib):
     _err(lib, lib.q2k_embedding_gather(A, C + 4, C, 3, 256, 2, None), "overlaps")
 
 
+D, E, F, G = 4 << 32, 5 << 32, 6 << 32, 7 << 32
+
+
+@pytest.mark.parametrize("ns,vocab,cap,frag", [
+    (0, 8, 4, "> 0"), (2, 0, 4, "> 0"), (2, 8, 0, "> 0"), (2, (1 << 29) + 1, 4, "exceeds the limit"),
+    (0xFFFFFFFF, 1 << 29, 0xFFFFFFFF, "overflow"),
+])
+def test_argmax_candidates_rejects_bad_sizes(lib, ns, vocab, cap, frag):
+    _err(lib, lib.q2k_argmax_candidates(A, ns, vocab, cap, B, C, D, E, F, None), frag)
+
+
+def test_argmax_candidates_rejects_null_misaligned_and_overlap(lib):
+    _err(lib, lib.q2k_argmax_candidates(A, 2, 8, 4, B, C, D, E, None, None), "null")
+    _err(lib, lib.q2k_argmax_candidates(A + 2, 2, 8, 4, B, C, D, E, F, None), "aligned")
+    _err(lib, lib.q2k_argmax_candidates(A, 2, 8, 4, B, C + 1, D, E, F, None), "aligned")
+    _err(lib, lib.q2k_argmax_candidates(A, 2, 8, 4, A + 60, C, D, E, F, None), "overlaps the logits")
+    _err(lib, lib.q2k_argmax_candidates(A, 2, 8, 4, B, B + 4, D, E, F, None), "overlap each other")
+    _err(lib, lib.q2k_argmax_candidates(A, 2, 8, 4, B, C, D, E, E + 4, None), "overlap each other")
+
+
 def test_python_binding_raises_typed_errors(lib):
     with pytest.raises(q2k.Q2KInvalidArgument, match="multiple of 256"):
         q2k.q2k_matmul(A, B, C, 1, 8, 100, stream=0)
