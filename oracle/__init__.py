@@ -10,7 +10,8 @@ Every function restates an item of the docs.rs source page of mlx-native
 fn block), the decode (fn reference_dequant), the dense product (fn run_dense,
 fn cpu_dot), the batched mat-vec test and the embedding gather test; and, from
 the docs.rs source page of mlx-native 0.9.5, src/mlx_native/ops/gpu_sample.rs,
-the first-max argmax with threshold candidates. The C file documents each one.
+the first-max argmax with threshold candidates; and the expert-routed product
+(fn run_expert and the slotted down-projection test). The C file documents each one.
 """
 from __future__ import annotations
 
@@ -72,6 +73,9 @@ def _load():
         lib.oracle_gather.restype = ctypes.c_int
         lib.oracle_argmax_candidates.argtypes = [P, L, L, L, P, P, P, P, P]
         lib.oracle_argmax_candidates.restype = ctypes.c_int
+        lib.oracle_matmul_id.argtypes = [P, P, P, P, P, L, L, L, L, L, L, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.POINTER(L)]
+        lib.oracle_matmul_id.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -177,6 +181,35 @@ def matmul_batched(x, w, batches: int, M: int, N: int, K: int, nthreads: int = 1
         ys.append(y)
         as_.append(a)
     return np.stack(ys), np.stack(as_)
+
+
+def matmul_id(x, w, ids, n_tokens: int, top_k: int, n: int, K: int, n_experts: int, expert_stride: int,
+              slotted: bool = False, bf16_operands: bool = False, nthreads: int = 1):
+    """The page's expert-routed product (fn run_expert; slotted: the down-projection test).
+
+    Route r = token * top_k + slot uses expert ids[r] (u32 [n_tokens, top_k]) and activation row r // top_k
+    of x [n_tokens, K], or row r of x [n_tokens, top_k, K] when ``slotted``. Expert e's n weight rows start
+    e * expert_stride bytes into w. Returns (y, a, bad): y and a are f64 [n_tokens * top_k, n] (a = sum |x*w|),
+    rows of routes whose id is >= n_experts are NaN, and bad counts those routes.
+    """
+    routes = n_tokens * top_k
+    xa = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    wa = _u8(w)
+    ia = np.ascontiguousarray(ids, dtype=np.uint32).reshape(-1)
+    rows_x = routes if slotted else n_tokens
+    row_bytes = (K // QK_K) * BLOCK_BYTES
+    if (K % QK_K or xa.size != rows_x * K or ia.size != routes or expert_stride < n * row_bytes
+            or wa.size < (n_experts - 1) * expert_stride + n * row_bytes):
+        raise OracleError("matmul_id shape mismatch")
+    y = np.empty((routes, n), dtype=np.float64)
+    a = np.empty((routes, n), dtype=np.float64)
+    bad = ctypes.c_long(0)
+    rc = _load().oracle_matmul_id(_ptr(xa), _ptr(wa), _ptr(ia), _ptr(y), _ptr(a), n_tokens, top_k, n, K,
+                                  n_experts, expert_stride, 1 if slotted else 0, 1 if bf16_operands else 0,
+                                  int(nthreads), ctypes.byref(bad))
+    if rc != 0:
+        raise OracleError("matmul_id rejected shape")
+    return y, a, bad.value
 
 
 def matmul_f32seq(x, w, M: int, N: int, K: int) -> np.ndarray:

@@ -17,7 +17,9 @@
  *   - test q2_k_embedding_gather_matches_canonical_rows_and_rejects_bad_ids:
  *     gather semantics and the id == vocab rejection;
  *   - fn run_dense: y[m, n] = sum_k x[m, k] * w[n, k], rows of w made of
- *     K/256 consecutive blocks.
+ *     K/256 consecutive blocks;
+ *   - fn run_expert and the slotted down-projection test: the expert-routed
+ *     product, one expert per (token, slot) route.
  *
  * Precision: the page decodes in f32 (d and dmin widened to f32, products and
  * the final subtraction in f32), so dequantization is done in f32 here too.
@@ -263,6 +265,68 @@ int oracle_argmax_candidates(const float *logits, long n_slots, long vocab, long
         top1_val[s] = top;
         cand_count[s] = n;
         overflow[s] = (long)n > cap ? 1u : 0u;
+    }
+    return 0;
+}
+
+/* Expert-routed product of the Q2_K page (fn run_expert, and the slotted
+ * test q2_k_slotted_down_mm_is_byte_identical_to_flattened_rows): route
+ * r = token * top_k + slot multiplies by expert ids[r]. Its output row is
+ * out[r, row] = sum over k of x[xr, k] * W_e[row, k], where xr = r / top_k
+ * (one activation row per token) or xr = r when `slotted` (one activation row
+ * per route, input [tokens, top_k, K]). Expert e's weights start
+ * e * expert_stride bytes into w and hold n rows of K/256 blocks each. The
+ * page states no rule for an id >= n_experts; here such a route's outputs are
+ * all NaN (never a read outside w) and it is counted in *bad. Accumulates in
+ * f64 in increasing k and returns a = sum |x * w| beside y, like
+ * oracle_matmul; bf16_operands rounds both operands to bf16 first. Returns 0,
+ * or -1 for a rejected shape. */
+int oracle_matmul_id(const float *x, const uint8_t *w, const uint32_t *ids, double *y, double *a,
+                     long n_tokens, long top_k, long n, long K, long n_experts, long expert_stride,
+                     int slotted, int bf16_operands, int nthreads, long *bad) {
+    if (n_tokens <= 0 || top_k <= 0 || n <= 0 || n_experts <= 0 || !matmul_shape_ok(1, n, K)) return -1;
+    if (expert_stride < n * (K / QK_K) * BLOCK_BYTES) return -1;
+    if (nthreads < 1) nthreads = 1;
+    const long routes = n_tokens * top_k;
+    long nbad = 0;
+    for (long r = 0; r < routes; ++r)
+        if ((long)ids[r] >= n_experts) ++nbad;
+    if (bad) *bad = nbad;
+#pragma omp parallel num_threads(nthreads)
+    {
+        float *wrow = (float *)malloc(sizeof(float) * (size_t)K);
+        float *xrow = (float *)malloc(sizeof(float) * (size_t)K);
+#pragma omp for schedule(static)
+        for (long r = 0; r < routes; ++r) {
+            double *yr = y + (size_t)r * (size_t)n;
+            double *ar = a ? a + (size_t)r * (size_t)n : NULL;
+            const long e = (long)ids[r];
+            if (e >= n_experts) {
+                for (long row = 0; row < n; ++row) {
+                    yr[row] = NAN;
+                    if (ar) ar[row] = NAN;
+                }
+                continue;
+            }
+            const long xr = slotted ? r : r / top_k;
+            const float *xm = x + (size_t)xr * (size_t)K;
+            for (long k = 0; k < K; ++k) xrow[k] = bf16_operands ? oracle_bf16_round(xm[k]) : xm[k];
+            const uint8_t *we = w + (size_t)e * (size_t)expert_stride;
+            for (long row = 0; row < n; ++row) {
+                dequant_row(we, row, K, wrow);
+                double s = 0.0, sa = 0.0;
+                for (long k = 0; k < K; ++k) {
+                    const float wk = bf16_operands ? oracle_bf16_round(wrow[k]) : wrow[k];
+                    const double p = (double)xrow[k] * (double)wk;
+                    s += p;
+                    sa += fabs(p);
+                }
+                yr[row] = s;
+                if (ar) ar[row] = sa;
+            }
+        }
+        free(wrow);
+        free(xrow);
     }
     return 0;
 }

@@ -149,3 +149,71 @@ def rows_of(blocks: np.ndarray, K: int, rows) -> np.ndarray:
     rb = (K // QK_K) * BLOCK_BYTES
     b = blocks.reshape(-1, rb)
     return np.ascontiguousarray(b[np.asarray(rows)]).reshape(-1)
+
+
+# --- Expert-routed (mm_id) inputs ------------------------------------------
+
+def page_expert_weights(experts: int, n: int) -> np.ndarray:
+    """fn run_expert's weights: row r of expert e is fn block(e * n + r + 1) (K = 256, one block per row)."""
+    return np.concatenate([page_block(e * n + r + 1) for e in range(experts) for r in range(n)])
+
+
+def page_routes(tokens: int, top_k: int, experts: int) -> np.ndarray:
+    """fn run_expert's routing: route (token t, slot s) takes expert (3 t + s) mod experts; u32 [tokens*top_k]."""
+    t = np.arange(tokens, dtype=np.int64)[:, None]
+    s = np.arange(top_k, dtype=np.int64)[None, :]
+    return ((3 * t + s) % experts).astype(np.uint32).reshape(-1)
+
+
+def random_routes(rng: np.random.Generator, tokens: int, top_k: int, experts: int) -> np.ndarray:
+    """Router-like ids: per token, top_k distinct experts drawn uniformly; u32 [tokens*top_k]."""
+    if top_k > experts:
+        return rng.integers(0, experts, tokens * top_k).astype(np.uint32)
+    keys = rng.random((tokens, experts))
+    return np.argsort(keys, axis=1)[:, :top_k].astype(np.uint32).reshape(-1)
+
+
+@dataclass(frozen=True)
+class MoeConfig:
+    index: int
+    name: str
+    tokens: int
+    top_k: int
+    experts: int
+    n: int
+    K: int
+
+    @property
+    def seed(self) -> int:
+        return 2000 + self.index
+
+    @property
+    def routes(self) -> int:
+        return self.tokens * self.top_k
+
+
+# The page's expert count and top_k (8 experts, top_k 6), with each expert the
+# size of the dense workloads' weight matrix (14336 x 4096).
+MOE_CONFIGS = [
+    MoeConfig(0, "expert-routed decode: 1 token, top_k 6 of 8 experts, N=14336 K=4096", 1, 6, 8, 14336, 4096),
+    MoeConfig(1, "expert-routed prefill: 512 tokens, top_k 6 of 8 experts, N=14336 K=4096", 512, 6, 8, 14336, 4096),
+]
+
+
+@dataclass
+class MoeInputs:
+    config: MoeConfig
+    blocks: np.ndarray   # u8, experts x n rows x K/256 blocks, expert stride n * K/256 * 84
+    x: np.ndarray        # f32 [tokens, K]
+    ids: np.ndarray      # u32 [tokens * top_k]
+
+
+def make_moe_inputs(cfg: MoeConfig | int) -> MoeInputs:
+    """Draw an expert-routed workload from PCG64(2000 + index): blocks, activations N(0,1), routes."""
+    if isinstance(cfg, int):
+        cfg = MOE_CONFIGS[cfg]
+    rng = np.random.Generator(np.random.PCG64(cfg.seed))
+    blocks = random_blocks(rng, cfg.experts * cfg.n * (cfg.K // QK_K))
+    x = rng.standard_normal((cfg.tokens, cfg.K), dtype=np.float32)
+    ids = random_routes(rng, cfg.tokens, cfg.top_k, cfg.experts)
+    return MoeInputs(cfg, blocks, x, ids)
