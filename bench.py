@@ -6,14 +6,15 @@ Timed step: one q2k_matmul call on the decode GEMV workload (M = 1, N = K =
 quoted on. Each step reads a different one of R byte-identical weight replicas
 (R * 5.5 MB >= 512 MiB, twice the 256 MiB Infinity Cache), so every step
 streams its weights from HBM. The other rows of the path (dequantize, gather,
-M = 8 GEMV, M = 512 matrix-core GEMM, batched mat-vec) are timed after the headline region and
+M = 8 GEMV, M = 512 matrix-core GEMM, batched mat-vec, argmax + candidates, expert-routed decode and
+prefill) are timed after the headline region and
 reported under "rows", each against the roofline that bounds it. The CPU
 oracle is timed on the host cores on a bounded sample and reported as
 "cpu_baseline".
 
 Other modes (used to collect rocprofv3 counters; they print one short JSON line):
   --only ROW         run only one row's timed loop (gemv1, dequant, gather, gemv8, mfma, batched,
-                     sample)
+                     sample, moe_decode, moe_prefill)
   --copy-probe       also run a device-to-device copy of COPY_BYTES (counter calibration)
   --derive-traffic FETCH_CSV WRITE_CSV
                      turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
@@ -47,7 +48,7 @@ KERNEL_SRC = os.path.join(ROOT, "ggml_q2_dequant_amd", "csrc", "q2k_kernels.hip"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMV_KERNEL = "k_gemv_seg<1"    # name prefix of the M = 1 GEMV kernel in rocprofv3 output
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-ROWS = ("gemv1", "dequant", "gather", "gemv8", "mfma", "batched", "sample")
+ROWS = ("gemv1", "dequant", "gather", "gemv8", "mfma", "batched", "sample", "moe_decode", "moe_prefill")
 
 
 def log(msg: str) -> None:
@@ -288,6 +289,46 @@ class Bench:
         return {"workload": "8 slots x 262144 logits, cap 64 (64 rotating logit sets, 512 MiB)", "us": t * 1e6,
                 "algorithmic_bytes": b, "GB/s": b / t / 1e9, "bound": "hbm", "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
 
+    def _moe(self, ci):
+        torch, np = self.torch, self.np
+        inp = self.synth.make_moe_inputs(ci)
+        c = inp.config
+        p = self.q2k.MatmulIdParams(n_tokens=c.tokens, top_k=c.top_k, n=c.n, k=c.K, n_experts=c.experts,
+                                    reserved=0, expert_stride=c.n * (c.K // 256) * 84)
+        x = torch.from_numpy(inp.x).to(self.dev)
+        ids = torch.from_numpy(inp.ids.astype(np.int32)).to(self.dev)
+        y = torch.empty((c.routes, c.n), dtype=torch.float32, device=self.dev)
+        return inp, c, p, x, ids, y
+
+    def moe_decode(self, n=200):
+        """Expert-routed decode: 1 token, top_k 6 of 8 experts (fp32 per-route schedule), cold weights."""
+        torch = self.torch
+        log("generating expert-routed decode inputs")
+        inp, c, p, x, ids, y = self._moe(0)
+        wh = torch.from_numpy(inp.blocks)
+        reps = max(1, math.ceil(COLD_BYTES / inp.blocks.size))
+        wr = [wh.to(self.dev) for _ in range(reps)]
+        t = time_launches(torch, lambda i: self.q2k.q2k_matmul_id(x, wr[i % reps], ids, y, p, stream=self.stream),
+                          n, 20)
+        experts_read = len(set(inp.ids.tolist()))
+        b = experts_read * c.n * (c.K // 256) * 84 + c.tokens * c.K * 4 + c.routes * 4 + c.routes * c.n * 4
+        log("expert-routed decode: %.2f us, %.1f GB/s" % (t * 1e6, b / t / 1e9))
+        return {"workload": c.name + " (%d experts read, %d cold weight replicas)" % (experts_read, reps),
+                "us": t * 1e6, "algorithmic_bytes": b, "GB/s": b / t / 1e9, "bound": "hbm",
+                "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
+
+    def moe_prefill(self, n=20):
+        """Expert-routed prefill: 512 tokens, top_k 6 of 8 experts (matrix-core schedule, one call)."""
+        torch = self.torch
+        log("generating expert-routed prefill inputs")
+        inp, c, p, x, ids, y = self._moe(1)
+        w = torch.from_numpy(inp.blocks).to(self.dev)
+        t = time_launches(torch, lambda i: self.q2k.q2k_matmul_id(x, w, ids, y, p, stream=self.stream), n, 3)
+        f = 2.0 * c.routes * c.n * c.K
+        log("expert-routed prefill: %.2f us, %.1f TFLOP/s" % (t * 1e6, f / t / 1e12))
+        return {"workload": c.name + " (one call: routing + bf16 row gather + GEMM)", "us": t * 1e6, "flop": f,
+                "TFLOP/s": f / t / 1e12, "bound": "mfma", "frac_bf16_mfma": f / t / 1e12 / BF16_PEAK_TFLOPS}
+
     def copy_probe(self):
         torch = self.torch
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=self.dev)
@@ -372,6 +413,8 @@ def main() -> int:
         rows["mfma_m512"] = b.mfma()
         rows["batched_mv"] = b.batched()
         rows["argmax_candidates"] = b.sample()
+        rows["moe_decode"] = b.moe_decode()
+        rows["moe_prefill"] = b.moe_prefill()
 
     # ------------------------------------------------------------------- CPU oracle baseline
     log("timing the CPU oracle (~%.0f s)" % args.cpu_seconds)

@@ -17,6 +17,12 @@ Functions carry the C names:
 * ``q2k_argmax_candidates(logits, n_slots, vocab, cap, top1_idx, top1_val,
   cand_count, overflow, cand_ids)`` — first-max argmax and the logits within
   0.5 of it, per slot.
+* ``q2k_matmul_id(x, w, ids, y, params, status=None)`` — the expert-routed
+  product (route token*top_k+slot uses expert ids[route]); ``q2k_matmul_id_path``
+  forces a schedule; ``q2k_matmul_id_pooled``, ``..._pooled_pair`` and
+  ``..._pooled_slotted`` take caller-held scratch of
+  ``q2k_matmul_id_scratch_bytes(params)`` bytes. ``params`` is a
+  ``MatmulIdParams`` (or a dict with its fields).
 * ``GGUFFile(path)`` — the GGUF tensor directory (``q2k_gguf_*``): names,
   ``tensor_info(name)`` and ``tensor_bytes(name)`` (host side, no GPU work).
 
@@ -54,6 +60,12 @@ EXPORTS = (
     "q2k_matmul_batched",
     "q2k_embedding_gather",
     "q2k_argmax_candidates",
+    "q2k_matmul_id",
+    "q2k_matmul_id_path",
+    "q2k_matmul_id_scratch_bytes",
+    "q2k_matmul_id_pooled",
+    "q2k_matmul_id_pooled_pair",
+    "q2k_matmul_id_pooled_slotted",
     "q2k_gguf_open",
     "q2k_gguf_close",
     "q2k_gguf_tensor_count",
@@ -92,6 +104,19 @@ class GGUFInfo(ctypes.Structure):
                 ("byte_len", ctypes.c_uint64)]
 
 
+class MatmulIdParams(ctypes.Structure):
+    """q2k_matmul_id_params: the expert-routed product's sizes."""
+    _fields_ = [("n_tokens", ctypes.c_uint32), ("top_k", ctypes.c_uint32), ("n", ctypes.c_uint32),
+                ("k", ctypes.c_uint32), ("n_experts", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("expert_stride", ctypes.c_uint64)]
+
+
+def _params(p) -> MatmulIdParams:
+    if isinstance(p, MatmulIdParams):
+        return p
+    return MatmulIdParams(**p)
+
+
 _lib = None
 
 
@@ -114,6 +139,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).restype = ctypes.c_int
     lib.q2k_argmax_candidates.argtypes = [P, U32, U32, U32, P, P, P, P, P, P]
     lib.q2k_argmax_candidates.restype = ctypes.c_int
+    PP = ctypes.POINTER(MatmulIdParams)
+    lib.q2k_matmul_id.argtypes = [P, P, P, P, PP, P, P]
+    lib.q2k_matmul_id_path.argtypes = [P, P, P, P, PP, P, ctypes.c_int, P]
+    lib.q2k_matmul_id_scratch_bytes.argtypes = [PP]
+    lib.q2k_matmul_id_scratch_bytes.restype = ctypes.c_uint64
+    lib.q2k_matmul_id_pooled.argtypes = [P, P, P, P, PP, P, ctypes.c_uint64, P, P]
+    lib.q2k_matmul_id_pooled_pair.argtypes = [P, P, P, P, P, P, PP, P, ctypes.c_uint64, P, P]
+    lib.q2k_matmul_id_pooled_slotted.argtypes = [P, P, P, P, PP, P, ctypes.c_uint64, P, P]
+    for name in ("q2k_matmul_id", "q2k_matmul_id_path", "q2k_matmul_id_pooled", "q2k_matmul_id_pooled_pair",
+                 "q2k_matmul_id_pooled_slotted"):
+        getattr(lib, name).restype = ctypes.c_int
     lib.q2k_gguf_open.argtypes = [ctypes.c_char_p, ctypes.POINTER(P)]
     lib.q2k_gguf_open.restype = ctypes.c_int
     lib.q2k_gguf_close.argtypes = [P]
@@ -205,6 +241,53 @@ def q2k_argmax_candidates(logits, n_slots: int, vocab: int, cap: int, top1_idx, 
     """Per slot: first-max index/value, candidate count (may exceed cap), overflow flag, candidate ids."""
     _check(load_library().q2k_argmax_candidates(_ptr(logits), n_slots, vocab, cap, _ptr(top1_idx), _ptr(top1_val),
                                                 _ptr(cand_count), _ptr(overflow), _ptr(cand_ids), _stream(stream)))
+
+
+def q2k_matmul_id(x, w, ids, y, params, status=None, stream=None) -> None:
+    """Expert-routed product; the schedule follows the page's rule (matrix cores for > 32 tokens, top_k 1/6/8)."""
+    p = _params(params)
+    _check(load_library().q2k_matmul_id(_ptr(x), _ptr(w), _ptr(ids), _ptr(y), ctypes.byref(p), _ptr(status),
+                                        _stream(stream)))
+
+
+def q2k_matmul_id_path(x, w, ids, y, params, path: int, status=None, stream=None) -> None:
+    """q2k_matmul_id with a forced schedule: PATH_AUTO, PATH_GEMV (fp32 per route) or PATH_MFMA."""
+    p = _params(params)
+    _check(load_library().q2k_matmul_id_path(_ptr(x), _ptr(w), _ptr(ids), _ptr(y), ctypes.byref(p), _ptr(status),
+                                             int(path), _stream(stream)))
+
+
+def q2k_matmul_id_scratch_bytes(params) -> int:
+    """Scratch bytes the pooled calls need (0 for invalid parameters)."""
+    p = _params(params)
+    return int(load_library().q2k_matmul_id_scratch_bytes(ctypes.byref(p)))
+
+
+def q2k_matmul_id_pooled(x, w, ids, y, params, scratch, status=None, stream=None, scratch_bytes: int | None = None):
+    """Matrix-core expert-routed product with caller-held scratch (a device tensor)."""
+    p = _params(params)
+    nb = _nbytes(scratch) if scratch_bytes is None else int(scratch_bytes)
+    _check(load_library().q2k_matmul_id_pooled(_ptr(x), _ptr(w), _ptr(ids), _ptr(y), ctypes.byref(p),
+                                               _ptr(scratch), nb, _ptr(status), _stream(stream)))
+
+
+def q2k_matmul_id_pooled_pair(x, w0, w1, ids, y0, y1, params, scratch, status=None, stream=None,
+                              scratch_bytes: int | None = None):
+    """Two weight sets (gate/up) with one routing: y0 from w0, y1 from w1."""
+    p = _params(params)
+    nb = _nbytes(scratch) if scratch_bytes is None else int(scratch_bytes)
+    _check(load_library().q2k_matmul_id_pooled_pair(_ptr(x), _ptr(w0), _ptr(w1), _ptr(ids), _ptr(y0), _ptr(y1),
+                                                    ctypes.byref(p), _ptr(scratch), nb, _ptr(status),
+                                                    _stream(stream)))
+
+
+def q2k_matmul_id_pooled_slotted(x, w, ids, y, params, scratch, status=None, stream=None,
+                                 scratch_bytes: int | None = None):
+    """One activation row per route: x [n_tokens, top_k, k], y [n_tokens, top_k, n]."""
+    p = _params(params)
+    nb = _nbytes(scratch) if scratch_bytes is None else int(scratch_bytes)
+    _check(load_library().q2k_matmul_id_pooled_slotted(_ptr(x), _ptr(w), _ptr(ids), _ptr(y), ctypes.byref(p),
+                                                       _ptr(scratch), nb, _ptr(status), _stream(stream)))
 
 
 class GGUFFile:

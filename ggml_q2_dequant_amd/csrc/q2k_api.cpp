@@ -150,6 +150,104 @@ q2k_status stream_workspace(hipStream_t st, size_t bytes, void **out) {
     return Q2K_OK;
 }
 
+// Shape rules of the expert-routed calls; sizes in bytes of x, w, ids, y.
+struct MoeShape {
+    uint32_t routes, x_div;
+    Range x, w, ids, y;
+};
+
+q2k_status check_moe_shape(const char *fn, const q2k_matmul_id_params *p, bool slotted, MoeShape *out) {
+    if (!p) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+    if (p->reserved != 0) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: params.reserved must be 0", fn);
+    if (p->n_tokens == 0 || p->top_k == 0 || p->n == 0 || p->k == 0 || p->n_experts == 0)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: n_tokens, top_k, n, k, n_experts must be >= 1 (got %u, %u, %u, %u, %u)",
+                    fn, p->n_tokens, p->top_k, p->n, p->k, p->n_experts);
+    if (p->k % q2k::kQK != 0) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: k=%u is not a multiple of 256", fn, p->k);
+    if (p->k > q2k::kMaxK) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: k=%u exceeds the limit %u", fn, p->k, q2k::kMaxK);
+    if (p->n_experts > q2k::kMoeMaxExperts)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: n_experts=%u exceeds the limit %u", fn, p->n_experts,
+                    q2k::kMoeMaxExperts);
+    uint64_t routes, t, rb, xb, wb, yb;
+    if (!mul_ok(p->n_tokens, p->top_k, &routes) || routes > q2k::kMoeMaxRoutes)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: n_tokens * top_k exceeds the limit %u", fn, q2k::kMoeMaxRoutes);
+    rb = static_cast<uint64_t>(p->k / q2k::kQK) * q2k::kBlockBytes;
+    uint64_t expert_bytes;
+    if (!mul_ok(p->n, rb, &expert_bytes)) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: size overflow", fn);
+    if (p->expert_stride < expert_bytes || p->expert_stride % 4 != 0)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: expert_stride=%llu must be a multiple of 4 and >= n * k/256 * 84 = %llu",
+                    fn, static_cast<unsigned long long>(p->expert_stride), static_cast<unsigned long long>(expert_bytes));
+    if (!mul_ok(p->n_experts - 1, p->expert_stride, &t) || t > UINT64_MAX - expert_bytes)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: size overflow", fn);
+    wb = t + expert_bytes;
+    if (!mul_ok(slotted ? routes : p->n_tokens, p->k, &t) || !mul_ok(t, 4, &xb) || !mul_ok(routes, p->n, &t) ||
+        !mul_ok(t, 4, &yb))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: size overflow", fn);
+    out->routes = static_cast<uint32_t>(routes);
+    out->x_div = slotted ? 1u : p->top_k;
+    out->x = {nullptr, xb};
+    out->w = {nullptr, wb};
+    out->ids = {nullptr, 4 * routes};
+    out->y = {nullptr, yb};
+    return Q2K_OK;
+}
+
+q2k_status check_moe(const char *fn, const float *x, const void *w, const uint32_t *ids, const float *y,
+                     const q2k_matmul_id_params *p, bool slotted, MoeShape *out) {
+    if (!x || !w || !ids || !y || !p) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+    q2k_status s = check_moe_shape(fn, p, slotted, out);
+    if (s != Q2K_OK) return s;
+    const uint64_t xb = out->x.bytes, wb = out->w.bytes, yb = out->y.bytes, routes = out->routes;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 4) || !aligned(ids, 4))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: x and y must be 16-byte aligned, w and ids 4-byte aligned", fn);
+    if (overlap(y, yb, x, xb) || overlap(y, yb, w, wb) || overlap(y, yb, ids, 4 * routes))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: y overlaps an input", fn);
+    out->x = {x, xb};
+    out->w = {w, wb};
+    out->ids = {ids, 4 * routes};
+    out->y = {y, yb};
+    return Q2K_OK;
+}
+
+q2k_status check_status_word(const char *fn, const int *status, const Range *outs, int n_outs) {
+    if (!status) return Q2K_OK;
+    if (!aligned(status, 4)) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: status must be 4-byte aligned", fn);
+    for (int i = 0; i < n_outs; ++i)
+        if (overlap(status, 4, outs[i].p, outs[i].bytes))
+            return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: status overlaps another argument", fn);
+    return Q2K_OK;
+}
+
+// The matrix-core schedule: route, gather, then one GEMM per weight set.
+q2k_status run_moe_mfma(const char *fn, const MoeShape &sh, const q2k_matmul_id_params *p, const void *w0,
+                        const void *w1, float *y0, float *y1, void *scratch, int *status, hipStream_t st) {
+    const q2k::MoeScratch sc = q2k::moe_scratch_carve(scratch, sh.routes, p->n_experts);
+    hipError_t e = q2k::launch_moe_route(static_cast<const uint32_t *>(sh.ids.p), sh.routes, p->n_experts, sc, status, st);
+    if (e == hipSuccess)
+        e = q2k::launch_moe_gather(static_cast<const float *>(sh.x.p), sh.routes, sh.x_div, p->k, sc, y0, y1, p->n, st);
+    if (e == hipSuccess)
+        e = q2k::launch_moe_gemm(static_cast<const uint8_t *>(w0), y0, sh.routes, p->n, p->k, p->n_experts,
+                                 p->expert_stride, sc, st);
+    if (e == hipSuccess && w1)
+        e = q2k::launch_moe_gemm(static_cast<const uint8_t *>(w1), y1, sh.routes, p->n, p->k, p->n_experts,
+                                 p->expert_stride, sc, st);
+    if (e != hipSuccess) return device_error(fn, e);
+    return ok();
+}
+
+q2k_status check_scratch(const char *fn, const MoeShape &sh, const q2k_matmul_id_params *p, const void *scratch,
+                         uint64_t scratch_bytes, const Range *args, int n_args) {
+    const uint64_t need = q2k::moe_scratch_bytes(sh.routes, p->n_experts, p->k);
+    if (!scratch) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: null scratch", fn);
+    if (!aligned(scratch, 256)) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: scratch must be 256-byte aligned", fn);
+    if (scratch_bytes < need)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: scratch holds %llu bytes, %llu needed", fn,
+                    static_cast<unsigned long long>(scratch_bytes), static_cast<unsigned long long>(need));
+    for (int i = 0; i < n_args; ++i)
+        if (overlap(scratch, need, args[i].p, args[i].bytes))
+            return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: scratch overlaps another argument", fn);
+    return Q2K_OK;
+}
+
 }  // namespace
 
 namespace q2k {
@@ -291,6 +389,87 @@ q2k_status q2k_argmax_candidates(const float *logits, uint32_t n_slots, uint32_t
         if (e != hipSuccess) return device_error("q2k_argmax_candidates launch", e);
     }
     return ok();
+}
+
+q2k_status q2k_matmul_id_path(const float *x, const void *w, const uint32_t *ids, float *y,
+                              const q2k_matmul_id_params *p, int *status, q2k_path path, void *stream) {
+    static const char fn[] = "q2k_matmul_id";
+    MoeShape sh;
+    q2k_status s = check_moe(fn, x, w, ids, y, p, false, &sh);
+    if (s != Q2K_OK) return s;
+    const Range args[4] = {sh.x, sh.w, sh.ids, sh.y};
+    if ((s = check_status_word(fn, status, args, 4)) != Q2K_OK) return s;
+    if (path == Q2K_PATH_AUTO)
+        path = p->n_tokens > 32 && (p->top_k == 1 || p->top_k == 6 || p->top_k == 8) ? Q2K_PATH_MFMA : Q2K_PATH_GEMV;
+    const auto st = static_cast<hipStream_t>(stream);
+    if (path == Q2K_PATH_GEMV) {
+        hipError_t e = q2k::launch_moe_gemv(x, static_cast<const uint8_t *>(w), ids, y, sh.routes, sh.x_div, p->n, p->k,
+                                            p->n_experts, p->expert_stride, status, st);
+        if (e != hipSuccess) return device_error(fn, e);
+        return ok();
+    }
+    if (path != Q2K_PATH_MFMA) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: unknown path %d", fn, static_cast<int>(path));
+    void *ws = nullptr;
+    s = stream_workspace(st, q2k::moe_scratch_bytes(sh.routes, p->n_experts, p->k), &ws);
+    if (s != Q2K_OK) return s;
+    return run_moe_mfma(fn, sh, p, w, nullptr, y, nullptr, ws, status, st);
+}
+
+q2k_status q2k_matmul_id(const float *x, const void *w, const uint32_t *ids, float *y,
+                         const q2k_matmul_id_params *p, int *status, void *stream) {
+    return q2k_matmul_id_path(x, w, ids, y, p, status, Q2K_PATH_AUTO, stream);
+}
+
+uint64_t q2k_matmul_id_scratch_bytes(const q2k_matmul_id_params *p) {
+    MoeShape sh;
+    if (check_moe_shape("q2k_matmul_id_scratch_bytes", p, false, &sh) != Q2K_OK) return 0;
+    return q2k::moe_scratch_bytes(sh.routes, p->n_experts, p->k);
+}
+
+q2k_status q2k_matmul_id_pooled(const float *x, const void *w, const uint32_t *ids, float *y,
+                                const q2k_matmul_id_params *p, void *scratch, uint64_t scratch_bytes, int *status,
+                                void *stream) {
+    static const char fn[] = "q2k_matmul_id_pooled";
+    MoeShape sh;
+    q2k_status s = check_moe(fn, x, w, ids, y, p, false, &sh);
+    if (s != Q2K_OK) return s;
+    const Range args[4] = {sh.x, sh.w, sh.ids, sh.y};
+    if ((s = check_scratch(fn, sh, p, scratch, scratch_bytes, args, 4)) != Q2K_OK) return s;
+    const Range args2[5] = {sh.x, sh.w, sh.ids, sh.y, {scratch, scratch_bytes}};
+    if ((s = check_status_word(fn, status, args2, 5)) != Q2K_OK) return s;
+    return run_moe_mfma(fn, sh, p, w, nullptr, y, nullptr, scratch, status, static_cast<hipStream_t>(stream));
+}
+
+q2k_status q2k_matmul_id_pooled_pair(const float *x, const void *w0, const void *w1, const uint32_t *ids, float *y0,
+                                     float *y1, const q2k_matmul_id_params *p, void *scratch, uint64_t scratch_bytes,
+                                     int *status, void *stream) {
+    static const char fn[] = "q2k_matmul_id_pooled_pair";
+    MoeShape s0, s1;
+    q2k_status s = check_moe(fn, x, w0, ids, y0, p, false, &s0);
+    if (s != Q2K_OK) return s;
+    if ((s = check_moe(fn, x, w1, ids, y1, p, false, &s1)) != Q2K_OK) return s;
+    if (overlap(y0, s0.y.bytes, y1, s1.y.bytes) || overlap(y0, s0.y.bytes, w1, s1.w.bytes) ||
+        overlap(y1, s1.y.bytes, w0, s0.w.bytes))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: an output overlaps the other output or weight set", fn);
+    const Range args[6] = {s0.x, s0.w, s1.w, s0.ids, s0.y, s1.y};
+    if ((s = check_scratch(fn, s0, p, scratch, scratch_bytes, args, 6)) != Q2K_OK) return s;
+    const Range args2[7] = {s0.x, s0.w, s1.w, s0.ids, s0.y, s1.y, {scratch, scratch_bytes}};
+    if ((s = check_status_word(fn, status, args2, 7)) != Q2K_OK) return s;
+    return run_moe_mfma(fn, s0, p, w0, w1, y0, y1, scratch, status, static_cast<hipStream_t>(stream));
+}
+
+q2k_status q2k_matmul_id_pooled_slotted(const float *x, const void *w, const uint32_t *ids, float *y,
+                                        const q2k_matmul_id_params *p, void *scratch, uint64_t scratch_bytes,
+                                        int *status, void *stream) {
+    static const char fn[] = "q2k_matmul_id_pooled_slotted";
+    MoeShape sh;
+    q2k_status s = check_moe(fn, x, w, ids, y, p, true, &sh);
+    if (s != Q2K_OK) return s;
+    const Range args[4] = {sh.x, sh.w, sh.ids, sh.y};
+    if ((s = check_scratch(fn, sh, p, scratch, scratch_bytes, args, 4)) != Q2K_OK) return s;
+    const Range args2[5] = {sh.x, sh.w, sh.ids, sh.y, {scratch, scratch_bytes}};
+    if ((s = check_status_word(fn, status, args2, 5)) != Q2K_OK) return s;
+    return run_moe_mfma(fn, sh, p, w, nullptr, y, nullptr, scratch, status, static_cast<hipStream_t>(stream));
 }
 
 q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *out, uint32_t vocab,

@@ -131,6 +131,17 @@ struct GemvBatch {
     uint64_t x_elems, w_bytes, y_elems;
 };
 
+// Expert-routed GEMV: grid.y walks routes route0 ..; route r multiplies
+// activation row r / x_div by expert ids[r] (expert_stride bytes apart) into
+// output row r. A route whose id is >= n_experts reads nothing, writes NaN to
+// its row and raises *status (when status is not null).
+struct GemvRoute {
+    const uint32_t *ids;
+    int *status;
+    uint64_t expert_stride;
+    uint32_t route0, x_div, n_experts;
+};
+
 // ---------------------------------------------------------------------------
 // fp32 GEMV for M <= 2 (decode).
 //
@@ -201,17 +212,32 @@ __device__ __forceinline__ SegLoads load_seg(__amdgpu_buffer_rsrc_t rs, uint32_t
     return t;
 }
 
-template <int M, int NI>
+template <int M, int NI, bool kRouted>
 __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, const uint8_t *__restrict__ w,
-                                                  float *__restrict__ y, uint32_t N, uint32_t K, GemvBatch bt) {
+                                                  float *__restrict__ y, uint32_t N, uint32_t K, GemvBatch bt,
+                                                  GemvRoute rt) {
     __shared__ float red[4][NI * 4 * M];
-    x += blockIdx.y * bt.x_elems;
-    w += blockIdx.y * bt.w_bytes;
-    y += blockIdx.y * bt.y_elems;
     const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1);
+    const uint32_t row0 = blockIdx.x * (4 * NI);
+    if constexpr (kRouted) {
+        static_assert(M == 1, "routes are single activation rows");
+        const uint32_t r = rt.route0 + blockIdx.y;
+        const uint32_t e = rt.ids[r];
+        y += static_cast<uint64_t>(r) * N;
+        if (e >= rt.n_experts) {
+            if (tid < 4 * NI && row0 + tid < N) y[row0 + tid] = __builtin_nanf("");
+            if (tid == 0 && rt.status) __hip_atomic_store(rt.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            return;
+        }
+        x += static_cast<uint64_t>(r / rt.x_div) * K;
+        w += e * rt.expert_stride;
+    } else {
+        x += blockIdx.y * bt.x_elems;
+        w += blockIdx.y * bt.w_bytes;
+        y += blockIdx.y * bt.y_elems;
+    }
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const uint32_t rr = lane >> 4, bq = (lane >> 2) & 3u, g = lane & 3u, h = g >> 1, s = g & 1u;
-    const uint32_t row0 = blockIdx.x * (4 * NI);
     const uint32_t nb = K >> 8;
     const uint32_t row_bytes = nb * kBlockBytes;
 
@@ -576,8 +602,21 @@ struct GemmRaw {
     uint32_t dd[2];
 };
 
+// Expert-routed mode: tile tm of the M dimension is tiles[tm], a run of
+// rows of the expert-ordered activations (bf16, p0 .. p0 + count - 1) that
+// all use one expert's weights; row p of the run is written to output row
+// perm[p]. Unused tile entries (count 0) end their workgroups at once.
+struct GemmRoute {
+    const MoeTile *tiles;
+    const uint32_t *perm;
+    uint64_t expert_stride;
+};
+static_assert(kGM == kMoeTileRows, "routing tiles must match the GEMM's M tile");
+
+template <bool kRouted>
 __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb, const uint8_t *__restrict__ w,
-                                                  float *__restrict__ y, uint32_t M, uint32_t N, uint32_t K) {
+                                                  float *__restrict__ y, uint32_t M, uint32_t N, uint32_t K,
+                                                  uint32_t tiles_m, GemmRoute rg) {
     // Eight wavefronts, two per SIMD: group g = wave / 4 runs the MFMAs of K
     // half g for the whole 128 x 256 tile (wavefront wave % 4 owns columns
     // 64 (wave % 4) .. +63), so while one wavefront of a SIMD waits on a
@@ -598,16 +637,34 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
     const uint32_t gtid = tid & 255u;
     const uint32_t kh = lane >> 5, col = lane & 31u;
     uint32_t tm, tn;
-    gemm_tile(blockIdx.x, (M + kGM - 1) / kGM, (N + kGN - 1) / kGN, &tm, &tn);
-    const uint32_t m0 = tm * kGM, n0 = tn * kGN;
+    gemm_tile(blockIdx.x, tiles_m, (N + kGN - 1) / kGN, &tm, &tn);
+    const uint32_t n0 = tn * kGN;
     const uint32_t nb = K >> 8, row_bytes = nb * kBlockBytes;
+    // rows: valid rows of the tile; xt, wt: its activations and weight matrix.
+    __shared__ uint32_t rowmap[kGM];
+    uint32_t m0 = 0, rows;
+    const __bf16 *xt;
+    const uint8_t *wt;
+    if constexpr (kRouted) {
+        const MoeTile t = rg.tiles[tm];
+        if (t.count == 0) return;
+        rows = t.count;
+        xt = xb + static_cast<uint64_t>(t.p0) * K;
+        wt = w + t.expert * rg.expert_stride;
+        if (tid < kGM) rowmap[tid] = tid < rows ? rg.perm[t.p0 + tid] : 0u;
+    } else {
+        m0 = tm * kGM;
+        rows = min(kGM, M - m0);
+        xt = xb + static_cast<uint64_t>(m0) * K;
+        wt = w;
+    }
     // Group g takes half-blocks [g nb, (g + 1) nb): 2 nb steps of 64 k each.
     const uint32_t hb0 = grp * nb, s0 = 2 * hb0, steps = 2 * nb;
 
     // Rows past M or N lie beyond these descriptors and load as zeros.
-    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(xb + static_cast<uint64_t>(m0) * K, min(kGM, M - m0) * K * 2u);
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(xt, rows * K * 2u);
     const __amdgpu_buffer_rsrc_t wr =
-        buffer_rsrc(w + static_cast<uint64_t>(n0) * row_bytes, min(kGN, N - n0) * row_bytes);
+        buffer_rsrc(wt + static_cast<uint64_t>(n0) * row_bytes, min(kGN, N - n0) * row_bytes);
 
     // Activation staging: chunk c = gtid + 256 i (i < 4) of the group's 128 x 64
     // tile is row c / 8, bf16 columns 8 (c % 8) .. +7; step s adds 128 bytes.
@@ -776,7 +833,7 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
     __syncthreads();
     const uint32_t partner = wave ^ 4u;
     // D layout of a 32x32 tile: lane l holds column l % 32, rows 8(v/4) + 4(l/32) + v%4.
-    const bool full = m0 + kGM <= M && n0 + kGN <= N;
+    const bool full = rows == kGM && n0 + kGN <= N;
     auto finish = [&](int base, bool lower_is_mine) {
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii)
@@ -789,8 +846,9 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
                     const float other = swap[((partner * 64u) + 32u * ii + 16u * jj + v) * 64u + lane];
                     const float mine = acc[base + ii][jj][v];
                     const float sum = lower_is_mine ? mine + other : other + mine;
-                    const uint32_t m = m0 + 32u * i + 8u * (v >> 2) + 4u * kh + (v & 3);
-                    if (full || (m < M && n < N)) y[static_cast<uint64_t>(m) * N + n] = sum;
+                    const uint32_t m = 32u * i + 8u * (v >> 2) + 4u * kh + (v & 3);
+                    const uint32_t dst = kRouted ? rowmap[m] : m0 + m;
+                    if (full || (m < rows && n < N)) y[static_cast<uint64_t>(dst) * N + n] = sum;
                 }
                 __builtin_amdgcn_sched_barrier(0);  // one 16-value group live at a time
             }
@@ -804,7 +862,8 @@ hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t 
                            GemvBatch bt, hipStream_t stream) {
     constexpr int NI = Q2K_GEMV_SEG_ITERS;
     const uint32_t blocks = (N + 4 * NI - 1) / (4 * NI);
-    hipLaunchKernelGGL((k_gemv_seg<M, NI>), dim3(blocks, batches), dim3(256), 0, stream, x, w, y, N, K, bt);
+    hipLaunchKernelGGL((k_gemv_seg<M, NI, false>), dim3(blocks, batches), dim3(256), 0, stream, x, w, y, N, K, bt,
+                       GemvRoute{});
     return hipGetLastError();
 }
 
@@ -868,10 +927,38 @@ hipError_t launch_gemm_mfma(const float *x, const uint8_t *w, float *y, uint32_t
     const uint64_t want = (n8 + 256 * kXU - 1) / (256 * kXU);
     hipLaunchKernelGGL(k_x_to_bf16, dim3(static_cast<uint32_t>(want < 1024u ? want : 1024u)), dim3(256), 0, stream,
                        reinterpret_cast<const float4 *>(x), static_cast<bf16x8 *>(x_bf16), n8);
-    const uint64_t tiles = static_cast<uint64_t>((N + kGN - 1) / kGN) * ((M + kGM - 1) / kGM);
+    const uint32_t tiles_m = (M + kGM - 1) / kGM;
+    const uint64_t tiles = static_cast<uint64_t>((N + kGN - 1) / kGN) * tiles_m;
     if (tiles > 0x7fffffffu) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_gemm_q2k, dim3(static_cast<uint32_t>(tiles)), dim3(512), 0, stream,
-                       static_cast<const __bf16 *>(x_bf16), w, y, M, N, K);
+    hipLaunchKernelGGL(k_gemm_q2k<false>, dim3(static_cast<uint32_t>(tiles)), dim3(512), 0, stream,
+                       static_cast<const __bf16 *>(x_bf16), w, y, M, N, K, tiles_m, GemmRoute{});
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_gemv(const float *x, const uint8_t *w, const uint32_t *ids, float *y, uint32_t routes,
+                           uint32_t x_div, uint32_t N, uint32_t K, uint32_t n_experts, uint64_t expert_stride,
+                           int *status, hipStream_t stream) {
+    constexpr int NI = Q2K_GEMV_SEG_ITERS;
+    const uint32_t blocks = (N + 4 * NI - 1) / (4 * NI);
+    for (uint32_t r0 = 0; r0 < routes; r0 += kMaxGridY) {
+        const uint32_t nr = routes - r0 < kMaxGridY ? routes - r0 : kMaxGridY;
+        const GemvRoute rt{ids, status, expert_stride, r0, x_div, n_experts};
+        hipLaunchKernelGGL((k_gemv_seg<1, NI, true>), dim3(blocks, nr), dim3(256), 0, stream, x, w, y, N, K,
+                           GemvBatch{}, rt);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_moe_gemm(const uint8_t *w, float *y, uint32_t routes, uint32_t N, uint32_t K, uint32_t n_experts,
+                           uint64_t expert_stride, MoeScratch s, hipStream_t stream) {
+    const uint32_t tiles_m = moe_tiles_max(routes, n_experts);
+    const uint64_t tiles = static_cast<uint64_t>((N + kGN - 1) / kGN) * tiles_m;
+    if (tiles > 0x7fffffffu) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_gemm_q2k<true>, dim3(static_cast<uint32_t>(tiles)), dim3(512), 0, stream,
+                       static_cast<const __bf16 *>(s.x_bf16), w, y, routes, N, K, tiles_m,
+                       GemmRoute{s.tiles, s.perm, expert_stride});
     return hipGetLastError();
 }
 

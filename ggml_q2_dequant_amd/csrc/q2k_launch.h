@@ -43,4 +43,41 @@ hipError_t launch_argmax_candidates(const float *logits, uint32_t n_slots, uint3
                                     uint32_t *top1_idx, float *top1_val, uint32_t *cand_count, uint32_t *overflow,
                                     uint32_t *cand_ids, void *workspace, hipStream_t stream);
 
+// Expert-routed product (routing and row gather in q2k_moe.hip, the routed
+// modes of the GEMV and GEMM kernels in q2k_kernels.hip). Route r of
+// n_tokens * top_k takes expert ids[r] and activation row r / x_div (x_div =
+// top_k, or 1 when every route has its own row); its output row is r.
+constexpr uint32_t kMoeMaxExperts = 512;     // LDS tables of the routing kernel
+constexpr uint32_t kMoeMaxRoutes = 1u << 24;
+constexpr uint32_t kMoeTileRows = 128;       // rows of one matrix-core tile
+
+struct MoeTile {
+    uint32_t expert, p0, count;  // rows p0 .. p0 + count - 1 of the expert-ordered list; count 0 = unused
+};
+
+// Device arrays carved from one scratch buffer (moe_scratch_bytes long).
+struct MoeScratch {
+    uint32_t *hdr;    // [4]: valid routes, tiles in use, routes with a bad id
+    uint32_t *perm;   // [routes]: the route at each row of the expert order, then the bad routes
+    MoeTile *tiles;   // [moe_tiles_max]
+    void *x_bf16;     // [routes, K] bf16 activations in expert order
+};
+uint32_t moe_tiles_max(uint32_t routes, uint32_t n_experts);
+uint64_t moe_scratch_bytes(uint32_t routes, uint32_t n_experts, uint32_t K);
+MoeScratch moe_scratch_carve(void *base, uint32_t routes, uint32_t n_experts);
+
+// fp32 path: one M = 1 GEMV per route; a route with a bad id gets a NaN row.
+hipError_t launch_moe_gemv(const float *x, const uint8_t *w, const uint32_t *ids, float *y, uint32_t routes,
+                           uint32_t x_div, uint32_t N, uint32_t K, uint32_t n_experts, uint64_t expert_stride,
+                           int *status, hipStream_t stream);
+// Matrix-core path, step 1: group routes by expert (stable), build the tile list.
+hipError_t launch_moe_route(const uint32_t *ids, uint32_t routes, uint32_t n_experts, MoeScratch s, int *status,
+                            hipStream_t stream);
+// Step 2: bf16 activations in expert order; NaN rows of y0 (and y1) for bad ids.
+hipError_t launch_moe_gather(const float *x, uint32_t routes, uint32_t x_div, uint32_t K, MoeScratch s, float *y0,
+                             float *y1, uint32_t N, hipStream_t stream);
+// Step 3: the tiles' products, written to their routes' rows of y.
+hipError_t launch_moe_gemm(const uint8_t *w, float *y, uint32_t routes, uint32_t N, uint32_t K, uint32_t n_experts,
+                           uint64_t expert_stride, MoeScratch s, hipStream_t stream);
+
 }  // namespace q2k

@@ -125,6 +125,96 @@ q2k_status q2k_matmul_batched(const float *x, const void *w, float *y, uint32_t 
                               uint32_t K, void *stream);
 
 /*
+ * Expert-routed product (mixture-of-experts "mm_id").
+ * Page: fn run_expert (GgmlQuantizedMatmulIdParams { n_tokens, top_k, n, k,
+ * n_experts, expert_stride }; tests q2_k_expert_routed_metal_matches_reference,
+ * q2_k_expert_mm_id_top_k_6_matches_reference,
+ * q2_k_public_prefill_top_k_6_matches_reference) and test
+ * q2_k_slotted_down_mm_is_byte_identical_to_flattened_rows.
+ * Route r = token * top_k + slot (0 <= r < n_tokens * top_k) multiplies an
+ * activation row by expert e = ids[r]:
+ *     y[r, j] = sum_k x[row(r), k] * W_e[j, k],   j < n,
+ * with row(r) = r / top_k (x is [n_tokens, k]) or, for the slotted call,
+ * row(r) = r (x is [n_tokens, top_k, k]). Expert e's weights are n rows of
+ * k/256 Q2_K blocks (layout as for q2k_matmul) starting e * expert_stride
+ * bytes into w.
+ *   x       device f32, 16-byte aligned.
+ *   w       device Q2_K bytes, (n_experts - 1) * expert_stride + n * k/256 * 84
+ *           long; 4-byte aligned. Bytes between experts are never read.
+ *   ids     device u32 [n_tokens, top_k]; 4-byte aligned; any values.
+ *   y       device f32 [n_tokens * top_k, n]; 16-byte aligned.
+ *   status  device int or NULL. A route whose id is >= n_experts reads no
+ *           weights and gets a row of NaN; if any route does, *status is set
+ *           to 1 (never cleared by libq2k). The call itself still returns
+ *           Q2K_OK: ids live on the device and are not waited for.
+ * Limits: n_tokens, top_k, n >= 1; k a multiple of 256, 256 <= k <= 2^21;
+ * 1 <= n_experts <= 512; n_tokens * top_k <= 2^24; expert_stride a multiple
+ * of 4 and >= n * k/256 * 84. Outputs may not overlap inputs (or each other).
+ * Two schedules compute it:
+ *   - fp32 mat-vec per route (Q2K_PATH_GEMV): |y - exact| <= 1e-5 * sum|x*w|;
+ *     route r's row is bit-identical to q2k_matmul(x row, W_e, M = 1).
+ *   - matrix-core (Q2K_PATH_MFMA): routes grouped by expert in increasing
+ *     route order, bf16(x) * bf16(w) with fp32 accumulation in tiles of up to
+ *     128 routes: |y - exact| <= 4e-3 * sum|x*w| + 1e-6. The rows of expert e
+ *     are bit-identical to q2k_matmul_path(.., Q2K_PATH_MFMA) of W_e with the
+ *     activation rows routed to e, stacked in route order.
+ * Asynchronous on `stream`.
+ */
+typedef struct q2k_matmul_id_params {
+    uint32_t n_tokens;      /* tokens, >= 1 */
+    uint32_t top_k;         /* routes per token, >= 1 */
+    uint32_t n;             /* weight rows per expert = output columns, >= 1 */
+    uint32_t k;             /* activation width, a multiple of 256 */
+    uint32_t n_experts;     /* 1 .. 512 */
+    uint32_t reserved;      /* must be 0 */
+    uint64_t expert_stride; /* bytes from one expert's weights to the next */
+} q2k_matmul_id_params;
+
+/* q2k_matmul_id — the routed product with libq2k choosing the schedule the way
+ * the page's test tolerances do: the matrix-core schedule when n_tokens > 32
+ * and top_k is 1, 6 or 8, the fp32 mat-vec otherwise. The matrix-core schedule
+ * uses the per-(device, stream) workspace (see q2k_matmul). */
+q2k_status q2k_matmul_id(const float *x, const void *w, const uint32_t *ids, float *y,
+                         const q2k_matmul_id_params *p, int *status, void *stream);
+
+/* q2k_matmul_id with an explicit schedule (Q2K_PATH_AUTO = q2k_matmul_id). */
+q2k_status q2k_matmul_id_path(const float *x, const void *w, const uint32_t *ids, float *y,
+                              const q2k_matmul_id_params *p, int *status, q2k_path path, void *stream);
+
+/* Bytes of caller-held scratch the pooled calls need for these parameters
+ * (the slotted call needs the same), or 0 if the parameters are invalid. */
+uint64_t q2k_matmul_id_scratch_bytes(const q2k_matmul_id_params *p);
+
+/* q2k_matmul_id_pooled — the matrix-core schedule with caller-held scratch
+ * (page: quantized_matmul_id_ggml_pooled with IdMmScratch). scratch is device
+ * memory of at least q2k_matmul_id_scratch_bytes(p) bytes, 256-byte aligned,
+ * not overlapping any argument; its contents on entry do not matter and it
+ * is in use until the call's work on `stream` ends. Same result, bit for bit,
+ * as q2k_matmul_id_path(.., Q2K_PATH_MFMA, ..). */
+q2k_status q2k_matmul_id_pooled(const float *x, const void *w, const uint32_t *ids, float *y,
+                                const q2k_matmul_id_params *p, void *scratch, uint64_t scratch_bytes,
+                                int *status, void *stream);
+
+/* q2k_matmul_id_pooled_pair — two weight sets with one routing (page:
+ * quantized_matmul_id_ggml_pooled_pair, the gate/up projections): y0 from w0
+ * and y1 from w1, both laid out as w. The routing, bf16 activations and tile
+ * schedule are shared, so each output equals, bit for bit, a pooled call on
+ * its own weights (the page's "prepared schedule preserves ordinary mm_id
+ * output" check: w0 == w1 gives y0 == y1). y0 and y1 may not overlap. */
+q2k_status q2k_matmul_id_pooled_pair(const float *x, const void *w0, const void *w1, const uint32_t *ids,
+                                     float *y0, float *y1, const q2k_matmul_id_params *p, void *scratch,
+                                     uint64_t scratch_bytes, int *status, void *stream);
+
+/* q2k_matmul_id_pooled_slotted — one activation row per route (page:
+ * quantized_matmul_id_ggml_pooled_slotted, the down projection): x is
+ * [n_tokens, top_k, k] and y [n_tokens, top_k, n]. Byte-identical to
+ * q2k_matmul_id_pooled on the flattened problem (n_tokens * top_k tokens,
+ * top_k = 1, the same ids). */
+q2k_status q2k_matmul_id_pooled_slotted(const float *x, const void *w, const uint32_t *ids, float *y,
+                                        const q2k_matmul_id_params *p, void *scratch, uint64_t scratch_bytes,
+                                        int *status, void *stream);
+
+/*
  * q2k_embedding_gather — out[t, :] = decoded row ids[t] of a Q2_K table.
  * Page: test q2_k_embedding_gather_matches_canonical_rows_and_rejects_bad_ids
  * (EmbeddingQ2KParams { vocab_size, embed_dim, n_tokens }; an id equal to

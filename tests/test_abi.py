@@ -150,6 +150,77 @@ def test_argmax_candidates_rejects_null_misaligned_and_overlap(lib):
     _err(lib, lib.q2k_argmax_candidates(A, 2, 8, 4, B, C, D, E, E + 4, None), "overlap each other")
 
 
+# ---------------------------------------------------------------- expert-routed product
+
+def _idp(**kw):
+    d = dict(n_tokens=2, top_k=2, n=8, k=256, n_experts=3, reserved=0, expert_stride=8 * 84)
+    d.update(kw)
+    return q2k.MatmulIdParams(**d)
+
+
+def _id(lib, p, x=A, w=B, ids=C, y=D, status=None, path=0):
+    return lib.q2k_matmul_id_path(x, w, ids, y, ctypes.byref(p), status, path, None)
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(n_tokens=0), ">= 1"), (dict(top_k=0), ">= 1"), (dict(n=0), ">= 1"), (dict(n_experts=0), ">= 1"),
+    (dict(k=0), ">= 1"), (dict(k=300), "multiple of 256"), (dict(k=(1 << 21) + 256), "exceeds the limit"),
+    (dict(n_experts=513), "exceeds the limit"), (dict(n_tokens=1 << 13, top_k=(1 << 11) + 1), "exceeds the limit"),
+    (dict(expert_stride=8 * 84 - 4), "expert_stride"), (dict(expert_stride=8 * 84 + 2), "expert_stride"),
+    (dict(reserved=1), "reserved"),
+])
+def test_matmul_id_rejects_bad_params(lib, kw, frag):
+    _err(lib, _id(lib, _idp(**kw)), frag)
+    assert lib.q2k_matmul_id_scratch_bytes(ctypes.byref(_idp(**kw))) == 0
+
+
+def test_matmul_id_rejects_null_misaligned_overlap_and_bad_path(lib):
+    p = _idp()
+    _err(lib, _id(lib, p, x=None), "null")
+    _err(lib, lib.q2k_matmul_id_path(A, B, C, D, None, None, 0, None), "null")
+    _err(lib, _id(lib, p, x=A + 4), "aligned")
+    _err(lib, _id(lib, p, w=B + 2), "aligned")
+    _err(lib, _id(lib, p, ids=C + 1), "aligned")
+    _err(lib, _id(lib, p, y=A + 2 * 256 * 4 - 16), "overlaps an input")     # end of x
+    _err(lib, _id(lib, p, y=B + 3 * 8 * 84 - 16), "overlaps an input")      # last expert of w
+    _err(lib, _id(lib, p, y=C), "overlaps an input")
+    _err(lib, _id(lib, p, status=E + 2), "status")
+    _err(lib, _id(lib, p, status=D + 4 * 8 * 4 - 4), "status overlaps")
+    _err(lib, _id(lib, p, path=7), "unknown path")
+
+
+def test_matmul_id_scratch_bytes_cover_the_bf16_rows(lib):
+    for tokens, top_k, k, experts in ((2, 2, 256, 3), (33, 6, 256, 8), (512, 6, 4096, 8), (1, 1, 256, 1)):
+        p = _idp(n_tokens=tokens, top_k=top_k, k=k, n_experts=experts, expert_stride=8 * k // 256 * 84)
+        b = lib.q2k_matmul_id_scratch_bytes(ctypes.byref(p))
+        assert b >= 2 * tokens * top_k * k + 4 * tokens * top_k
+    assert lib.q2k_matmul_id_scratch_bytes(None) == 0
+
+
+def test_matmul_id_pooled_rejects_bad_scratch(lib):
+    p = _idp()
+    need = lib.q2k_matmul_id_scratch_bytes(ctypes.byref(p))
+    pooled = lib.q2k_matmul_id_pooled
+    _err(lib, pooled(A, B, C, D, ctypes.byref(p), None, need, None, None), "null scratch")
+    _err(lib, pooled(A, B, C, D, ctypes.byref(p), F + 128, need, None, None), "256-byte aligned")
+    _err(lib, pooled(A, B, C, D, ctypes.byref(p), F, need - 1, None, None), "needed")
+    _err(lib, pooled(A, B, C, D, ctypes.byref(p), A - 256, need, None, None), "scratch overlaps")
+    _err(lib, pooled(A, B, C, D, ctypes.byref(p), F, need, F + 64, None), "status overlaps")
+    slotted = lib.q2k_matmul_id_pooled_slotted
+    # Slotted: x holds one row per route (4 rows), so y right after 2 rows overlaps it.
+    _err(lib, slotted(A, B, C, A + 2 * 256 * 4, ctypes.byref(p), F, need, None, None), "overlaps an input")
+
+
+def test_matmul_id_pair_rejects_overlapping_outputs(lib):
+    p = _idp()
+    need = lib.q2k_matmul_id_scratch_bytes(ctypes.byref(p))
+    pair = lib.q2k_matmul_id_pooled_pair
+    _err(lib, pair(A, B, B, C, D, D + 64, ctypes.byref(p), F, need, None, None), "overlaps the other")
+    _err(lib, pair(A, B, G, C, D, G, ctypes.byref(p), F, need, None, None), "overlaps an input")
+    _err(lib, pair(A, B, G, C, G, E, ctypes.byref(p), F, need, None, None), "overlaps the other")
+    _err(lib, pair(A, B, B, C, D, None, ctypes.byref(p), F, need, None, None), "null")
+
+
 def test_python_binding_raises_typed_errors(lib):
     with pytest.raises(q2k.Q2KInvalidArgument, match="multiple of 256"):
         q2k.q2k_matmul(A, B, C, 1, 8, 100, stream=0)
