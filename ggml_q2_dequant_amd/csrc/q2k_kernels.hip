@@ -90,10 +90,6 @@ __global__ __launch_bounds__(256) void k_gather(const uint8_t *__restrict__ tabl
 
 // ---------------------------------------------------------------------------
 // Cross-lane helpers (DPP, gfx9 encodings).
-constexpr int kDppQuadBcast0 = 0x00;   // quad_perm [0,0,0,0]
-constexpr int kDppQuadBcast1 = 0x55;   // quad_perm [1,1,1,1]
-constexpr int kDppQuadBcast2 = 0xAA;   // quad_perm [2,2,2,2]
-constexpr int kDppQuadBcast3 = 0xFF;   // quad_perm [3,3,3,3]
 constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppRowRor4 = 0x124;
@@ -102,25 +98,6 @@ constexpr int kDppRowRor8 = 0x128;
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
-}
-
-// The four code bytes of a dword at one 2-bit position, as floats q * 2^-9:
-// masked to 0..3 per byte, each byte is an OCP e4m3 subnormal of that value.
-constexpr float kCodeScale = 512.0f;  // 2^9 undoes the e4m3 subnormal scale exactly
-
-__device__ __forceinline__ void codes4(uint32_t v, uint32_t shift, float *q) {
-    const int c = static_cast<int>((v >> shift) & 0x03030303u);
-    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
-    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
-    q[0] = lo[0];
-    q[1] = lo[1];
-    q[2] = hi[0];
-    q[3] = hi[1];
 }
 
 // Batched GEMV: grid.y walks independent problems laid out batch-major;
@@ -359,161 +336,244 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
 }
 
 // ---------------------------------------------------------------------------
-// fp32 GEMV for 3 <= M <= 8 (batched decode).
+// Matrix-core GEMV for 3 <= M <= 8, accurate to fp32 level.
 //
-// A 512-thread workgroup owns a run of consecutive weight rows and walks K in
-// chunks of 16 blocks (4096 weights). Lane l of wavefront w owns one
-// sub-block of the chunk: block 4 (w % 4) + l / 16, half h = (l / 8) % 2, code
-// segment s = (l / 4) % 2 and 2-bit position p = l % 4, i.e. the 16 weights
-// 128 h + 32 p + 16 s + i that share scale byte 8h + 2p + s. Its 16 * M
-// activations stay in registers while the workgroup sweeps its rows in
-// batches of R; wavefronts 0-3 take the even batches and 4-7 the odd ones,
-// two wavefronts per SIMD, so one's latency hides under the other's FMAs.
-// For each row the lane forms T_m = sum_i q_i x[m, i] and the partial
-// dl * T_m - ml * sum_i x[m, i]; the four lanes of a quad share the
-// segment's 16 code bytes (one dword each, passed around with DPP). A batch's
-// partials are summed over its four wavefronts through LDS in a fixed order
-// (lanes, then wavefronts) and added to per-row totals chunk by chunk, so each
-// output row depends only on its own activation row.
-constexpr uint32_t kGemvMaxBatches = 16;  // rows per workgroup <= 16 batches (host-checked)
+// Per 256-weight block the product is split as
+//   sum_k x[m,k] w[n,k] = d * sum_k x[m,k] sc(k) q(k) - dmin * sum_s mn(s) sum_{k in s} x[m,k],
+// and both sums run on the matrix cores in f16 with fp32 accumulation:
+//  - B holds the integers sc * q (<= 45) and mn (<= 15) as the raw bits of f16
+//    subnormals, i.e. v * 2^-24 exactly: 2-bit codes become f16 operands with a
+//    byte permute, a mask and a 24-bit multiply, no conversion instruction;
+//  - A holds x in two f16 pieces (x' = h1 + h2 to 2^-22 of |x'|), after scaling
+//    each row of each block by a power of two 2^s so its largest |x| lies in
+//    [2^13, 2^14). Products h * v * 2^-24 are exact in fp32.
+// k_mv_prep builds the A fragments once per call; k_gemv_mfma streams the
+// weights. Codes at 2-bit position p are masked in place (value 4^p q for
+// p < 3, 4q for p = 3 after a 4-bit shift), so the A pieces of position p
+// carry the inverse factor 1, 1/4, 1/16 or 1/4 (exact powers of two).
+//
+// MFMA v_mfma_f32_16x16x32_f16: lane l holds A row l % 16 (m = row % 8, piece =
+// row / 8) and k = 8 (l / 16) .. +7, B column l % 16 and the same k, and D
+// rows 4 (l / 16) .. +3 of column l % 16. MFMA j (0..7) of a block covers code
+// segment G = l / 16 (the 16 code bytes 16 G .. 16 G + 15), 2-bit position
+// p = j / 2 and bytes 8 (j % 2) .. +7 of the segment: block elements
+// 128 (G / 2) + 32 p + 16 (G % 2) + 8 (j % 2) + i, i < 8, all of sub-block
+// 8 (G / 2) + 2 p + G % 2. The min term is one v_mfma_f32_16x16x16_f16 per
+// block with k = sub-block (lane l: sub-blocks 4 (l / 16) .. +3).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int M>
-struct GemvRowsCfg {
-    static constexpr int kR = M <= 5 ? 8 : 4;  // rows per batch (register budget)
-    static constexpr int kV = kR * M;          // partial sums per lane per batch
+constexpr uint32_t kMvTiles = 4;             // 16-column tiles per workgroup
+constexpr uint32_t kMvWaves = 16;
+constexpr uint32_t kMvFragBytes = 8 * 64 * 16;                  // A fragments of one block
+constexpr uint32_t kMvMinsOff = kMvFragBytes;                   // min-term A fragments (64 x 8 B)
+constexpr uint32_t kMvScaleOff = kMvMinsOff + 64 * 8;           // 8 inverse row scales
+constexpr uint32_t kMvPrepBytes = kMvScaleOff + 8 * 4;          // per (problem, block)
+static_assert(kMvPrepBytes % 16 == 0, "prep records stay 16-byte aligned");
+
+__device__ __forceinline__ void f16_pieces(float v, _Float16 *h1, _Float16 *h2) {
+    const _Float16 a = static_cast<_Float16>(v);
+    *h1 = a;
+    *h2 = static_cast<_Float16>(v - static_cast<float>(a));
+}
+
+// grid (K / 256, problems); 256 threads, thread t <-> element t of the block
+// in every row. x of problem p starts at p * x_elems. Row maxima and sub-block
+// sums are lane-shuffle trees (sub-block s is lanes 16 (s % 4) .. +15 of
+// wavefront s / 4); the scaled rows are staged element-major in LDS.
+__global__ __launch_bounds__(256) void k_mv_prep(const float *__restrict__ x, uint8_t *__restrict__ ws, uint32_t M,
+                                                 uint32_t K, uint64_t x_elems) {
+    __shared__ float xs[256][8];
+    __shared__ float wmax[4][8];
+    __shared__ float sub[16][8];
+    __shared__ float fwd[8];
+    const uint32_t b = blockIdx.x, t = threadIdx.x, lane = t & 63u, wave = t >> 6, nb = K >> 8;
+    const float *xb = x + blockIdx.y * x_elems + b * 256u;
+    uint8_t *rec = ws + (static_cast<uint64_t>(blockIdx.y) * nb + b) * kMvPrepBytes;
+    float v[8], a[8], sm[8];
+#pragma unroll
+    for (uint32_t m = 0; m < 8; ++m) v[m] = m < M ? xb[static_cast<uint64_t>(m) * K + t] : 0.0f;
+#pragma unroll
+    for (uint32_t m = 0; m < 8; ++m) {
+        a[m] = __builtin_fabsf(v[m]);
+        sm[m] = v[m];
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+        for (uint32_t m = 0; m < 8; ++m) {
+            a[m] = __builtin_fmaxf(a[m], __shfl_xor(a[m], o, 64));
+            sm[m] += __shfl_xor(sm[m], o, 64);
+        }
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1)
+#pragma unroll
+        for (uint32_t m = 0; m < 8; ++m) a[m] = __builtin_fmaxf(a[m], __shfl_xor(a[m], o, 64));
+    if ((lane & 15u) == 0) {
+#pragma unroll
+        for (uint32_t m = 0; m < 8; ++m) sub[t >> 4][m] = sm[m];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (uint32_t m = 0; m < 8; ++m) wmax[wave][m] = a[m];
+    }
+    __syncthreads();
+    // s = 13 - floor(log2 max): the scaled row lies in [2^13, 2^14). A subnormal
+    // maximum counts as 2^-127; zero, inf or NaN maxima leave the row unscaled.
+    if (t < 8) {
+        const float mx = __builtin_fmaxf(__builtin_fmaxf(wmax[0][t], wmax[1][t]), __builtin_fmaxf(wmax[2][t], wmax[3][t]));
+        int s = 0;
+        if (mx > 0.0f && mx <= 3.4e38f) {
+            const int e = static_cast<int>(__builtin_bit_cast(uint32_t, mx) >> 23) - 127;
+            s = 13 - e;
+            s = s < -100 ? -100 : (s > 100 ? 100 : s);
+        }
+        fwd[t] = __builtin_bit_cast(float, static_cast<uint32_t>(127 + s) << 23);
+        reinterpret_cast<float *>(rec + kMvScaleOff)[t] = __builtin_bit_cast(float, static_cast<uint32_t>(127 - s) << 23);
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t m = 0; m < 8; ++m) xs[t][m] = v[m] * fwd[m];
+    __syncthreads();
+    // A fragments: entry q = (j, lane) for q = t and t + 256.
+#pragma unroll
+    for (uint32_t h = 0; h < 2; ++h) {
+        const uint32_t q = t + 256u * h, j = q >> 6, l = q & 63u, r = l & 15u, m = r & 7u, G = l >> 4, p = j >> 1;
+        const uint32_t e0 = 128u * (G >> 1) + 32u * p + 16u * (G & 1u) + 8u * (j & 1u);
+        const float c = p == 0 ? 1.0f : (p == 2 ? 0.0625f : 0.25f);
+        f16x8 f;
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i) {
+            _Float16 h1, h2;
+            f16_pieces(xs[e0 + i][m] * c, &h1, &h2);
+            f[i] = r < 8 ? h1 : h2;
+        }
+        reinterpret_cast<f16x8 *>(rec)[q] = f;
+    }
+    if (t < 64) {
+        const uint32_t r = t & 15u, m = r & 7u, G = t >> 4;
+        f16x4 f;
+#pragma unroll
+        for (uint32_t i = 0; i < 4; ++i) {
+            _Float16 h1, h2;
+            f16_pieces(sub[4u * G + i][m] * fwd[m] * 0.03125f, &h1, &h2);  // |sum| < 2^18: scaled by 2^-5 into f16 range
+            f[i] = r < 8 ? h1 : h2;
+        }
+        reinterpret_cast<f16x4 *>(rec + kMvMinsOff)[t] = f;
+    }
+}
+
+// Which blocks and tiles a wavefront of k_gemv_mfma takes (set by the host):
+// with nb = K / 256 >= 16 every wavefront takes blocks wave, wave + 16, ...
+// of all tiles (kAll); otherwise wavefront w < nb * (16 / nb) takes block
+// w % nb of the tiles t with t % (16 / nb) == w / nb.
+struct MvPlan {
+    uint32_t wpb, active;
 };
 
-template <int M>
-__global__ __launch_bounds__(512) void k_gemv_rows(const float *__restrict__ x, const uint8_t *__restrict__ w,
-                                                   float *__restrict__ y, uint32_t N, uint32_t K, uint32_t rows_per_wg,
-                                                   GemvBatch bt) {
-    constexpr int R = GemvRowsCfg<M>::kR, V = GemvRowsCfg<M>::kV;
-    x += blockIdx.y * bt.x_elems;
+// grid (ceil(N / (16 kMvTiles)), problems); 1024 threads = 16 wavefronts. Each
+// keeps its block's A fragments in registers for all its tiles; per tile the
+// wavefronts' partial sums (both pieces) meet in LDS and are added in
+// wavefront order, piece 1 before piece 2.
+template <bool kAll>
+__global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ w, float *__restrict__ y,
+                                                   const uint8_t *__restrict__ ws, uint32_t M, uint32_t N, uint32_t K,
+                                                   GemvBatch bt, MvPlan plan) {
+    __shared__ float red[kMvWaves][kMvTiles][256];
     w += blockIdx.y * bt.w_bytes;
     y += blockIdx.y * bt.y_elems;
-    __shared__ float red[2][4][V][kWave];
-    __shared__ float tot[kGemvMaxBatches][V];
-    const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1);
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const uint32_t par = wave >> 2, wq = wave & 3u;  // batch parity, block group
-    const uint32_t bq = lane >> 4, h = (lane >> 3) & 1u, sg = (lane >> 2) & 1u, p = lane & 3u;
     const uint32_t nb = K >> 8, row_bytes = nb * kBlockBytes;
-    const uint32_t row0 = blockIdx.x * rows_per_wg;
-    const uint32_t nrows = min(rows_per_wg, N - row0);
-    const uint32_t batches = (nrows + R - 1) / R, pairs = (batches + 1) / 2;
-
-    // One descriptor over the workgroup's rows; rows past the end re-read the
-    // last row (never stored). The host keeps rows_per_wg * row_bytes below 2^31.
+    const uint8_t *prep = ws + static_cast<uint64_t>(blockIdx.y) * nb * kMvPrepBytes;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t col = lane & 15u, G = lane >> 4;
+    const uint32_t row0 = blockIdx.x * (16u * kMvTiles);
+    const uint32_t nrows = min(16u * kMvTiles, N - row0);
+    // Rows past N lie beyond the descriptor and read as zeros (their sums are never stored).
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(w + static_cast<uint64_t>(row0) * row_bytes, nrows * row_bytes);
-    __amdgpu_buffer_rsrc_t xr[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) xr[m] = buffer_rsrc(x + static_cast<uint64_t>(m) * K, K * 4u);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-    // Output (batch 2 i + par, value v) is finished by thread 256 par + 4 v + q;
-    // the thread with q = 0 keeps the running total over K chunks in tot.
-    const uint32_t ot = tid & 255u, ov = ot >> 2, oq = ot & 3u;
+    f32x4 acc[kMvTiles];
+#pragma unroll
+    for (uint32_t t = 0; t < kMvTiles; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (uint32_t kb0 = 0; kb0 < nb; kb0 += 16) {
-        const uint32_t kb = kb0 + 4 * wq + bq;
-        // Lanes past the end of K read zeros (activations beyond K, weights
-        // beyond the descriptor) and add nothing.
-        const uint32_t boff = kb < nb ? kb * kBlockBytes : 0x80000000u;
-        const uint32_t xoff = kb < nb ? 4u * (kb * 256u + 128u * h + 32u * p + 16u * sg) : 0x80000000u;
-        float xv[M][16], xs[M];
+    const bool active = kAll || wave < plan.active;
+    const uint32_t tl = kAll ? 0u : wave / nb;
+    const uint32_t b_first = kAll ? wave : wave % nb, b_step = kAll ? kMvWaves : nb;
+    for (uint32_t b = b_first; active && b < nb; b += b_step) {
+        const uint8_t *rec = prep + static_cast<uint64_t>(b) * kMvPrepBytes;
+        f16x8 af[8];
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
+        for (uint32_t j = 0; j < 8; ++j) af[j] = reinterpret_cast<const f16x8 *>(rec)[j * 64u + lane];
+        const f16x4 am = reinterpret_cast<const f16x4 *>(rec + kMvMinsOff)[lane];
+        const f32x4 isc = reinterpret_cast<const f32x4 *>(rec + kMvScaleOff)[G & 1u];
+        // Every tile's bytes of this block are requested before any arithmetic.
+        u32x4 qv[kMvTiles];
+        u32x2 scv[kMvTiles];
+        uint32_t mnv[kMvTiles], ddv[kMvTiles];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr[m], xoff + 16u * i, 0, 0);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const uint32_t e = v[c];
-                    xv[m][4 * i + c] = __builtin_bit_cast(float, e);
-                }
-            }
-            float t = xv[m][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) t += xv[m][i];
-            xs[m] = t;
+        for (uint32_t t = 0; t < kMvTiles; ++t) {
+            const uint32_t off = (16u * t + col) * row_bytes + b * kBlockBytes;
+            qv[t] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16u + 16u * G, 0, 0);
+            scv[t] = __builtin_amdgcn_raw_buffer_load_b64(wr, off + 8u * (G >> 1), 0, 0);
+            mnv[t] = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 4u * G, 0, 0);
+            ddv[t] = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 80u, 0, 0);
         }
-
-        // Per row: the lane's dword of the segment's code bytes, the dword
-        // holding its scale byte, and the block's d, dmin.
-        struct RowLoads {
-            uint32_t q, sc, dd;
-        };
-        auto load_row = [&](uint32_t r) {
-            const uint32_t off = min(r, nrows - 1) * row_bytes + boff;
-            RowLoads t;
-            t.q = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 16u + 32u * h + 16u * sg + 4u * p, 0, 0);
-            t.sc = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 8u * h + 4u * (p >> 1), 0, 0);
-            t.dd = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 80u, 0, 0);
-            return t;
-        };
-        RowLoads cur[R], nxt[R];
+        // Keep every load above the arithmetic: sunk next to its use, each A
+        // fragment load would wait out a full memory latency on its own.
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < R; ++r) cur[r] = load_row(par * R + r);
-
-        for (uint32_t i = 0; i < pairs; ++i) {
-            const uint32_t g = 2 * i + par;
+        for (uint32_t t = 0; t < kMvTiles; ++t) {
+            if (!kAll && t % plan.wpb != tl) continue;
+            uint32_t u[8];
 #pragma unroll
-            for (int r = 0; r < R; ++r) nxt[r] = load_row((g + 2) * R + r);
-            float part[R][M];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t qd[4] = {dpp_u32<kDppQuadBcast0>(cur[r].q), dpp_u32<kDppQuadBcast1>(cur[r].q),
-                                        dpp_u32<kDppQuadBcast2>(cur[r].q), dpp_u32<kDppQuadBcast3>(cur[r].q)};
-                float q[16];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) codes4(qd[j], 2 * p, q + 4 * j);
-                // scale byte 8h + 2p + s is byte 2 (p % 2) + s of the dword loaded
-                const uint32_t sbyte = (cur[r].sc >> (8u * (2u * (p & 1u) + sg))) & 0xffu;
-                const float dl = f16_low(cur[r].dd) * static_cast<float>(sbyte & 15u) * kCodeScale;
-                const float ml = f16_high(cur[r].dd) * static_cast<float>(sbyte >> 4);
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    float t = q[0] * xv[m][0];
-#pragma unroll
-                    for (int k = 1; k < 16; ++k) t = __builtin_fmaf(q[k], xv[m][k], t);
-                    part[r][m] = __builtin_fmaf(dl, t, -(ml * xs[m]));
-                }
+            for (uint32_t i = 0; i < 4; ++i) {
+                u[2 * i] = __builtin_amdgcn_perm(0u, qv[t][i], 0x0c010c00u);      // bytes 0, 1 -> 16-bit slots
+                u[2 * i + 1] = __builtin_amdgcn_perm(0u, qv[t][i], 0x0c030c02u);  // bytes 2, 3
             }
-            // Sum each batch over its four wavefronts: lanes 16 q .. 16 q + 15 of
-            // every wavefront by thread 4 v + q, in order, then the four q by DPP.
+            const uint32_t sh = 8u * (G & 1u);
+            const uint32_t sc[4] = {(scv[t][0] >> sh) & 15u, (scv[t][0] >> (sh + 16u)) & 15u,
+                                    (scv[t][1] >> sh) & 15u, (scv[t][1] >> (sh + 16u)) & 15u};
+            f32x4 d1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int r = 0; r < R; ++r)
+            for (uint32_t j = 0; j < 8; ++j) {
+                const uint32_t p = j >> 1, jj = j & 1u;
+                const uint32_t mask = p == 0 ? 0x00030003u : (p == 2 ? 0x00300030u : 0x000C000Cu);
+                u32x4 bv;
 #pragma unroll
-                for (int m = 0; m < M; ++m) red[par][wq][r * M + m][lane] = part[r][m];
-            __syncthreads();
-            float s = 0.0f;
-            if (ov < static_cast<uint32_t>(V)) {
-#pragma unroll
-                for (int wv = 0; wv < 4; ++wv) {
-                    const float4 *src = reinterpret_cast<const float4 *>(&red[par][wv][ov][16u * oq]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float4 a = src[j];
-                        s += a.x;
-                        s += a.y;
-                        s += a.z;
-                        s += a.w;
-                    }
+                for (uint32_t i = 0; i < 4; ++i) {
+                    const uint32_t vv = p == 3 ? u[4 * jj + i] >> 4 : u[4 * jj + i];
+                    bv[i] = __umul24(vv & mask, sc[p]);
                 }
+                d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[j], __builtin_bit_cast(f16x8, bv), d1, 0, 0, 0);
             }
-            s += dpp<kDppQuadXor1>(s);
-            s += dpp<kDppQuadXor2>(s);
-            if (oq == 0 && ov < static_cast<uint32_t>(V) && g < batches)
-                tot[g][ov] = (kb0 == 0 ? 0.0f : tot[g][ov]) + s;
-            __syncthreads();
+            u32x2 bm;
+            bm[0] = (__builtin_amdgcn_perm(0u, mnv[t], 0x0c010c00u) >> 4) & 0x000F000Fu;
+            bm[1] = (__builtin_amdgcn_perm(0u, mnv[t], 0x0c030c02u) >> 4) & 0x000F000Fu;
+            const f32x4 d2 = __builtin_amdgcn_mfma_f32_16x16x16f16(am, __builtin_bit_cast(f16x4, bm),
+                                                                  f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            const float dl = f16_low(ddv[t]) * 16777216.0f;     // d * 2^24
+            const float ml = f16_high(ddv[t]) * 536870912.0f;   // dmin * 2^24 * 2^5
 #pragma unroll
-            for (int r = 0; r < R; ++r) cur[r] = nxt[r];
+            for (uint32_t v = 0; v < 4; ++v)
+                acc[t][v] = __builtin_fmaf(isc[v], __builtin_fmaf(-ml, d2[v], dl * d1[v]), acc[t][v]);
         }
     }
 
-    if (oq == 0 && ov < static_cast<uint32_t>(V)) {
-        const uint32_t r = ov / M, m = ov % M;
-        for (uint32_t g = par; g < batches; g += 2)
-            if (g * R + r < nrows) y[static_cast<uint64_t>(m) * N + row0 + g * R + r] = tot[g][ov];
+    // Lane l holds rows 4 G + v (piece G / 2 of m = 4 (G % 2) + v) of column l % 16.
+#pragma unroll
+    for (uint32_t t = 0; t < kMvTiles; ++t)
+#pragma unroll
+        for (uint32_t v = 0; v < 4; ++v) red[wave][t][(4u * G + v) * 16u + col] = acc[t][v];
+    __syncthreads();
+    if (tid < kMvTiles * 128u) {
+        const uint32_t t = tid >> 7, q = tid & 127u, m = q >> 4, c = q & 15u, n = row0 + 16u * t + c;
+        float s = red[0][t][q] + red[0][t][q + 128u];
+#pragma unroll
+        for (uint32_t wv = 1; wv < kMvWaves; ++wv) s += red[wv][t][q] + red[wv][t][q + 128u];
+        if (m < M && n < N) y[static_cast<uint64_t>(m) * N + n] = s;
     }
 }
 
@@ -867,20 +927,6 @@ hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t 
     return hipGetLastError();
 }
 
-// Rows per workgroup: enough workgroups to cover the 256 CUs once, each
-// sweeping whole batches of rows, at most kGemvMaxBatches of them.
-template <int M>
-hipError_t launch_gemv_rows(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, uint32_t batches,
-                            GemvBatch bt, hipStream_t stream) {
-    constexpr uint32_t R = GemvRowsCfg<M>::kR;
-    uint32_t rows = (N + 255) / 256;
-    rows = (rows + R - 1) / R * R;
-    if (rows > kGemvMaxBatches * R) rows = kGemvMaxBatches * R;
-    const uint32_t blocks = (N + rows - 1) / rows;
-    hipLaunchKernelGGL((k_gemv_rows<M>), dim3(blocks, batches), dim3(512), 0, stream, x, w, y, N, K, rows, bt);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_dequantize(const uint8_t *blocks, uint64_t nblocks, float *out, hipStream_t stream) {
@@ -903,20 +949,33 @@ hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, 
     return hipGetLastError();
 }
 
+uint64_t gemv_workspace_bytes(uint32_t M, uint32_t K, uint32_t batches) {
+    return M <= 2 ? 0 : static_cast<uint64_t>(batches) * (K / kQK) * kMvPrepBytes;
+}
+
 hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
-                       uint32_t batches, hipStream_t stream) {
+                       uint32_t batches, void *ws, hipStream_t stream) {
     if (batches == 0 || batches > kMaxGridY) return hipErrorInvalidValue;
     const GemvBatch bt{static_cast<uint64_t>(M) * K, static_cast<uint64_t>(N) * (K / kQK) * kBlockBytes,
                        static_cast<uint64_t>(M) * N};
     switch (M) {
         case 1: return launch_gemv_seg<1>(x, w, y, N, K, batches, bt, stream);
         case 2: return launch_gemv_seg<2>(x, w, y, N, K, batches, bt, stream);
-        case 3: return launch_gemv_rows<3>(x, w, y, N, K, batches, bt, stream);
-        case 4: return launch_gemv_rows<4>(x, w, y, N, K, batches, bt, stream);
-        case 5: return launch_gemv_rows<5>(x, w, y, N, K, batches, bt, stream);
-        case 6: return launch_gemv_rows<6>(x, w, y, N, K, batches, bt, stream);
-        case 7: return launch_gemv_rows<7>(x, w, y, N, K, batches, bt, stream);
-        case 8: return launch_gemv_rows<8>(x, w, y, N, K, batches, bt, stream);
+        case 3: case 4: case 5: case 6: case 7: case 8: {
+            auto *rec = static_cast<uint8_t *>(ws);
+            const uint32_t nb = K / kQK;
+            hipLaunchKernelGGL(k_mv_prep, dim3(nb, batches), dim3(256), 0, stream, x, rec, M, K, bt.x_elems);
+            const uint32_t wgs = (N + 16 * kMvTiles - 1) / (16 * kMvTiles);
+            if (nb >= kMvWaves) {
+                hipLaunchKernelGGL(k_gemv_mfma<true>, dim3(wgs, batches), dim3(1024), 0, stream, w, y, rec, M, N, K, bt,
+                                   MvPlan{1, kMvWaves});
+            } else {
+                const uint32_t wpb = kMvWaves / nb;
+                hipLaunchKernelGGL(k_gemv_mfma<false>, dim3(wgs, batches), dim3(1024), 0, stream, w, y, rec, M, N, K,
+                                   bt, MvPlan{wpb, nb * wpb});
+            }
+            return hipGetLastError();
+        }
         default: return hipErrorInvalidValue;
     }
 }

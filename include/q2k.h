@@ -87,7 +87,10 @@ q2k_status q2k_dequantize(const void *blocks, size_t blocks_bytes, float *out, s
  *   w  device Q2_K bytes, N * K/256 * 84 long (layout above); 4-byte aligned.
  *   y  device f32 [M, N] row-major; 16-byte aligned.
  *   M, N >= 1; K a multiple of 256 with 256 <= K <= 2^21.
- * M <= 8 runs the fp32 GEMV: |y - exact| <= 1e-5 * sum_k |x*w| per output.
+ * M <= 8 runs the fp32-accurate GEMV: |y - exact| <= 1e-5 * sum_k |x*w| per
+ * output. M <= 2 uses fp32 FMAs; 3 <= M <= 8 uses the matrix cores on exact
+ * f16 encodings of the weights' integer parts and a two-piece f16 split of x
+ * (staging 8736 bytes per 256 columns of K in the workspace below).
  * A row of y depends only on its own row of x: calls with the same M give it
  * bit-identical values whatever the other rows hold (M <= 2 and 3 <= M <= 8
  * run different kernels and may differ in the last bits).
@@ -119,7 +122,9 @@ q2k_status q2k_matmul_path(const float *x, const void *w, float *y, uint32_t M, 
  *   batches, N >= 1; 1 <= M <= 8 (the fp32 mat-vec path); K as for q2k_matmul.
  * Slice b of y is bit-identical to q2k_matmul(x + b*M*K, w + b*N*K/256*84,
  * y + b*M*N, M, N, K), whatever the other slices hold. Asynchronous on
- * `stream`; allocates nothing.
+ * `stream`. For M >= 3 it uses the per-(device, stream) workspace (at most
+ * 64 MiB; larger batches run in several launches); for M <= 2 it allocates
+ * nothing.
  */
 q2k_status q2k_matmul_batched(const float *x, const void *w, float *y, uint32_t batches, uint32_t M, uint32_t N,
                               uint32_t K, void *stream);

@@ -235,6 +235,26 @@ def test_gemv_ragged_shapes(M, N, K):
     check_gemv(y, x, blocks, M, N, K)
 
 
+@pytest.mark.parametrize("M", [3, 8])
+def test_gemv_wide_dynamic_range_activations(M):
+    # 3 <= M <= 8 splits each row of each 256-column block into two f16 pieces
+    # after a power-of-two scale of that row and block: rows far apart in
+    # magnitude, a 1e3 spread inside blocks, zero rows and exact zeros must
+    # all stay within the fp32 rule.
+    rng = np.random.Generator(np.random.PCG64(36 + M))
+    N, K = 300, 1280
+    blocks = synth.random_blocks(rng, N * K // QK_K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x *= np.float32(10.0) ** rng.integers(-3, 4, (M, K)).astype(np.float32)   # 1e3 spread within rows
+    scales = np.array([1e-20, 1.0, 1e20, 0.0, 3e-5, 7e8, 1.0, 2.0 ** -60], np.float32)[:M]
+    x *= scales[:, None]
+    x[0, ::7] = 0.0
+    y = gpu_matmul(x, blocks, M, N, K)
+    zero = scales == 0
+    assert np.all(y[zero] == 0.0)
+    check_gemv(y[~zero], x[~zero], blocks, int((~zero).sum()), N, K)
+
+
 def test_gemv_rows_do_not_depend_on_other_rows():
     # An output row depends only on its own activation row: rows of a call
     # equal the same rows computed in a call of the same kernel variant
