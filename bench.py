@@ -16,6 +16,7 @@ Other modes (used to collect rocprofv3 counters; they print one short JSON line)
   --only ROW         run only one row's timed loop (gemv1, dequant, gather, gemv8, mfma, batched,
                      sample, moe_decode, moe_prefill)
   --copy-probe       also run a device-to-device copy of COPY_BYTES (counter calibration)
+  --sweep            M=1 GEMV over N = 4096 .. 131072 (K = 4096, cold) beside the plain-read ceiling
   --derive-traffic FETCH_CSV WRITE_CSV
                      turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
                      `--only gemv1 --copy-probe` into profiles/traffic.json: HBM bytes
@@ -85,6 +86,50 @@ def time_launches(torch, launch, n: int, warmup: int):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / n * 1e-3  # seconds per launch
+
+
+def time_blocks(torch, launch, blocks: int = 50, per: int = 20, warmup: int = 20):
+    """Spread of the per-call time: `blocks` runs of `per` back-to-back calls, one event between runs (an event
+    before every call would stall the queue on each one); p10, p50, p90 and mean of the run averages, seconds."""
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
+    ev[0].record()
+    for j in range(blocks):
+        for i in range(per):
+            launch(j * per + i)
+        ev[j + 1].record()
+    torch.cuda.synchronize()
+    per_call = sorted(ev[j].elapsed_time(ev[j + 1]) * 1e-3 / per for j in range(blocks))
+    pick = lambda q: per_call[min(blocks - 1, int(q * blocks))]
+    return {"mean": ev[0].elapsed_time(ev[blocks]) * 1e-3 / (blocks * per), "p10": pick(0.10), "p50": pick(0.50),
+            "p90": pick(0.90)}
+
+
+def dist_us(d):
+    return {k: round(v * 1e6, 3) for k, v in d.items()}
+
+
+def time_graph(torch, make_launch, n: int):
+    """Seconds per launch when n launches are captured in one graph and replayed. make_launch(stream) returns a
+    launch function bound to that HIP stream (the capture stream)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            launch = make_launch(torch.cuda.current_stream().cuda_stream)
+            for i in range(n):
+                launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) * 1e-3 / n
 
 
 def cpu_baseline(inp, budget_s: float):
@@ -174,14 +219,28 @@ class Bench:
                        y=self.torch.empty((c.M, c.N), dtype=self.torch.float32, device=self.dev),
                        bytes=inp.blocks.size + c.M * c.K * 4 + c.M * c.N * 4)
         lib = self.q2k.load_library()
-        g, st = self.g1, self.stream
+        g = self.g1
 
-        def step(i):
-            rc = lib.q2k_matmul(g["x"].data_ptr(), g["replicas"][i % reps].data_ptr(), g["y"].data_ptr(),
-                                c.M, c.N, c.K, st)
-            if rc:
-                raise RuntimeError(lib.q2k_last_error_message().decode())
-        return step
+        def make_step(st):
+            def step(i):
+                rc = lib.q2k_matmul(g["x"].data_ptr(), g["replicas"][i % reps].data_ptr(), g["y"].data_ptr(),
+                                    c.M, c.N, c.K, st)
+                if rc:
+                    raise RuntimeError(lib.q2k_last_error_message().decode())
+            return step
+        g["make_step"] = make_step
+        return make_step(self.stream)
+
+    def read_ceiling(self, replicas, n=200):
+        """Plain streaming read of the same cold replicas (q2k_read_probe): the bandwidth a transfer of this size
+        can reach at all."""
+        torch = self.torch
+        sink = torch.empty(self.q2k.READ_PROBE_SINK_WORDS, dtype=torch.int32, device=self.dev)
+        views = [r[: r.numel() // 16 * 16] for r in replicas]
+        t = time_launches(torch, lambda i: self.q2k.q2k_read_probe(views[i % len(views)], sink, stream=self.stream),
+                          n, 20)
+        b = views[0].numel()
+        return {"bytes": b, "us": t * 1e6, "GB/s": b / t / 1e9}
 
     def dequant(self, n=200):
         g = self.g1
@@ -233,8 +292,8 @@ class Bench:
         log("GEMV M=8: %.2f us, %.1f GB/s, %.2f TFLOP/s" % (t * 1e6, b / t / 1e9, f / t / 1e12))
         return {"workload": "M=8 N=14336 K=4096 (%d cold weight replicas)" % reps, "us": t * 1e6,
                 "algorithmic_bytes": b, "flop": f, "GB/s": b / t / 1e9, "TFLOP/s": f / t / 1e12,
-                "bound": "alu", "frac_fp32": f / t / 1e12 / FP32_PEAK_TFLOPS,
-                "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
+                "bound": "hbm", "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
+                "frac_fp32": f / t / 1e12 / FP32_PEAK_TFLOPS, "read_ceiling": self.read_ceiling(wr)}
 
     def mfma(self, n=50):
         torch = self.torch
@@ -268,7 +327,7 @@ class Bench:
         log("batched mat-vec 8 x (M=1, N=K=4096): %.2f us, %.1f GB/s" % (t * 1e6, b / t / 1e9))
         return {"workload": "8 matrices x (M=1, N=K=4096) in one call, %d cold weight replicas" % reps,
                 "us": t * 1e6, "algorithmic_bytes": b, "GB/s": b / t / 1e9, "bound": "hbm",
-                "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
+                "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS, "read_ceiling": self.read_ceiling(wr)}
 
     def sample(self, n=200):
         """First-max argmax + threshold candidates over 8 slots x 262144 logits (cap 64)."""
@@ -350,6 +409,8 @@ def main() -> int:
     ap.add_argument("--only", choices=ROWS, help="run only this row's timed loop")
     ap.add_argument("--copy-probe", action="store_true", help="also run the calibration copy")
     ap.add_argument("--derive-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--sweep", action="store_true",
+                    help="M=1, K=4096 GEMV and read ceiling over N = 4096 .. 131072 (cold), one JSON line per N")
     args = ap.parse_args()
 
     if args.derive_traffic:
@@ -368,6 +429,31 @@ def main() -> int:
 
     q2k.load_library()
     b = Bench(torch, q2k, synth, np)
+
+    if args.sweep:
+        lib = q2k.load_library()
+        for N in (4096, 8192, 16384, 32768, 65536, 131072):
+            K = 4096
+            rng = np.random.Generator(np.random.PCG64(5000 + N))
+            blocks = synth.random_blocks(rng, N * K // 256)
+            reps = max(1, math.ceil(COLD_BYTES / blocks.size))
+            wh = torch.from_numpy(blocks)
+            wr = [wh.to(b.dev) for _ in range(reps)]
+            x = torch.from_numpy(rng.standard_normal((1, K), dtype=np.float32)).to(b.dev)
+            y = torch.empty((1, N), dtype=torch.float32, device=b.dev)
+            st = b.stream
+
+            def step(i):
+                rc = lib.q2k_matmul(x.data_ptr(), wr[i % reps].data_ptr(), y.data_ptr(), 1, N, K, st)
+                if rc:
+                    raise RuntimeError(lib.q2k_last_error_message().decode())
+            d = time_blocks(torch, step, 30, 20)
+            byt = blocks.size + 4 * K + 4 * N
+            print(json.dumps({"sweep": "gemv_m1", "N": N, "K": K, "weight_replicas": reps, "bytes": byt,
+                              "us": dist_us(d), "GB/s": byt / d["mean"] / 1e9,
+                              "read_ceiling": b.read_ceiling(wr, 300)}), flush=True)
+            del wr
+        return 0
 
     if args.only:
         out = {"only": args.only}
@@ -404,6 +490,12 @@ def main() -> int:
     sec_per_step = t_start.elapsed_time(t_end) * 1e-3 / args.steps
     gbs = g["bytes"] / sec_per_step / 1e9
     log("GEMV M=1: %.3f us/step, %.1f GB/s" % (sec_per_step * 1e6, gbs))
+    # Per-call spread (runs of 20 calls) and graph replay of the same launches, after the timed region.
+    dist = time_blocks(torch, step, 50, 20)
+    graph_s = time_graph(torch, g["make_step"], min(args.steps, 500))
+    ceiling = b.read_ceiling(g["replicas"])
+    log("GEMV M=1 per call p10/p50/p90 %.2f/%.2f/%.2f us, graph %.2f us; read ceiling %.2f us (%.0f GB/s)" % (
+        dist["p10"] * 1e6, dist["p50"] * 1e6, dist["p90"] * 1e6, graph_s * 1e6, ceiling["us"], ceiling["GB/s"]))
 
     rows = {}
     if not args.no_rows:
@@ -439,6 +531,8 @@ def main() -> int:
                    "algorithmic_bytes_per_step": g["bytes"], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("k_gemv_m1")},
+        "step_us": dict(dist_us(dist), graph_replay=round(graph_s * 1e6, 3)),
+        "read_ceiling": ceiling,
         "cpu_baseline": {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
                          "sample": "the whole decode GEMV workload (M=1, N=K=4096), %d calls of the f64 "
                                    "oracle matmul, %.4f s per call" % (cpu_reps, sec_cpu)},

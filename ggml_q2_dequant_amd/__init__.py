@@ -66,6 +66,7 @@ EXPORTS = (
     "q2k_matmul_id_pooled",
     "q2k_matmul_id_pooled_pair",
     "q2k_matmul_id_pooled_slotted",
+    "q2k_read_probe",
     "q2k_gguf_open",
     "q2k_gguf_close",
     "q2k_gguf_tensor_count",
@@ -139,6 +140,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).restype = ctypes.c_int
     lib.q2k_argmax_candidates.argtypes = [P, U32, U32, U32, P, P, P, P, P, P]
     lib.q2k_argmax_candidates.restype = ctypes.c_int
+    lib.q2k_read_probe.argtypes = [P, SZ, P, SZ, P]
+    lib.q2k_read_probe.restype = ctypes.c_int
     PP = ctypes.POINTER(MatmulIdParams)
     lib.q2k_matmul_id.argtypes = [P, P, P, P, PP, P, P]
     lib.q2k_matmul_id_path.argtypes = [P, P, P, P, PP, P, ctypes.c_int, P]
@@ -288,6 +291,14 @@ def q2k_matmul_id_pooled_slotted(x, w, ids, y, params, scratch, status=None, str
     nb = _nbytes(scratch) if scratch_bytes is None else int(scratch_bytes)
     _check(load_library().q2k_matmul_id_pooled_slotted(_ptr(x), _ptr(w), _ptr(ids), _ptr(y), ctypes.byref(p),
                                                        _ptr(scratch), nb, _ptr(status), _stream(stream)))
+
+
+READ_PROBE_SINK_WORDS = 2048
+
+
+def q2k_read_probe(data, sink, stream=None) -> None:
+    """Measurement aid: read ``data`` (a device tensor, 16-byte multiple) once; one word per workgroup to sink."""
+    _check(load_library().q2k_read_probe(_ptr(data), _nbytes(data), _ptr(sink), sink.numel(), _stream(stream)))
 
 
 class GGUFFile:

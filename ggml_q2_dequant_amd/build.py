@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libq2k.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("q2k_kernels.hip", "q2k_sample.hip", "q2k_moe.hip", "q2k_api.cpp", "q2k_gguf.cpp")]
+SOURCES = [os.path.join(CSRC, n) for n in ("q2k_kernels.hip", "q2k_sample.hip", "q2k_moe.hip", "q2k_probe.hip", "q2k_api.cpp", "q2k_gguf.cpp")]
 ARCH = os.environ.get("Q2K_OFFLOAD_ARCH", "gfx950")
 
 # -ffp-contract=off: only FMAs written as such are fused, so every kernel's

@@ -488,6 +488,22 @@ q2k_status q2k_matmul_id_pooled_slotted(const float *x, const void *w, const uin
     return run_moe_mfma(fn, sh, p, w, nullptr, y, nullptr, scratch, status, static_cast<hipStream_t>(stream));
 }
 
+q2k_status q2k_read_probe(const void *data, size_t bytes, uint32_t *sink, size_t sink_elems, void *stream) {
+    if (!data || !sink) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_read_probe: null pointer");
+    if (bytes == 0 || bytes % 16 != 0)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_read_probe: %zu bytes is not a positive multiple of 16", bytes);
+    if (sink_elems < q2k::kReadProbeMaxGrid)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_read_probe: sink holds %zu words, %u needed", sink_elems,
+                    q2k::kReadProbeMaxGrid);
+    if (!aligned(data, 16) || !aligned(sink, 4))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_read_probe: data must be 16-byte aligned, sink 4-byte aligned");
+    if (overlap(sink, 4ull * sink_elems, data, bytes))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_read_probe: sink overlaps data");
+    hipError_t e = q2k::launch_read_probe(data, bytes, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_error("q2k_read_probe launch", e);
+    return ok();
+}
+
 q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *out, uint32_t vocab,
                                 uint32_t embed_dim, uint32_t n_tokens, void *stream) {
     if (!table || !ids || !out) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_embedding_gather: null pointer");

@@ -308,6 +308,17 @@ q2k_status q2k_gguf_tensor_info(const q2k_gguf *f, const char *name, q2k_gguf_in
  * hipMemcpy); fails if the type's size is unknown. */
 q2k_status q2k_gguf_tensor_data(const q2k_gguf *f, const char *name, const void **data, uint64_t *byte_len);
 
+/*
+ * q2k_read_probe — measurement aid, not part of the Q2_K path: reads `bytes`
+ * of device memory once with the grid shape of the decode GEMV and stores
+ * one XOR word per workgroup in `sink`, so a benchmark can time the plain
+ * streaming-read ceiling for a transfer of a given size.
+ *   data        device memory, 16-byte aligned; bytes a positive multiple of 16.
+ *   sink        device u32 [sink_elems], sink_elems >= 2048; not overlapping data.
+ * Asynchronous on `stream`; allocates nothing.
+ */
+q2k_status q2k_read_probe(const void *data, size_t bytes, uint32_t *sink, size_t sink_elems, void *stream);
+
 /* Static English name of a status code ("Q2K_OK", ...). Never NULL. */
 const char *q2k_status_string(q2k_status s);
 

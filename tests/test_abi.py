@@ -221,6 +221,15 @@ def test_matmul_id_pair_rejects_overlapping_outputs(lib):
     _err(lib, pair(A, B, B, C, D, None, ctypes.byref(p), F, need, None, None), "null")
 
 
+def test_read_probe_rejects_bad_arguments(lib):
+    _err(lib, lib.q2k_read_probe(None, 64, B, 2048, None), "null")
+    _err(lib, lib.q2k_read_probe(A, 0, B, 2048, None), "multiple of 16")
+    _err(lib, lib.q2k_read_probe(A, 20, B, 2048, None), "multiple of 16")
+    _err(lib, lib.q2k_read_probe(A, 64, B, 2047, None), "2048 needed")
+    _err(lib, lib.q2k_read_probe(A + 8, 64, B, 2048, None), "aligned")
+    _err(lib, lib.q2k_read_probe(A, 1 << 20, A + 4096, 2048, None), "overlaps")
+
+
 def test_python_binding_raises_typed_errors(lib):
     with pytest.raises(q2k.Q2KInvalidArgument, match="multiple of 256"):
         q2k.q2k_matmul(A, B, C, 1, 8, 100, stream=0)

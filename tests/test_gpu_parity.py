@@ -222,7 +222,8 @@ def test_gemv_configs(cfg):
     inp = inputs(cfg)
     c = inp.config
     y = gpu_matmul(inp.x, inp.blocks, c.M, c.N, c.K)
-    check_gemv(y, inp.x, inp.blocks, c.M, c.N, c.K)
+    worst = check_gemv(y, inp.x, inp.blocks, c.M, c.N, c.K)
+    print("parity cfg%d (%s): max |y - y_ref| / A = %.3g" % (cfg, c.name, worst))
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (3, 7, 768), (8, 130, 1280), (5, 4097, 256), (2, 9, 4352),
@@ -391,7 +392,8 @@ def test_mfma_config4_full_size_sampled():
     ns = np.unique(np.concatenate([[0, 1, 127, 128, 7167, 7168, 14334, 14335], rng.integers(0, c.N, 40)]))
     x_s = inp.x[ms]
     w_s = synth.rows_of(inp.blocks, c.K, ns)
-    check_mfma(y[np.ix_(ms, ns)], x_s, w_s, len(ms), len(ns), c.K)
+    worst = check_mfma(y[np.ix_(ms, ns)], x_s, w_s, len(ms), len(ns), c.K)
+    print("parity cfg4 (%s, %d x %d sampled outputs): max |y - y_ref| / A = %.3g" % (c.name, len(ms), len(ns), worst))
 
 
 def test_mfma_one_hot_returns_bf16_weights_bitwise():
@@ -440,3 +442,17 @@ def test_mfma_is_deterministic():
     blocks = synth.random_blocks(rng, N * K // QK_K)
     x = rng.standard_normal((M, K), dtype=np.float32)
     assert bits_equal(gpu_matmul(x, blocks, M, N, K), gpu_matmul(x, blocks, M, N, K))
+
+
+# ----------------------------------------------------------------- measurement aid
+
+def test_read_probe_reads_every_word():
+    # q2k_read_probe stores one XOR word per workgroup; their XOR is the XOR of all data words.
+    rng = np.random.Generator(np.random.PCG64(44))
+    for nbytes in (16, 4096 + 16, 5 * 1024 * 1024 + 48):
+        data = rng.integers(0, 2 ** 32, nbytes // 4, dtype=np.uint32)
+        sink = torch.zeros(q2k.READ_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda:0")
+        q2k.q2k_read_probe(dev(data.view(np.int32)), sink)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(data)
