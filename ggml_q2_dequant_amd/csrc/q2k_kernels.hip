@@ -582,14 +582,14 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
 //
 // k_x_to_bf16 rounds the activations to bf16 (nearest even) once, into a
 // workspace. k_gemm_q2k then computes a 128 (M) x 256 (N) tile of y per
-// 256-thread workgroup. Wavefront w owns columns 64w .. 64w+63 of the tile for
-// all 128 rows, as a 4 x 2 grid of v_mfma_f32_32x32x16_bf16 accumulators.
-// K advances 64 weights per step (a quarter super-block). The activation tile
-// (128 x 64 bf16) is staged through double-buffered LDS and shared by the four
-// wavefronts; the weights never touch LDS: each wavefront decodes its own 64
-// columns straight into MFMA B fragments, one step ahead of the MFMAs that
-// use them, so the decode arithmetic overlaps the matrix cores and LDS carries
-// only activations. One workgroup barrier per step.
+// 512-thread workgroup: two groups of four wavefronts split K in halves, and
+// wavefront w of a group owns columns 64w .. 64w+63 of the tile for all 128
+// rows, as a 4 x 2 grid of v_mfma_f32_32x32x16_bf16 accumulators. K advances
+// 64 weights per step (a quarter super-block). Activation tiles (128 x 64
+// bf16) and each wavefront's raw weight blocks reach LDS through direct
+// buffer-to-LDS loads; each wavefront decodes its own 64 columns from LDS into
+// MFMA B fragments one slice ahead of the MFMAs that use them, so the decode
+// arithmetic overlaps the matrix cores. One workgroup barrier per step.
 //
 // Inside a step the 64 k are taken in an order that suits the code bytes: the
 // k-chunk of 8 that MFMA slice kk gives to lane half kh (lanes 32kh .. 32kh+31)
@@ -673,28 +673,53 @@ struct GemmRoute {
 };
 static_assert(kGM == kMoeTileRows, "routing tiles must match the GEMM's M tile");
 
+// Wait until at most N vector-memory operations of this wavefront are still in
+// flight, then meet the rest of the workgroup (gfx9 s_waitcnt: vmcnt in bits
+// 3:0 and 15:14, expcnt and lgkmcnt left at their "no wait" maxima). The
+// barrier is a compiler memory barrier too, so no LDS access moves across it.
+template <uint32_t N>
+__device__ __forceinline__ void vm_barrier() {
+    static_assert(N < 64, "vmcnt has six bits");
+    __builtin_amdgcn_s_waitcnt(static_cast<int>((N & 15u) | ((N >> 4) << 14) | 0x0F70u));
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Weight staging in LDS (per group and block): wavefront wq's 64 columns fill
+// 22 runs of 65 dwords. Run j holds columns 3 j, 3 j + 1, 3 j + 2 of the
+// wavefront as 21 dwords each (the whole 84-byte block) and one pad dword;
+// run 21 holds only column 63 (its other slots are filled and never read).
+// The 65-dword run stride spreads the columns a fragment reads over the banks.
+constexpr uint32_t kWRun = 65, kWRuns = 22;
+constexpr uint32_t kWWave = kWRun * kWRuns;  // dwords per wavefront and block
+constexpr uint32_t kWGroup = 4 * kWWave;     // dwords per group and block
+
 template <bool kRouted>
 __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb, const uint8_t *__restrict__ w,
                                                   float *__restrict__ y, uint32_t M, uint32_t N, uint32_t K,
                                                   uint32_t tiles_m, GemmRoute rg) {
     // Eight wavefronts, two per SIMD: group g = wave / 4 runs the MFMAs of K
-    // half g for the whole 128 x 256 tile (wavefront wave % 4 owns columns
-    // 64 (wave % 4) .. +63), so while one wavefront of a SIMD waits on a
-    // barrier, LDS or memory, the other keeps the matrix core busy. Each group
-    // has two activation buffers of 128 x 64 bf16 (rows padded to 72); at the
-    // end the same memory carries the partial sums the groups exchange.
+    // half g (blocks g nblk .. g nblk + nblk - 1) for the whole 128 x 256 tile;
+    // wavefront wave % 4 owns columns 64 (wave % 4) .. +63.
+    //
+    // Both operands reach LDS by direct buffer-to-LDS loads (the LDS bit of a
+    // buffer load: no registers on the way). Activations: two stage buffers
+    // per group of 128 rows x 64 bf16 (16 KiB), one 64-k step ahead. Weights:
+    // two block buffers per group, whole 84-byte blocks copied as contiguous
+    // dwords, one block ahead. Copying whole blocks keeps each load
+    // instruction on a few cache lines; a wavefront fetching its fragments'
+    // bytes straight from memory touches 32 rows per instruction, and the
+    // per-line cost of that dominated the kernel. At the end the same memory
+    // carries the partial sums the groups exchange.
     constexpr uint32_t kStepK = 64;
-    constexpr uint32_t kLd = kStepK + 8;
-    constexpr uint32_t kBuf = kGM * kLd;
-    constexpr uint32_t kXBytes = 2 * 2 * kBuf * 2;
-    constexpr uint32_t kSwapBytes = 8 * 64 * 64 * 4;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kXBytes > kSwapBytes ? kXBytes : kSwapBytes];
-    __bf16 *xs = reinterpret_cast<__bf16 *>(smem);
+    constexpr uint32_t kTile = kGM * kStepK;  // bf16 per group and stage
+    __shared__ __attribute__((aligned(16))) __bf16 xs0[2 * kTile], xs1[2 * kTile];
+    __shared__ __attribute__((aligned(16))) uint32_t ws0[2 * kWGroup], ws1[2 * kWGroup];
+    static_assert(2 * kTile * 2 == 2 * 64 * 64 * 4 && 2 * kWGroup * 4 >= 2 * 64 * 64 * 4,
+                  "the partial-sum exchange needs 16 KiB per wavefront");
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const uint32_t grp = wave >> 2, wq = wave & 3u;
-    const uint32_t gtid = tid & 255u;
     const uint32_t kh = lane >> 5, col = lane & 31u;
     uint32_t tm, tn;
     gemm_tile(blockIdx.x, tiles_m, (N + kGN - 1) / kGN, &tm, &tn);
@@ -718,47 +743,70 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
         xt = xb + static_cast<uint64_t>(m0) * K;
         wt = w;
     }
-    // Group g takes half-blocks [g nb, (g + 1) nb): 2 nb steps of 64 k each.
-    const uint32_t hb0 = grp * nb, s0 = 2 * hb0, steps = 2 * nb;
+    // Group g takes blocks kb0 .. kb0 + nblk - 1. With an odd block count the
+    // last block of group 1 does not exist; that group then only meets the
+    // barriers of its last block.
+    const uint32_t nblk = (nb + 1) >> 1, kb0 = grp * nblk;
 
     // Rows past M or N lie beyond these descriptors and load as zeros.
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(xt, rows * K * 2u);
     const __amdgpu_buffer_rsrc_t wr =
         buffer_rsrc(wt + static_cast<uint64_t>(n0) * row_bytes, min(kGN, N - n0) * row_bytes);
 
-    // Activation staging: chunk c = gtid + 256 i (i < 4) of the group's 128 x 64
-    // tile is row c / 8, bf16 columns 8 (c % 8) .. +7; step s adds 128 bytes.
-    const uint32_t xg = ((gtid >> 3) * K + 8u * (gtid & 7u)) * 2u;  // + i * 32 rows
-    const uint32_t xl = grp * 2 * kBuf + (gtid >> 3) * kLd + 8u * (gtid & 7u);
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 xq[4];
-    auto load_x = [&](uint32_t step) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            xq[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xg + i * 32u * K * 2u + step * 128u, 0, 0);
-    };
-    auto store_x = [&](uint32_t buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4 *>(&xs[buf * kBuf + xl + i * 32u * kLd]) = xq[i];
+    // Activation loads: instruction i of wavefront wq fills the 64 16-byte
+    // slots 64 (4 wq + i) + lane of the group's stage tile, i.e. tile row
+    // r = 32 wq + 8 i + lane / 8, stored chunk lane % 8, which receives
+    // activation chunk (lane % 8) ^ ((r / 2) % 8) of the step (8 bf16). Rows
+    // are 128 B with no padding. A fragment read serves 16 lanes (16
+    // consecutive rows, one chunk each) per pass over the 64 banks; the XOR
+    // key (r / 2) % 8 gives the 8 even and the 8 odd rows 8 different chunk
+    // slots, so the 16 reads hit 16 different 4-bank groups. The whole offset
+    // goes in the lane offset, which the descriptor's range check covers.
+    const uint32_t xrow = (32u * wq + (lane >> 3)) * K * 2u;
+    const uint32_t xv0 = xrow + 16u * ((lane & 7u) ^ (lane >> 4));       // even i: key lane / 16
+    const uint32_t xv1 = xrow + 16u * ((lane & 7u) ^ (4u + (lane >> 4)));  // odd i: key 4 + lane / 16
+    // Step s of the group is K step 4 kb0 + s (64 k each).
+    auto dma_x = [&](__bf16 *stage, uint32_t s, uint32_t i) __attribute__((always_inline)) {
+        __bf16 *dst = stage + grp * kTile + 4u * wq * 512u + 512u * i;
+        // The uniform part is summed in scalar registers first, so that the
+        // per-instruction lane offsets are not hoisted out of the loop.
+        const uint32_t u = __builtin_amdgcn_readfirstlane(i * 8u * K * 2u + (4u * kb0 + s) * 128u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void *)dst, 16,
+                                                 static_cast<int>((i & 1u ? xv1 : xv0) + u), 0, 0, 0);
     };
 
-    uint32_t wrow[2];
+    // Weight loads, one dword per lane: in run j, lane l takes dword l % 21
+    // of column 3 j + l / 21 (lane 63 repeats lane 62's dword into the pad).
+    const uint32_t wl = lane == 63u ? 62u : lane;
+    const uint32_t wv = (64u * wq + wl / 21u) * row_bytes + 4u * (wl % 21u);
+    auto dma_w = [&](uint32_t *buf, uint32_t kb, uint32_t j) __attribute__((always_inline)) {
+        uint32_t *dst = buf + grp * kWGroup + wq * kWWave + kWRun * j;
+        const uint32_t u = __builtin_amdgcn_readfirstlane(3u * j * row_bytes + kb * kBlockBytes);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void *)dst, 4,
+                                                 static_cast<int>(wv + u), 0, 0, 0);
+    };
+
+    // This lane's two columns (32 jj + col of the wavefront) in a block buffer.
+    uint32_t wcol[2];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) wrow[jj] = (64u * wq + 32u * jj + col) * row_bytes;
-    auto load_raw = [&](GemmRaw &r, uint32_t hb) {
-        const uint32_t kb = hb >> 1, h = hb & 1u;
+    for (int jj = 0; jj < 2; ++jj) {
+        const uint32_t c = 32u * jj + col;
+        wcol[jj] = grp * kWGroup + wq * kWWave + kWRun * (c / 3u) + 21u * (c % 3u);
+    }
+    // Half-block h's bytes for both columns: the lane's 16-byte code segment,
+    // the half's 8 scale bytes, d and dmin.
+    auto read_raw = [&](GemmRaw &r, const uint32_t *buf, uint32_t h) __attribute__((always_inline)) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const uint32_t base = wrow[jj] + kb * kBlockBytes;
-            const auto q = __builtin_amdgcn_raw_buffer_load_b128(wr, base + 16u + 32u * h + 16u * kh, 0, 0);
-            const auto sc = __builtin_amdgcn_raw_buffer_load_b64(wr, base + 8u * h, 0, 0);
+            const uint32_t *c = buf + wcol[jj];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r.q[jj][e] = q[e];
-            r.sc[jj][0] = sc[0];
-            r.sc[jj][1] = sc[1];
-            r.dd[jj] = __builtin_amdgcn_raw_buffer_load_b32(wr, base + 80u, 0, 0);
+            for (int e = 0; e < 4; ++e) r.q[jj][e] = c[4u + 8u * h + 4u * kh + e];
+            r.sc[jj][0] = c[2u * h];
+            r.sc[jj][1] = c[2u * h + 1u];
+            r.dd[jj] = c[20];
         }
     };
+
     // B fragments of MFMA slice kk (0..7) of a half-block, both columns: 2-bit
     // position p = kk / 2, code bytes 8 (kk % 2) .. +7 of segment kh. The code
     // bits become floats with the e4m3 trick: masked with 0x03 a byte is
@@ -766,7 +814,7 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
     // 4-bit shift). The power of two is folded into d * sc, so
     // fma(dl, code, -ml) rounds d*sc*q - dmin*mn once, exactly as the decode
     // rule, before the bf16 rounding.
-    auto decode = [&](const GemmRaw &r, int kk, bf16x8 (&b)[2]) {
+    auto decode = [&](const GemmRaw &r, int kk, bf16x8 (&b)[2]) __attribute__((always_inline)) {
         const int p = kk >> 1, ih = kk & 1;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
@@ -799,27 +847,46 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
 
-    // A fragment of slice kq (0..3 within a 64-k step), row block i: row
-    // 32 i + col, 8-element chunk 4 (kq / 2) + 2 kh + kq % 2 of the step.
-    const uint32_t a_lane = grp * 2 * kBuf + col * kLd + 16u * kh;
-    auto read_a = [&](bf16x8 (&a)[4], uint32_t buf, int kq) {
-        const uint32_t off = buf * kBuf + a_lane + 32u * (kq >> 1) + 8u * (kq & 1);
+    // A fragment of slice kq (0..3 within a 64-k step), row block i: tile row
+    // 32 i + col, activation chunk c = 4 (kq / 2) + 2 kh + kq % 2 of the step,
+    // stored as chunk c ^ ((col / 2) % 8) of the row.
+    auto read_a = [&](bf16x8 (&a)[4], const __bf16 *stage, int kq) __attribute__((always_inline)) {
+        const uint32_t c = 4u * static_cast<uint32_t>(kq >> 1) + 2u * kh + static_cast<uint32_t>(kq & 1);
+        const __bf16 *src = stage + grp * kTile + col * kStepK + 8u * (c ^ ((col >> 1) & 7u));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(&xs[off + 32u * kLd * i]);
+        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(src + 32u * kStepK * i);
     };
 
     // One 64-k step = slices 4 odd .. 4 odd + 3 of half-block rc (odd = which
-    // quarter of the half). Slice kq's MFMAs run while slice kq + 1 is read and
-    // decoded; during the last slice, the next step's slice 0 is decoded (from
-    // rn when the next step starts a new half-block) and read after the
-    // barrier that opens it.
+    // quarter of the half), read from stage cur. Slice kq's MFMAs run while
+    // slice kq + 1 is read and decoded; during the last slice, the next step's
+    // slice 0 is decoded (from rn when the next step starts a new half-block).
+    // Slices 0 and 1 first issue the next step's activation loads (two
+    // each); slices 1..3 of the first two steps of a block issue the next
+    // block's weight loads (runs 0..10, then 11..21). Spread out like this,
+    // the loads of eight wavefronts never pile up in front of the texture
+    // unit at once.
     bf16x8 af[2][4], bf[2][2];
-    auto step = [&](uint32_t buf, const GemmRaw &rc, int odd, const GemmRaw &rn) {
-        read_a(af[0], buf, 0);
+    auto step = [&](const __bf16 *cur, __bf16 *ahead, uint32_t s, int t, const GemmRaw &rc, const GemmRaw &rn,
+                    uint32_t *wnext, uint32_t kbn) __attribute__((always_inline)) {
+        const int odd = t & 1;
+        read_a(af[0], cur, 0);
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (kq < 2) {
+                dma_x(ahead, s + 1, 2u * kq);
+                dma_x(ahead, s + 1, 2u * kq + 1u);
+            }
+            if (t < 2 && kq >= 1) {
+                const uint32_t j0 = 11u * t + (kq == 1 ? 0u : kq == 2 ? 4u : 8u);
+                const uint32_t nj = kq == 3 ? 3u : 4u;
+#pragma unroll
+                for (uint32_t j = 0; j < nj; ++j) dma_w(wnext, kbn, j0 + j);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             if (kq < 3) {
-                read_a(af[(kq + 1) & 1], buf, kq + 1);
+                read_a(af[(kq + 1) & 1], cur, kq + 1);
                 decode(rc, 4 * odd + kq + 1, bf[(kq + 1) & 1]);
             } else if (odd == 0) {
                 decode(rc, 4, bf[0]);
@@ -834,64 +901,90 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
         }
     };
 
-    // Step s of the group (K step s0 + s): the barrier means every wavefront
-    // has finished step s - 1, so buffer (s + 1) % 2 is free for step s + 1's
-    // tile and buffer s % 2 holds step s's. Half-block hb + 1's bytes are
-    // requested at the start of half-block hb, two steps before their first
-    // use. Loads past the group's range read beyond it (the other group's
-    // columns, the next row, or zeros past the descriptors) and are never
-    // used; the store after the last step lands in a buffer nobody reads.
+    // Block b of the group (K block kb0 + b) runs steps 4 b .. 4 b + 3 from
+    // stages 0, 1, 0, 1 and weight buffer b % 2; its first two steps fill the
+    // other weight buffer with block b + 1, which was last read in block
+    // b - 1's first two steps. Raw bytes: half 1 of block b is read from LDS
+    // in step 0 (used from the end of step 1), half 0 of block b + 1 in step 3
+    // (used from the end of step 3). Step s stores step s + 1's activations
+    // into stage (s + 1) % 2, last read in step s - 1. Barriers: each step
+    // ends by waiting for its own activation loads; weight loads issued after
+    // them may stay in flight, 11 after steps 0 and 1, none after steps 2 and
+    // 3, so a block's weights are in before its predecessor's last step.
     GemmRaw raw[2];
-    load_raw(raw[0], hb0);
-    load_x(s0);
-    store_x(0);
-    load_x(s0 + 1);
+#pragma unroll
+    for (uint32_t j = 0; j < kWRuns; ++j) dma_w(ws0, kb0, j);
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) dma_x(xs0, 0, i);
+    vm_barrier<0>();
+    read_raw(raw[0], ws0, 0);
     decode(raw[0], 0, bf[0]);
-    auto half = [&](uint32_t hl, GemmRaw &rc, GemmRaw &rn) {
-        // quarter 0 of the half
-        __syncthreads();
+    auto block = [&](uint32_t b, uint32_t *wcur, uint32_t *wnext) __attribute__((always_inline)) {
+        const uint32_t kb = kb0 + b;
+        const uint32_t s = 4u * b;
+        read_raw(raw[1], wcur, 1);
+        step(xs0, xs1, s, 0, raw[0], raw[1], wnext, kb + 1);
         __builtin_amdgcn_sched_barrier(0);
-        load_raw(rn, hb0 + hl + 1);
-        store_x(1);
-        load_x(s0 + 2 * hl + 2);
-        step(0, rc, 0, rn);
+        vm_barrier<11>();
         __builtin_amdgcn_sched_barrier(0);
-        // quarter 1 of the half
-        __syncthreads();
+        step(xs1, xs0, s + 1, 1, raw[0], raw[1], wnext, kb + 1);
         __builtin_amdgcn_sched_barrier(0);
-        store_x(0);
-        load_x(s0 + 2 * hl + 3);
-        step(1, rc, 1, rn);
+        vm_barrier<11>();
+        __builtin_amdgcn_sched_barrier(0);
+        step(xs0, xs1, s + 2, 2, raw[1], raw[0], wnext, kb + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        vm_barrier<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        read_raw(raw[0], wnext, 0);
+        step(xs1, xs0, s + 3, 3, raw[1], raw[0], wnext, kb + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        vm_barrier<0>();
         __builtin_amdgcn_sched_barrier(0);
     };
-    uint32_t hl = 0;
-    for (; hl + 2 <= nb; hl += 2) {
-        half(hl, raw[0], raw[1]);
-        half(hl + 1, raw[1], raw[0]);
+    // The missing last block of group 1 (odd block count) only keeps the
+    // barrier count: four barriers, no loads, no MFMAs.
+    auto idle = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) vm_barrier<0>();
+    };
+    uint32_t b = 0;
+    for (; b + 2 <= nblk; b += 2) {
+        block(b, ws0, ws1);
+        if (kb0 + b + 1 < nb) block(b + 1, ws1, ws0);
+        else idle();
     }
-    if (hl < nb) half(hl, raw[0], raw[1]);
-    (void)steps;
+    if (b < nblk) {
+        if (kb0 + b < nb) block(b, ws0, ws1);
+        else idle();
+    }
 
     // The two K halves meet: group 1 hands over row blocks 0 and 1, group 0
-    // row blocks 2 and 3, lane-major (one dword per lane, rows of 64 lanes).
-    // Both groups add (lower half) + (upper half) in that order. The group
-    // index selects register blocks only through uniform branches, so the
-    // accumulators are never indexed at run time.
+    // row blocks 2 and 3, lane-major (one dword per lane, rows of 64 lanes, a
+    // 16 KiB region per wavefront in the stage and weight buffers). Both
+    // groups add (lower half) + (upper half) in that order. The group index
+    // selects register blocks only through uniform branches, so the
+    // accumulators are never indexed at run time. The full barrier first
+    // drains the loads still in flight (those past the group's range).
     __syncthreads();
-    float *swap = reinterpret_cast<float *>(smem);
+    auto swap_of = [&](uint32_t wv2) -> float * {
+        float *base = wv2 < 2 ? reinterpret_cast<float *>(xs0)
+                              : (wv2 < 4 ? reinterpret_cast<float *>(xs1)
+                                         : (wv2 < 6 ? reinterpret_cast<float *>(ws0) : reinterpret_cast<float *>(ws1)));
+        return base + (wv2 & 1u) * 4096u;
+    };
+    float *const sw_mine = swap_of(wave);
+    const float *const sw_other = swap_of(wave ^ 4u);
     auto give = [&](int base) {
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    swap[((wave * 64u) + 32u * ii + 16u * jj + v) * 64u + lane] = acc[base + ii][jj][v];
+                for (int v = 0; v < 16; ++v) sw_mine[(32u * ii + 16u * jj + v) * 64u + lane] = acc[base + ii][jj][v];
     };
     if (grp == 0) give(2);
     else give(0);
     __syncthreads();
-    const uint32_t partner = wave ^ 4u;
     // D layout of a 32x32 tile: lane l holds column l % 32, rows 8(v/4) + 4(l/32) + v%4.
     const bool full = rows == kGM && n0 + kGN <= N;
     auto finish = [&](int base, bool lower_is_mine) {
@@ -903,7 +996,7 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
                 const uint32_t n = n0 + 64u * wq + 32u * jj + col;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const float other = swap[((partner * 64u) + 32u * ii + 16u * jj + v) * 64u + lane];
+                    const float other = sw_other[(32u * ii + 16u * jj + v) * 64u + lane];
                     const float mine = acc[base + ii][jj][v];
                     const float sum = lower_is_mine ? mine + other : other + mine;
                     const uint32_t m = 32u * i + 8u * (v >> 2) + 4u * kh + (v & 3);
