@@ -295,7 +295,7 @@ class Bench:
                 "bound": "hbm", "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
                 "frac_fp32": f / t / 1e12 / FP32_PEAK_TFLOPS, "read_ceiling": self.read_ceiling(wr)}
 
-    def mfma(self, n=50):
+    def mfma(self, n=400):
         torch = self.torch
         log("generating M=512 inputs")
         inp = self.synth.make_inputs(4)
@@ -303,7 +303,9 @@ class Bench:
         w = torch.from_numpy(inp.blocks).to(self.dev)
         x = torch.from_numpy(inp.x).to(self.dev)
         y = torch.empty((c.M, c.N), dtype=torch.float32, device=self.dev)
-        t = time_launches(torch, lambda i: self.q2k.q2k_matmul(x, w, y, c.M, c.N, c.K, stream=self.stream), n, 5)
+        # Enough calls (about 30 ms) that the clock has settled; a short run reads 10 % slow.
+        t = time_launches(torch, lambda i: self.q2k.q2k_matmul(x, w, y, c.M, c.N, c.K, stream=self.stream), n,
+                          n // 10)
         f = 2.0 * c.M * c.N * c.K
         log("MFMA M=512: %.2f us, %.1f TFLOP/s" % (t * 1e6, f / t / 1e12))
         return {"workload": "M=512 N=14336 K=4096 (one call: bf16(x) pre-pass + GEMM)", "us": t * 1e6,
@@ -376,13 +378,13 @@ class Bench:
                 "us": t * 1e6, "algorithmic_bytes": b, "GB/s": b / t / 1e9, "bound": "hbm",
                 "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS}
 
-    def moe_prefill(self, n=20):
+    def moe_prefill(self, n=60):
         """Expert-routed prefill: 512 tokens, top_k 6 of 8 experts (matrix-core schedule, one call)."""
         torch = self.torch
         log("generating expert-routed prefill inputs")
         inp, c, p, x, ids, y = self._moe(1)
         w = torch.from_numpy(inp.blocks).to(self.dev)
-        t = time_launches(torch, lambda i: self.q2k.q2k_matmul_id(x, w, ids, y, p, stream=self.stream), n, 3)
+        t = time_launches(torch, lambda i: self.q2k.q2k_matmul_id(x, w, ids, y, p, stream=self.stream), n, 6)
         f = 2.0 * c.routes * c.n * c.K
         log("expert-routed prefill: %.2f us, %.1f TFLOP/s" % (t * 1e6, f / t / 1e12))
         return {"workload": c.name + " (one call: routing + bf16 row gather + GEMM)", "us": t * 1e6, "flop": f,
