@@ -242,6 +242,13 @@ class Bench:
         b = views[0].numel()
         return {"bytes": b, "us": t * 1e6, "GB/s": b / t / 1e9}
 
+    def write_ceiling(self, outs, n=200):
+        """torch's own fill kernel over the same output buffers: the bandwidth a plain write of this size reaches."""
+        torch = self.torch  # fills run on torch's current stream, the stream the library calls use
+        t = time_launches(torch, lambda i: outs[i % len(outs)].zero_(), n, 20)
+        b = outs[0].numel() * outs[0].element_size()
+        return {"bytes": b, "us": t * 1e6, "GB/s": b / t / 1e9}
+
     def dequant(self, n=200):
         g = self.g1
         w_bytes = g["inp"].blocks.size
@@ -253,7 +260,7 @@ class Bench:
         log("dequantize: %.2f us, %.1f GB/s" % (t * 1e6, gbs))
         return {"workload": "%d blocks (the decode GEMV weights), cold replicas" % (w_bytes // 84),
                 "us": t * 1e6, "algorithmic_bytes": b, "GB/s": gbs, "bound": "hbm",
-                "frac_hbm": gbs / HBM_PEAK_GBS}
+                "frac_hbm": gbs / HBM_PEAK_GBS, "write_ceiling": self.write_ceiling([out])}
 
     def gather(self, n=200):
         np, torch = self.np, self.torch
@@ -273,7 +280,7 @@ class Bench:
         log("gather: %.2f us/call (synchronous), %.1f GB/s" % (t * 1e6, gbs))
         return {"workload": "512 ids into a 262144 x 4096 table (64 rotating id sets); the call waits for "
                             "its id check", "us_per_call_incl_sync": t * 1e6, "algorithmic_bytes": b,
-                "GB/s": gbs, "bound": "hbm", "frac_hbm": gbs / HBM_PEAK_GBS}
+                "GB/s": gbs, "bound": "hbm", "frac_hbm": gbs / HBM_PEAK_GBS, "write_ceiling": self.write_ceiling(outs)}
 
     def gemv8(self, n=300):
         torch = self.torch

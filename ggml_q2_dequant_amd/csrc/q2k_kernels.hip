@@ -36,6 +36,14 @@ __device__ __forceinline__ uint32_t load_u32(const uint8_t *p) {
     return *reinterpret_cast<const uint32_t *>(p);
 }
 
+// Raw buffer resources (gfx9 dword 3): loads past num_records return zero,
+// which is how lanes beyond the end of the data read nothing.
+constexpr int kRsrcFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kRsrcFlags);
+}
+
 // Weights e0..e0+3 (e0 % 4 == 0) of one block. The four share a scale byte and
 // one 2-bit position of four consecutive code bytes.
 __device__ __forceinline__ float4 decode_quad(const uint8_t *blk, uint32_t e0) {
@@ -54,38 +62,72 @@ __device__ __forceinline__ float4 decode_quad(const uint8_t *blk, uint32_t e0) {
 }
 
 // ---------------------------------------------------------------------------
-// Dequantize: one 16-byte store per thread, a wavefront per block (1 KiB of
-// output), grid-stride over all quads.
-__global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ blocks, float4 *__restrict__ out,
-                                                    uint64_t nquads) {
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
-    for (uint64_t g = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < nquads; g += stride) {
-        const uint8_t *blk = blocks + (g >> 6) * kBlockBytes;
-        out[g] = decode_quad(blk, static_cast<uint32_t>(g & 63) << 2);
-    }
+// Dequantize and gather share one shape: a wavefront decodes a run of
+// consecutive blocks. It first copies their bytes into its own LDS region
+// with direct buffer-to-LDS dword loads, all in flight at once, then writes
+// block i as one 1 KiB run of 16-byte stores, lane l taking weights
+// 4l..4l+3. With one block per wavefront (84 bytes of reads in flight) the
+// dequantize mostly waited on memory latency; with runs of 64 blocks a
+// wavefront's whole input (5376 bytes) is requested before any of it is
+// needed. A wavefront only touches its own region, so there are no barriers.
+constexpr uint32_t kRunBlocks = 64;                           // blocks per dequantize wavefront
+constexpr uint32_t kRunDwords = kRunBlocks * kBlockBytes / 4;  // 1344 = 21 loads of 64 dwords
+
+// Copies blocks src[0 .. nb) into r (ceil(21 nb / 64) * 64 dwords, which r
+// must hold) and waits until they are in. Loads past the last block lie
+// beyond the descriptor and read zeros.
+__device__ __forceinline__ void stage_blocks(const uint8_t *src, uint32_t nb, uint32_t *r, uint32_t lane) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, nb * kBlockBytes);
+    const uint32_t loads = (nb * (kBlockBytes / 4) + kWave - 1) / kWave;
+    for (uint32_t j = 0; j < loads; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(r + kWave * j), 4,
+                                                 static_cast<int>(4u * (kWave * j + lane)), 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront wrote the whole region
 }
 
-// ---------------------------------------------------------------------------
-// Embedding gather: grid.y walks tokens, grid.x the 16-byte quads of a row.
-// A token whose id is >= vocab raises the status word and its row is neither
-// read nor written.
+__global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ blocks, float4 *__restrict__ out,
+                                                    uint64_t nblocks) {
+    __shared__ __attribute__((aligned(16))) uint32_t raw[4][kRunDwords];
+    const uint32_t lane = threadIdx.x & (kWave - 1u);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint64_t b0 = (static_cast<uint64_t>(blockIdx.x) * 4u + wave) * kRunBlocks;
+    if (b0 >= nblocks) return;
+    const uint32_t nb = static_cast<uint32_t>(min(static_cast<uint64_t>(kRunBlocks), nblocks - b0));
+    stage_blocks(blocks + b0 * kBlockBytes, nb, raw[wave], lane);
+    const uint8_t *rb = reinterpret_cast<const uint8_t *>(raw[wave]);
+    for (uint32_t i = 0; i < nb; ++i) out[(b0 + i) * 64u + lane] = decode_quad(rb + i * kBlockBytes, 4u * lane);
+}
+
+// Embedding gather: wavefront u takes run u % runs of token u / runs, where a
+// row of blocks_per_row blocks splits into runs = ceil(blocks_per_row / 4)
+// runs of 4 blocks. A gather moves few bytes per row, so shorter runs keep
+// more wavefronts busy (512 rows of 16 blocks: 4.5 us with 4-block runs,
+// 5.3 us with 64-block runs). A token whose id is >= vocab raises the status
+// word and its row is neither read nor written.
+constexpr uint32_t kGatherRun = 4;
+constexpr uint32_t kGatherDwords = (kGatherRun * kBlockBytes / 4 + kWave - 1) / kWave * kWave;
+
 __global__ __launch_bounds__(256) void k_gather(const uint8_t *__restrict__ table, const uint32_t *__restrict__ ids,
                                                 float4 *__restrict__ out, uint32_t vocab, uint32_t blocks_per_row,
                                                 uint32_t n_tokens, int *status) {
-    const uint32_t row_quads = blocks_per_row * 64u;
-    const uint64_t row_bytes = static_cast<uint64_t>(blocks_per_row) * kBlockBytes;
-    for (uint32_t t = blockIdx.y; t < n_tokens; t += gridDim.y) {
-        const uint32_t id = ids[t];
-        if (id >= vocab) {
-            if (blockIdx.x == 0 && threadIdx.x == 0)
-                __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            continue;
-        }
-        const uint8_t *row = table + static_cast<uint64_t>(id) * row_bytes;
-        float4 *orow = out + static_cast<uint64_t>(t) * row_quads;
-        for (uint32_t q = blockIdx.x * blockDim.x + threadIdx.x; q < row_quads; q += gridDim.x * blockDim.x)
-            orow[q] = decode_quad(row + (q >> 6) * kBlockBytes, (q & 63u) << 2);
+    __shared__ __attribute__((aligned(16))) uint32_t raw[4][kGatherDwords];
+    const uint32_t lane = threadIdx.x & (kWave - 1u);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t runs = (blocks_per_row + kGatherRun - 1) / kGatherRun;
+    const uint64_t u = static_cast<uint64_t>(blockIdx.x) * 4u + wave;
+    if (u >= static_cast<uint64_t>(n_tokens) * runs) return;
+    const uint32_t t = static_cast<uint32_t>(u / runs), c = static_cast<uint32_t>(u % runs);
+    const uint32_t id = ids[t];
+    if (id >= vocab) {
+        if (c == 0 && lane == 0) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        return;
     }
+    const uint32_t kb0 = c * kGatherRun, nb = min(kGatherRun, blocks_per_row - kb0);
+    const uint64_t row_bytes = static_cast<uint64_t>(blocks_per_row) * kBlockBytes;
+    stage_blocks(table + id * row_bytes + kb0 * kBlockBytes, nb, raw[wave], lane);
+    const uint8_t *rb = reinterpret_cast<const uint8_t *>(raw[wave]);
+    float4 *orow = out + (static_cast<uint64_t>(t) * blocks_per_row + kb0) * 64u;
+    for (uint32_t i = 0; i < nb; ++i) orow[i * 64u + lane] = decode_quad(rb + i * kBlockBytes, 4u * lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -144,14 +186,6 @@ struct GemvRoute {
 #ifndef Q2K_GEMV_SEG_ITERS
 #define Q2K_GEMV_SEG_ITERS 4  // row quadruples per workgroup
 #endif
-
-// Raw buffer resources (gfx9 dword 3): loads past num_records return zero,
-// which is how lanes beyond the end of K read nothing.
-constexpr int kRsrcFlags = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kRsrcFlags);
-}
 
 __device__ __forceinline__ void e4m3x4(uint32_t c, float *q) {
     const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c), false);
@@ -1023,21 +1057,20 @@ hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t 
 }  // namespace
 
 hipError_t launch_dequantize(const uint8_t *blocks, uint64_t nblocks, float *out, hipStream_t stream) {
-    const uint64_t nquads = nblocks * 64u;
-    const uint64_t want = (nquads + 255) / 256;
-    const uint32_t grid = static_cast<uint32_t>(want < 65536u ? want : 65536u);
-    hipLaunchKernelGGL(k_dequantize, dim3(grid), dim3(256), 0, stream, blocks, reinterpret_cast<float4 *>(out),
-                       nquads);
+    const uint64_t waves = (nblocks + kRunBlocks - 1) / kRunBlocks;
+    const uint64_t grid = (waves + 3) / 4;
+    if (grid > 0x7fffffffu) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_dequantize, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, blocks,
+                       reinterpret_cast<float4 *>(out), nblocks);
     return hipGetLastError();
 }
 
 hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, uint32_t vocab,
                          uint32_t blocks_per_row, uint32_t n_tokens, int *status, hipStream_t stream) {
-    const uint64_t row_quads = static_cast<uint64_t>(blocks_per_row) * 64u;
-    const uint64_t gx = (row_quads + 255) / 256;
-    const uint32_t grid_x = static_cast<uint32_t>(gx < 4096u ? gx : 4096u);
-    const uint32_t grid_y = n_tokens < 32768u ? n_tokens : 32768u;
-    hipLaunchKernelGGL(k_gather, dim3(grid_x, grid_y), dim3(256), 0, stream, table, ids,
+    const uint64_t runs = (blocks_per_row + kGatherRun - 1) / kGatherRun;
+    const uint64_t grid = (static_cast<uint64_t>(n_tokens) * runs + 3) / 4;
+    if (grid > 0x7fffffffu) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_gather, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, table, ids,
                        reinterpret_cast<float4 *>(out), vocab, blocks_per_row, n_tokens, status);
     return hipGetLastError();
 }

@@ -177,6 +177,17 @@ def test_gather_ragged_multi_block_rows_with_duplicates():
     assert bits_equal(gpu_gather(table, ids, vocab, dim, len(ids)), oracle.gather(table, ids, vocab, dim, len(ids)))
 
 
+def test_gather_rows_longer_than_one_run():
+    # 70 blocks per row: one run of 64 blocks and a ragged run of 6 per token.
+    rng = np.random.Generator(np.random.PCG64(38))
+    vocab, dim = 3, 70 * QK_K
+    table = synth.random_blocks(rng, vocab * dim // QK_K)
+    ids = [2, 0, 1, 2, 0]
+    assert bits_equal(gpu_gather(table, ids, vocab, dim, len(ids)), oracle.gather(table, ids, vocab, dim, len(ids)))
+    with pytest.raises(q2k.Q2KIdOutOfRange):
+        gpu_gather(table, [1, vocab, 0], vocab, dim, 3)
+
+
 def test_gather_config2_full_size_and_bad_id():
     inp = inputs(2)
     c = inp.config
