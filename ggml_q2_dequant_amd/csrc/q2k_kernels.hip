@@ -842,34 +842,47 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
     };
 
     // B fragments of MFMA slice kk (0..7) of a half-block, both columns: 2-bit
-    // position p = kk / 2, code bytes 8 (kk % 2) .. +7 of segment kh. The code
-    // bits become floats with the e4m3 trick: masked with 0x03 a byte is
-    // q * 2^-9, masked with 0x0C it is q * 2^-7 (positions 2 and 3 after a
-    // 4-bit shift). The power of two is folded into d * sc, so
-    // fma(dl, code, -ml) rounds d*sc*q - dmin*mn once, exactly as the decode
-    // rule, before the bf16 rounding.
+    // position p = kk / 2, code bytes 8 (kk % 2) .. +7 of segment kh. All 16
+    // weights of a sub-block share d * sc and dmin * mn, so a weight takes one
+    // of four values: w(q) = RN(d*sc*q - dmin*mn) for q = 0..3 (d*sc*q and
+    // dmin*mn are exact, the fma rounds once, as the decode rule does), then
+    // rounded to bf16. Those four bf16 values form an 8-byte table (w0 w1 in
+    // one dword, w2 w3 in the other), built when the sub-block's first slice
+    // (kk even) is decoded and kept for its second. Each code selects its
+    // entry with a byte permute: masked to 2q per byte, the codes become the
+    // selector bytes 2q, 2q + 1 of two table bytes. Slices are always decoded
+    // in the order 0, 1, 2, ..., so the table in hand is the sub-block's.
+    uint32_t lut[2][2];
     auto decode = [&](const GemmRaw &r, int kk, bf16x8 (&b)[2]) __attribute__((always_inline)) {
         const int p = kk >> 1, ih = kk & 1;
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const float d = f16_low(r.dd[jj]), dmin = f16_high(r.dd[jj]);
-            const uint32_t sbyte = (r.sc[jj][p >> 1] >> (8u * kh + 16u * (p & 1))) & 0xffu;  // scale byte 2p + kh
-            const float dl = d * static_cast<float>(sbyte & 15u) * ((p & 1) == 0 ? 512.0f : 128.0f);
-            const float ml = dmin * static_cast<float>(sbyte >> 4);
-            const uint32_t mask = (p & 1) == 0 ? 0x03030303u : 0x0C0C0C0Cu;
-            float wv[8];
+            if (ih == 0) {
+                // Scale byte 2p + kh: the low nibble scales d, the high one dmin.
+                const uint32_t sh = 8u * kh + 16u * static_cast<uint32_t>(p & 1);
+                const float sc = static_cast<float>(__builtin_amdgcn_ubfe(r.sc[jj][p >> 1], sh, 4));
+                const float mn = static_cast<float>(__builtin_amdgcn_ubfe(r.sc[jj][p >> 1], sh + 4u, 4));
+                const float dl = f16_low(r.dd[jj]) * sc, ml = f16_high(r.dd[jj]) * mn;
+                const bf16x2 w01 = {static_cast<__bf16>(-ml), static_cast<__bf16>(dl - ml)};
+                const bf16x2 w23 = {static_cast<__bf16>(__builtin_fmaf(dl, 2.0f, -ml)),
+                                    static_cast<__bf16>(__builtin_fmaf(dl, 3.0f, -ml))};
+                lut[jj][0] = __builtin_bit_cast(uint32_t, w01);
+                lut[jj][1] = __builtin_bit_cast(uint32_t, w23);
+            }
+            u32x4 o;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
+                // Four weights from one code dword: bytes 2q (m2) and 2q + 1 (m3), interleaved
+                // into per-weight selector pairs, pick their bf16 entries from the table.
                 const uint32_t v = r.q[jj][2 * ih + t];
-                const int c = static_cast<int>((p >= 2 ? (v >> 4) : v) & mask);
-                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
-                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
-                wv[4 * t + 0] = __builtin_fmaf(dl, lo[0], -ml);
-                wv[4 * t + 1] = __builtin_fmaf(dl, lo[1], -ml);
-                wv[4 * t + 2] = __builtin_fmaf(dl, hi[0], -ml);
-                wv[4 * t + 3] = __builtin_fmaf(dl, hi[1], -ml);
+                const uint32_t m2 = (p == 0 ? (v << 1) : (v >> (2 * p - 1))) & 0x06060606u;
+                const uint32_t m3 = m2 | 0x01010101u;
+                o[2 * t] = __builtin_amdgcn_perm(lut[jj][1], lut[jj][0], __builtin_amdgcn_perm(m3, m2, 0x05010400u));
+                o[2 * t + 1] = __builtin_amdgcn_perm(lut[jj][1], lut[jj][0], __builtin_amdgcn_perm(m3, m2, 0x07030602u));
             }
-            b[jj] = pack_bf16(wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]);
+            b[jj] = __builtin_bit_cast(bf16x8, o);
         }
     };
 
