@@ -865,7 +865,9 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
                 const float sc = static_cast<float>(__builtin_amdgcn_ubfe(r.sc[jj][p >> 1], sh, 4));
                 const float mn = static_cast<float>(__builtin_amdgcn_ubfe(r.sc[jj][p >> 1], sh + 4u, 4));
                 const float dl = f16_low(r.dd[jj]) * sc, ml = f16_high(r.dd[jj]) * mn;
-                const bf16x2 w01 = {static_cast<__bf16>(-ml), static_cast<__bf16>(dl - ml)};
+                // w(0) as fma(dl, 0, -ml), not -ml: an infinite or NaN dl must make it NaN, as
+                // d*sc*0 - dmin*mn is in the decode rule.
+                const bf16x2 w01 = {static_cast<__bf16>(__builtin_fmaf(dl, 0.0f, -ml)), static_cast<__bf16>(dl - ml)};
                 const bf16x2 w23 = {static_cast<__bf16>(__builtin_fmaf(dl, 2.0f, -ml)),
                                     static_cast<__bf16>(__builtin_fmaf(dl, 3.0f, -ml))};
                 lut[jj][0] = __builtin_bit_cast(uint32_t, w01);

@@ -407,6 +407,26 @@ def test_mfma_config4_full_size_sampled():
     print("parity cfg4 (%s, %d x %d sampled outputs): max |y - y_ref| / A = %.3g" % (c.name, len(ms), len(ns), worst))
 
 
+def test_mfma_non_finite_scales_give_nan_columns():
+    # d = +inf with zero scale nibbles and zero codes makes every d*sc*q - dmin*mn NaN (inf * 0),
+    # even for q = 0, and dmin = NaN makes the whole block NaN: those columns of y are NaN, the
+    # rest match the oracle.
+    rng = np.random.Generator(np.random.PCG64(39))
+    M, N, K = 9, 16, 512
+    blocks = synth.random_blocks(rng, N * K // QK_K).reshape(N, K // QK_K, BB).copy()
+    blocks[3, 0, 0:16] &= 0xF0                                                  # scales 0
+    blocks[3, 0, 16:80] = 0                                                     # codes 0
+    blocks[3, 0, 80:82] = np.frombuffer(np.float16(np.inf).tobytes(), np.uint8)  # d = +inf
+    blocks[7, 1, 82:84] = np.frombuffer(np.float16(np.nan).tobytes(), np.uint8)  # dmin = NaN
+    blocks = blocks.reshape(-1)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    y = gpu_matmul(x, blocks, M, N, K)
+    ref, _ = oracle.matmul(x, blocks, M, N, K)
+    assert np.array_equal(np.isnan(y), np.isnan(ref)) and np.all(np.isnan(y[:, [3, 7]]))
+    keep = [n for n in range(N) if n not in (3, 7)]
+    check_mfma(y[:, keep], x, synth.rows_of(blocks, K, keep), M, len(keep), K)
+
+
 def test_mfma_one_hot_returns_bf16_weights_bitwise():
     rng = np.random.Generator(np.random.PCG64(37))
     N, K = 72, 1024
