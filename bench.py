@@ -315,9 +315,23 @@ class Bench:
                           n // 10)
         f = 2.0 * c.M * c.N * c.K
         log("MFMA M=512: %.2f us, %.1f TFLOP/s" % (t * 1e6, f / t / 1e12))
+        # Context, not part of the path: the same call with all-zero activations (the part's clock is
+        # power-managed and MFMA power depends on the operand bits), and torch's own bf16 linear layer on
+        # the same shape with both operands already bf16 in memory (no decode, no conversion).
+        x0 = torch.zeros_like(x)
+        t0 = time_launches(torch, lambda i: self.q2k.q2k_matmul(x0, w, y, c.M, c.N, c.K, stream=self.stream), n,
+                           n // 10)
+        x16 = x.to(torch.bfloat16)
+        w16 = torch.randn((c.N, c.K), dtype=torch.float32, device=self.dev).to(torch.bfloat16)
+        tv = time_launches(torch, lambda i: torch.nn.functional.linear(x16, w16), n, n // 10)
+        log("  same call, zero activations: %.2f us; torch bf16 linear, same shape: %.2f us" % (t0 * 1e6, tv * 1e6))
+        del x0, x16, w16
         return {"workload": "M=512 N=14336 K=4096 (one call: bf16(x) pre-pass + GEMM)", "us": t * 1e6,
                 "flop": f, "TFLOP/s": f / t / 1e12, "bound": "mfma",
-                "frac_bf16_mfma": f / t / 1e12 / BF16_PEAK_TFLOPS}
+                "frac_bf16_mfma": f / t / 1e12 / BF16_PEAK_TFLOPS,
+                "context": {"zero_activations_us": t0 * 1e6,
+                            "torch_bf16_linear_same_shape": {"us": tv * 1e6, "TFLOP/s": f / tv / 1e12,
+                                                             "frac_bf16_mfma": f / tv / 1e12 / BF16_PEAK_TFLOPS}}}
 
     def batched(self, n=200):
         """Batched mat-vec: 8 independent decode GEMVs (M=1, N=K=4096) in one call, cold weights."""

@@ -306,12 +306,7 @@ q2k_status q2k_matmul_path(const float *x, const void *w, float *y, uint32_t M, 
     const auto st = static_cast<hipStream_t>(stream);
     if (path == Q2K_PATH_GEMV) {
         if (M > q2k::kGemvMaxM) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul: the GEMV path takes M <= 8 (got %u)", M);
-        void *ws = nullptr;
-        if (const uint64_t wsb = q2k::gemv_workspace_bytes(M, K, 1)) {
-            s = stream_workspace(st, static_cast<size_t>(wsb), &ws);
-            if (s != Q2K_OK) return s;
-        }
-        e = q2k::launch_gemv(x, wb, y, M, N, K, 1, ws, st);
+        e = q2k::launch_gemv(x, wb, y, M, N, K, 1, st);
     } else if (path == Q2K_PATH_MFMA) {
         void *ws = nullptr;
         s = stream_workspace(st, static_cast<size_t>(M) * K * 2, &ws);
@@ -349,20 +344,11 @@ q2k_status q2k_matmul_batched(const float *x, const void *w, float *y, uint32_t 
         return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul_batched: y overlaps an input");
     const auto st = static_cast<hipStream_t>(stream);
     const auto *wp = static_cast<const uint8_t *>(w);
-    // Problems per launch: at most kMaxGridY, and (for M >= 3) few enough that
-    // their activation fragments fit a 64 MiB workspace.
-    uint64_t per = q2k::kMaxGridY;
-    void *ws = nullptr;
-    if (const uint64_t one = q2k::gemv_workspace_bytes(M, K, 1)) {
-        const uint64_t fit = (uint64_t{64} << 20) / one;
-        if (fit < per) per = fit > 0 ? fit : 1;
-        const uint64_t n = batches < per ? batches : per;
-        q2k_status s = stream_workspace(st, static_cast<size_t>(n * one), &ws);
-        if (s != Q2K_OK) return s;
-    }
+    // Problems per launch: at most kMaxGridY.
+    const uint64_t per = q2k::kMaxGridY;
     for (uint64_t b0 = 0; b0 < batches; b0 += per) {
         const uint32_t nbat = static_cast<uint32_t>(batches - b0 < per ? batches - b0 : per);
-        hipError_t e = q2k::launch_gemv(x + b0 * xe, wp + b0 * we, y + b0 * ye, M, N, K, nbat, ws, st);
+        hipError_t e = q2k::launch_gemv(x + b0 * xe, wp + b0 * we, y + b0 * ye, M, N, K, nbat, st);
         if (e != hipSuccess) return device_error("q2k_matmul_batched launch", e);
     }
     return ok();

@@ -381,8 +381,8 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
 //  - A holds x in two f16 pieces (x' = h1 + h2 to 2^-22 of |x'|), after scaling
 //    each row of each block by a power of two 2^s so its largest |x| lies in
 //    [2^13, 2^14). Products h * v * 2^-24 are exact in fp32.
-// k_mv_prep builds the A fragments once per call; k_gemv_mfma streams the
-// weights. Codes at 2-bit position p are masked in place (value 4^p q for
+// k_gemv_mfma builds each block's A fragments inside the wavefront that uses
+// them and streams the weights. Codes at 2-bit position p are masked in place (value 4^p q for
 // p < 3, 4q for p = 3 after a 4-bit shift), so the A pieces of position p
 // carry the inverse factor 1, 1/4, 1/16 or 1/4 (exact powers of two).
 //
@@ -400,102 +400,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kMvTiles = 4;             // 16-column tiles per workgroup
 constexpr uint32_t kMvWaves = 16;
-constexpr uint32_t kMvFragBytes = 8 * 64 * 16;                  // A fragments of one block
-constexpr uint32_t kMvMinsOff = kMvFragBytes;                   // min-term A fragments (64 x 8 B)
-constexpr uint32_t kMvScaleOff = kMvMinsOff + 64 * 8;           // 8 inverse row scales
-constexpr uint32_t kMvPrepBytes = kMvScaleOff + 8 * 4;          // per (problem, block)
-static_assert(kMvPrepBytes % 16 == 0, "prep records stay 16-byte aligned");
 
 __device__ __forceinline__ void f16_pieces(float v, _Float16 *h1, _Float16 *h2) {
     const _Float16 a = static_cast<_Float16>(v);
     *h1 = a;
     *h2 = static_cast<_Float16>(v - static_cast<float>(a));
-}
-
-// grid (K / 256, problems); 256 threads, thread t <-> element t of the block
-// in every row. x of problem p starts at p * x_elems. Row maxima and sub-block
-// sums are lane-shuffle trees (sub-block s is lanes 16 (s % 4) .. +15 of
-// wavefront s / 4); the scaled rows are staged element-major in LDS.
-__global__ __launch_bounds__(256) void k_mv_prep(const float *__restrict__ x, uint8_t *__restrict__ ws, uint32_t M,
-                                                 uint32_t K, uint64_t x_elems) {
-    __shared__ float xs[256][8];
-    __shared__ float wmax[4][8];
-    __shared__ float sub[16][8];
-    __shared__ float fwd[8];
-    const uint32_t b = blockIdx.x, t = threadIdx.x, lane = t & 63u, wave = t >> 6, nb = K >> 8;
-    const float *xb = x + blockIdx.y * x_elems + b * 256u;
-    uint8_t *rec = ws + (static_cast<uint64_t>(blockIdx.y) * nb + b) * kMvPrepBytes;
-    float v[8], a[8], sm[8];
-#pragma unroll
-    for (uint32_t m = 0; m < 8; ++m) v[m] = m < M ? xb[static_cast<uint64_t>(m) * K + t] : 0.0f;
-#pragma unroll
-    for (uint32_t m = 0; m < 8; ++m) {
-        a[m] = __builtin_fabsf(v[m]);
-        sm[m] = v[m];
-    }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1)
-#pragma unroll
-        for (uint32_t m = 0; m < 8; ++m) {
-            a[m] = __builtin_fmaxf(a[m], __shfl_xor(a[m], o, 64));
-            sm[m] += __shfl_xor(sm[m], o, 64);
-        }
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1)
-#pragma unroll
-        for (uint32_t m = 0; m < 8; ++m) a[m] = __builtin_fmaxf(a[m], __shfl_xor(a[m], o, 64));
-    if ((lane & 15u) == 0) {
-#pragma unroll
-        for (uint32_t m = 0; m < 8; ++m) sub[t >> 4][m] = sm[m];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (uint32_t m = 0; m < 8; ++m) wmax[wave][m] = a[m];
-    }
-    __syncthreads();
-    // s = 13 - floor(log2 max): the scaled row lies in [2^13, 2^14). A subnormal
-    // maximum counts as 2^-127; zero, inf or NaN maxima leave the row unscaled.
-    if (t < 8) {
-        const float mx = __builtin_fmaxf(__builtin_fmaxf(wmax[0][t], wmax[1][t]), __builtin_fmaxf(wmax[2][t], wmax[3][t]));
-        int s = 0;
-        if (mx > 0.0f && mx <= 3.4e38f) {
-            const int e = static_cast<int>(__builtin_bit_cast(uint32_t, mx) >> 23) - 127;
-            s = 13 - e;
-            s = s < -100 ? -100 : (s > 100 ? 100 : s);
-        }
-        fwd[t] = __builtin_bit_cast(float, static_cast<uint32_t>(127 + s) << 23);
-        reinterpret_cast<float *>(rec + kMvScaleOff)[t] = __builtin_bit_cast(float, static_cast<uint32_t>(127 - s) << 23);
-    }
-    __syncthreads();
-#pragma unroll
-    for (uint32_t m = 0; m < 8; ++m) xs[t][m] = v[m] * fwd[m];
-    __syncthreads();
-    // A fragments: entry q = (j, lane) for q = t and t + 256.
-#pragma unroll
-    for (uint32_t h = 0; h < 2; ++h) {
-        const uint32_t q = t + 256u * h, j = q >> 6, l = q & 63u, r = l & 15u, m = r & 7u, G = l >> 4, p = j >> 1;
-        const uint32_t e0 = 128u * (G >> 1) + 32u * p + 16u * (G & 1u) + 8u * (j & 1u);
-        const float c = p == 0 ? 1.0f : (p == 2 ? 0.0625f : 0.25f);
-        f16x8 f;
-#pragma unroll
-        for (uint32_t i = 0; i < 8; ++i) {
-            _Float16 h1, h2;
-            f16_pieces(xs[e0 + i][m] * c, &h1, &h2);
-            f[i] = r < 8 ? h1 : h2;
-        }
-        reinterpret_cast<f16x8 *>(rec)[q] = f;
-    }
-    if (t < 64) {
-        const uint32_t r = t & 15u, m = r & 7u, G = t >> 4;
-        f16x4 f;
-#pragma unroll
-        for (uint32_t i = 0; i < 4; ++i) {
-            _Float16 h1, h2;
-            f16_pieces(sub[4u * G + i][m] * fwd[m] * 0.03125f, &h1, &h2);  // |sum| < 2^18: scaled by 2^-5 into f16 range
-            f[i] = r < 8 ? h1 : h2;
-        }
-        reinterpret_cast<f16x4 *>(rec + kMvMinsOff)[t] = f;
-    }
 }
 
 // Which blocks and tiles a wavefront of k_gemv_mfma takes (set by the host):
@@ -506,28 +415,47 @@ struct MvPlan {
     uint32_t wpb, active;
 };
 
-// grid (ceil(N / (16 kMvTiles)), problems); 1024 threads = 16 wavefronts. Each
-// keeps its block's A fragments in registers for all its tiles; per tile the
-// wavefronts' partial sums (both pieces) meet in LDS and are added in
-// wavefront order, piece 1 before piece 2.
+// Activation rows of one block in LDS: 8 rows of 256 floats per wavefront,
+// rows 260 floats apart so that lanes reading different rows at the same
+// column start in different banks.
+constexpr uint32_t kMvXRow = 260;
+constexpr uint32_t kMvXWave = 8 * kMvXRow;
+
+// grid (ceil(N / (16 kMvTiles)), problems); 1024 threads = 16 wavefronts.
+// Each wavefront builds its block's A fragments itself: it copies the block's
+// 8 activation rows into its own LDS region (direct buffer-to-LDS loads,
+// issued before the weight loads so they land first), finds each row's
+// power-of-two scale and the sub-block sums there, and splits the scaled
+// activations into f16 pieces, all while its weight bytes are in flight. The
+// fragments stay in registers for all its tiles; per tile the wavefronts'
+// partial sums (both pieces) meet in LDS and are added in wavefront order,
+// piece 1 before piece 2.
 template <bool kAll>
-__global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ w, float *__restrict__ y,
-                                                   const uint8_t *__restrict__ ws, uint32_t M, uint32_t N, uint32_t K,
+__global__ __launch_bounds__(1024) void k_gemv_mfma(const float *__restrict__ x, const uint8_t *__restrict__ w,
+                                                   float *__restrict__ y, uint32_t M, uint32_t N, uint32_t K,
                                                    GemvBatch bt, MvPlan plan) {
-    __shared__ float red[kMvWaves][kMvTiles][256];
+    __shared__ __attribute__((aligned(16))) float lds[kMvWaves * kMvXWave];
+    static_assert(kMvXWave >= kMvTiles * 256, "the partial sums reuse the activation rows");
+    x += blockIdx.y * bt.x_elems;
     w += blockIdx.y * bt.w_bytes;
     y += blockIdx.y * bt.y_elems;
     const uint32_t nb = K >> 8, row_bytes = nb * kBlockBytes;
-    const uint8_t *prep = ws + static_cast<uint64_t>(blockIdx.y) * nb * kMvPrepBytes;
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t col = lane & 15u, G = lane >> 4;
     const uint32_t row0 = blockIdx.x * (16u * kMvTiles);
     const uint32_t nrows = min(16u * kMvTiles, N - row0);
-    // Rows past N lie beyond the descriptor and read as zeros (their sums are never stored).
+    // Rows past N (weights) or M (activations) lie beyond these descriptors and read as zeros.
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(w + static_cast<uint64_t>(row0) * row_bytes, nrows * row_bytes);
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, M * K * 4u);
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    float *const xw = lds + wave * kMvXWave;
+    // A row r = col of this lane: activation row m = r % 8, piece r / 8. Its
+    // elements of MFMA j lie in sub-block 8 (G / 2) + 2 (j / 2) + G % 2.
+    const uint32_t m = col & 7u;
+    const bool second = col >= 8u;
+    const uint32_t xbase = m * kMvXRow + 128u * (G >> 1) + 16u * (G & 1u);
 
     f32x4 acc[kMvTiles];
 #pragma unroll
@@ -537,27 +465,114 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
     const uint32_t tl = kAll ? 0u : wave / nb;
     const uint32_t b_first = kAll ? wave : wave % nb, b_step = kAll ? kMvWaves : nb;
     for (uint32_t b = b_first; active && b < nb; b += b_step) {
-        const uint8_t *rec = prep + static_cast<uint64_t>(b) * kMvPrepBytes;
-        f16x8 af[8];
+        // Activation rows 0..7 of block b: one 1 KiB load per row, 16 bytes a lane.
 #pragma unroll
-        for (uint32_t j = 0; j < 8; ++j) af[j] = reinterpret_cast<const f16x8 *>(rec)[j * 64u + lane];
-        const f16x4 am = reinterpret_cast<const f16x4 *>(rec + kMvMinsOff)[lane];
-        const f32x4 isc = reinterpret_cast<const f32x4 *>(rec + kMvScaleOff)[G & 1u];
-        // Every tile's bytes of this block are requested before any arithmetic.
+        for (uint32_t r = 0; r < 8; ++r) {
+            const uint32_t u = __builtin_amdgcn_readfirstlane((r * K + 256u * b) * 4u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void *)(xw + r * kMvXRow),
+                                                     16, static_cast<int>(u + 16u * lane), 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // Every tile's bytes of this block (with a partial plan, the
+        // wavefront's own tiles') are requested before any arithmetic.
         u32x4 qv[kMvTiles];
         u32x2 scv[kMvTiles];
         uint32_t mnv[kMvTiles], ddv[kMvTiles];
 #pragma unroll
         for (uint32_t t = 0; t < kMvTiles; ++t) {
+            if (!kAll && t % plan.wpb != tl) continue;
             const uint32_t off = (16u * t + col) * row_bytes + b * kBlockBytes;
             qv[t] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16u + 16u * G, 0, 0);
             scv[t] = __builtin_amdgcn_raw_buffer_load_b64(wr, off + 8u * (G >> 1), 0, 0);
             mnv[t] = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 4u * G, 0, 0);
             ddv[t] = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 80u, 0, 0);
         }
-        // Keep every load above the arithmetic: sunk next to its use, each A
-        // fragment load would wait out a full memory latency on its own.
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kAll) {
+            // Loads complete in issue order: the activation rows are in once at
+            // most the 4 kMvTiles weight loads issued after them are in flight,
+            // so the scaling below overlaps the weights' memory latency.
+            constexpr uint32_t kAfter = 4 * kMvTiles;
+            __builtin_amdgcn_s_waitcnt(static_cast<int>((kAfter & 15u) | ((kAfter >> 4) << 14) | 0x0F70u));
+        } else {
+            // The weight loads depend on the plan here, so wait for all of them.
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Row maximum of |x| over the block and the sum of each of this
+        // lane's four sub-blocks (pairwise, in element order).
+        float mx = 0.0f, ssum[4];
+#pragma unroll
+        for (uint32_t p = 0; p < 4; ++p) {
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(xw + xbase + 32u * p);
+            float v[16];
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q) {
+                const f32x4 t4 = src[q];
+                v[4 * q] = t4[0];
+                v[4 * q + 1] = t4[1];
+                v[4 * q + 2] = t4[2];
+                v[4 * q + 3] = t4[3];
+            }
+#pragma unroll
+            for (uint32_t i = 0; i < 16; ++i) mx = p == 0 && i == 0 ? __builtin_fabsf(v[0]) : __builtin_fmaxf(mx, __builtin_fabsf(v[i]));
+            float s2[8], s4[4];
+#pragma unroll
+            for (uint32_t i = 0; i < 8; ++i) s2[i] = v[2 * i] + v[2 * i + 1];
+#pragma unroll
+            for (uint32_t i = 0; i < 4; ++i) s4[i] = s2[2 * i] + s2[2 * i + 1];
+            ssum[p] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // s = 13 - floor(log2 max): the scaled row lies in [2^13, 2^14). A subnormal
+        // maximum counts as 2^-127; zero, inf or NaN maxima leave the row unscaled.
+        int sx = 0;
+        if (mx > 0.0f && mx <= 3.4e38f) {
+            const int e = static_cast<int>(__builtin_bit_cast(uint32_t, mx) >> 23) - 127;
+            sx = 13 - e;
+            sx = sx < -100 ? -100 : (sx > 100 ? 100 : sx);
+        }
+        const float fwd = __builtin_bit_cast(float, static_cast<uint32_t>(127 + sx) << 23);
+        const float inv = __builtin_bit_cast(float, static_cast<uint32_t>(127 - sx) << 23);
+
+        // A fragments: MFMA j takes elements 8 (j % 2) .. +7 of sub-block p = j / 2,
+        // scaled by 2^s and by the position factor 1, 1/4, 1/16, 1/4.
+        f16x8 af[8];
+#pragma unroll
+        for (uint32_t j = 0; j < 8; ++j) {
+            const uint32_t p = j >> 1;
+            const float c = p == 0 ? 1.0f : (p == 2 ? 0.0625f : 0.25f);
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(xw + xbase + 32u * p + 8u * (j & 1u));
+            const f32x4 lo = src[0], hi = src[1];
+            const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+            for (uint32_t i = 0; i < 8; ++i) {
+                _Float16 h1, h2;
+                f16_pieces(v[i] * fwd * c, &h1, &h2);
+                af[j][i] = second ? h2 : h1;
+            }
+            if (j & 1u) __builtin_amdgcn_sched_barrier(0);
+        }
+        // Min-term fragment: sub-blocks 4 G .. 4 G + 3 of row m, whose sums lie
+        // with lanes 16 (2 (G / 2) + i % 2) + col, as their sum number
+        // 2 (G % 2) + i / 2.
+        f16x4 am;
+#pragma unroll
+        for (uint32_t i = 0; i < 4; ++i) {
+            const int src = static_cast<int>(16u * (2u * (G >> 1) + (i & 1u)) + col);
+            const float s0 = __shfl(ssum[i >> 1], src, 64), s1 = __shfl(ssum[2 + (i >> 1)], src, 64);
+            _Float16 h1, h2;
+            f16_pieces((G & 1u ? s1 : s0) * fwd * 0.03125f, &h1, &h2);  // |sum| < 2^18: scaled by 2^-5 into f16 range
+            am[i] = second ? h2 : h1;
+        }
+        // Inverse scales of D rows 4 (G % 2) .. +3 (activation rows of lanes 0..7).
+        f32x4 isc;
+#pragma unroll
+        for (uint32_t v = 0; v < 4; ++v) isc[v] = __shfl(inv, static_cast<int>(4u * (G & 1u) + v), 64);
+
 #pragma unroll
         for (uint32_t t = 0; t < kMvTiles; ++t) {
             if (!kAll && t % plan.wpb != tl) continue;
@@ -597,17 +612,20 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const uint8_t *__restrict__ 
     }
 
     // Lane l holds rows 4 G + v (piece G / 2 of m = 4 (G % 2) + v) of column l % 16.
+    // The partial sums reuse the activation rows once every wavefront is done with them.
+    __syncthreads();
 #pragma unroll
     for (uint32_t t = 0; t < kMvTiles; ++t)
 #pragma unroll
-        for (uint32_t v = 0; v < 4; ++v) red[wave][t][(4u * G + v) * 16u + col] = acc[t][v];
+        for (uint32_t v = 0; v < 4; ++v) xw[t * 256u + (4u * G + v) * 16u + col] = acc[t][v];
     __syncthreads();
     if (tid < kMvTiles * 128u) {
-        const uint32_t t = tid >> 7, q = tid & 127u, m = q >> 4, c = q & 15u, n = row0 + 16u * t + c;
-        float s = red[0][t][q] + red[0][t][q + 128u];
+        const uint32_t t = tid >> 7, q = tid & 127u, mm = q >> 4, c = q & 15u, n = row0 + 16u * t + c;
+        const float *rs = lds + t * 256u;
+        float s = rs[q] + rs[q + 128u];
 #pragma unroll
-        for (uint32_t wv = 1; wv < kMvWaves; ++wv) s += red[wv][t][q] + red[wv][t][q + 128u];
-        if (m < M && n < N) y[static_cast<uint64_t>(m) * N + n] = s;
+        for (uint32_t wv = 1; wv < kMvWaves; ++wv) s += rs[wv * kMvXWave + q] + rs[wv * kMvXWave + q + 128u];
+        if (mm < M && n < N) y[static_cast<uint64_t>(mm) * N + n] = s;
     }
 }
 
@@ -1090,12 +1108,8 @@ hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, 
     return hipGetLastError();
 }
 
-uint64_t gemv_workspace_bytes(uint32_t M, uint32_t K, uint32_t batches) {
-    return M <= 2 ? 0 : static_cast<uint64_t>(batches) * (K / kQK) * kMvPrepBytes;
-}
-
 hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
-                       uint32_t batches, void *ws, hipStream_t stream) {
+                       uint32_t batches, hipStream_t stream) {
     if (batches == 0 || batches > kMaxGridY) return hipErrorInvalidValue;
     const GemvBatch bt{static_cast<uint64_t>(M) * K, static_cast<uint64_t>(N) * (K / kQK) * kBlockBytes,
                        static_cast<uint64_t>(M) * N};
@@ -1103,16 +1117,14 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, u
         case 1: return launch_gemv_seg<1>(x, w, y, N, K, batches, bt, stream);
         case 2: return launch_gemv_seg<2>(x, w, y, N, K, batches, bt, stream);
         case 3: case 4: case 5: case 6: case 7: case 8: {
-            auto *rec = static_cast<uint8_t *>(ws);
             const uint32_t nb = K / kQK;
-            hipLaunchKernelGGL(k_mv_prep, dim3(nb, batches), dim3(256), 0, stream, x, rec, M, K, bt.x_elems);
             const uint32_t wgs = (N + 16 * kMvTiles - 1) / (16 * kMvTiles);
             if (nb >= kMvWaves) {
-                hipLaunchKernelGGL(k_gemv_mfma<true>, dim3(wgs, batches), dim3(1024), 0, stream, w, y, rec, M, N, K, bt,
+                hipLaunchKernelGGL(k_gemv_mfma<true>, dim3(wgs, batches), dim3(1024), 0, stream, x, w, y, M, N, K, bt,
                                    MvPlan{1, kMvWaves});
             } else {
                 const uint32_t wpb = kMvWaves / nb;
-                hipLaunchKernelGGL(k_gemv_mfma<false>, dim3(wgs, batches), dim3(1024), 0, stream, w, y, rec, M, N, K,
+                hipLaunchKernelGGL(k_gemv_mfma<false>, dim3(wgs, batches), dim3(1024), 0, stream, x, w, y, M, N, K,
                                    bt, MvPlan{wpb, nb * wpb});
             }
             return hipGetLastError();

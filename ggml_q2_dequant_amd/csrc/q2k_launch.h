@@ -24,11 +24,9 @@ hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, 
 
 // 1 <= M <= 8; batches problems laid out batch-major (x [batches, M, K],
 // w [batches, N, K/256 blocks], y [batches, M, N]), 1 <= batches <= kMaxGridY.
-// For M >= 3, ws is a device workspace of gemv_workspace_bytes(M, K, batches)
-// bytes (16-byte aligned) for the f16 activation fragments; unused for M <= 2.
-uint64_t gemv_workspace_bytes(uint32_t M, uint32_t K, uint32_t batches);
+// Needs no workspace.
 hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
-                       uint32_t batches, void *ws, hipStream_t stream);
+                       uint32_t batches, hipStream_t stream);
 
 // Matrix-core path. x_bf16 is a device workspace of at least M * K * 2 bytes
 // (16-byte aligned) that receives bf16(x) before the GEMM reads it.

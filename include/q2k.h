@@ -89,8 +89,8 @@ q2k_status q2k_dequantize(const void *blocks, size_t blocks_bytes, float *out, s
  *   M, N >= 1; K a multiple of 256 with 256 <= K <= 2^21.
  * M <= 8 runs the fp32-accurate GEMV: |y - exact| <= 1e-5 * sum_k |x*w| per
  * output. M <= 2 uses fp32 FMAs; 3 <= M <= 8 uses the matrix cores on exact
- * f16 encodings of the weights' integer parts and a two-piece f16 split of x
- * (staging 8736 bytes per 256 columns of K in the workspace below).
+ * f16 encodings of the weights' integer parts and a two-piece f16 split of x,
+ * built inside the kernel (no workspace).
  * A row of y depends only on its own row of x: calls with the same M give it
  * bit-identical values whatever the other rows hold (M <= 2 and 3 <= M <= 8
  * run different kernels and may differ in the last bits).
@@ -122,9 +122,8 @@ q2k_status q2k_matmul_path(const float *x, const void *w, float *y, uint32_t M, 
  *   batches, N >= 1; 1 <= M <= 8 (the fp32 mat-vec path); K as for q2k_matmul.
  * Slice b of y is bit-identical to q2k_matmul(x + b*M*K, w + b*N*K/256*84,
  * y + b*M*N, M, N, K), whatever the other slices hold. Asynchronous on
- * `stream`. For M >= 3 it uses the per-(device, stream) workspace (at most
- * 64 MiB; larger batches run in several launches); for M <= 2 it allocates
- * nothing.
+ * `stream`. Allocates nothing; more than 65535 problems run in several
+ * launches.
  */
 q2k_status q2k_matmul_batched(const float *x, const void *w, float *y, uint32_t batches, uint32_t M, uint32_t N,
                               uint32_t K, void *stream);

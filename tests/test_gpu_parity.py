@@ -238,8 +238,10 @@ def test_gemv_configs(cfg):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (3, 7, 768), (8, 130, 1280), (5, 4097, 256), (2, 9, 4352),
-                                   (7, 33, 1024)])
+                                   (7, 33, 1024), (8, 100, 8448), (4, 65, 4352)])
 def test_gemv_ragged_shapes(M, N, K):
+    # For 3 <= M <= 8, K < 4096 gives blocks shared by several wavefronts, and
+    # K > 4096 (33 and 17 blocks here) wavefronts that walk several blocks.
     rng = np.random.Generator(np.random.PCG64(M * 1000 + N + K))
     blocks = synth.random_blocks(rng, N * K // QK_K)
     x = rng.standard_normal((M, K), dtype=np.float32)
