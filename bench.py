@@ -13,8 +13,8 @@ oracle is timed on the host cores on a bounded sample and reported as
 "cpu_baseline".
 
 Other modes (used to collect rocprofv3 counters; they print one short JSON line):
-  --only ROW         run only one row's timed loop (gemv1, dequant, gather, gemv8, mfma, batched,
-                     sample, moe_decode, moe_prefill)
+  --only ROW         run only one row's timed loop (gemv1, dequant, gather, gemv8, mfma, mfma_context,
+                     batched, sample, moe_decode, moe_prefill)
   --copy-probe       also run a device-to-device copy of COPY_BYTES (counter calibration)
   --sweep            M=1 GEMV over N = 4096 .. 131072 (K = 4096, cold) beside the plain-read ceiling
   --derive-traffic FETCH_CSV WRITE_CSV
@@ -49,7 +49,8 @@ KERNEL_SRC = os.path.join(ROOT, "ggml_q2_dequant_amd", "csrc", "q2k_kernels.hip"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMV_KERNEL = "k_gemv_seg<1"    # name prefix of the M = 1 GEMV kernel in rocprofv3 output
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-ROWS = ("gemv1", "dequant", "gather", "gemv8", "mfma", "batched", "sample", "moe_decode", "moe_prefill")
+ROWS = ("gemv1", "dequant", "gather", "gemv8", "mfma", "mfma_context", "batched", "sample", "moe_decode",
+        "moe_prefill")
 
 
 def log(msg: str) -> None:
@@ -278,9 +279,19 @@ class Bench:
                                                                          stream=self.stream), n, 20)
         gbs = b / t / 1e9
         log("gather: %.2f us/call (synchronous), %.1f GB/s" % (t * 1e6, gbs))
+        # The asynchronous entry point on the same calls: back-to-back launches, one status word checked
+        # once after the timed region.
+        status = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        ta = time_launches(torch, lambda i: self.q2k.q2k_embedding_gather_async(
+            table, id_sets[i % 64], outs[i % 8], c.vocab, c.embed_dim, c.n_tokens, status, stream=self.stream), n, 20)
+        if int(status.item()) != 0:
+            raise RuntimeError("gather: a valid id set raised the status word")
+        log("gather: %.2f us/call (asynchronous), %.1f GB/s" % (ta * 1e6, b / ta / 1e9))
         return {"workload": "512 ids into a 262144 x 4096 table (64 rotating id sets); the call waits for "
                             "its id check", "us_per_call_incl_sync": t * 1e6, "algorithmic_bytes": b,
-                "GB/s": gbs, "bound": "hbm", "frac_hbm": gbs / HBM_PEAK_GBS, "write_ceiling": self.write_ceiling(outs)}
+                "GB/s": gbs, "bound": "hbm", "frac_hbm": gbs / HBM_PEAK_GBS,
+                "async": {"us_per_call": ta * 1e6, "GB/s": b / ta / 1e9, "frac_hbm": b / ta / 1e9 / HBM_PEAK_GBS},
+                "write_ceiling": self.write_ceiling(outs)}
 
     def gemv8(self, n=300):
         torch = self.torch
@@ -315,23 +326,32 @@ class Bench:
                           n // 10)
         f = 2.0 * c.M * c.N * c.K
         log("MFMA M=512: %.2f us, %.1f TFLOP/s" % (t * 1e6, f / t / 1e12))
-        # Context, not part of the path: the same call with all-zero activations (the part's clock is
-        # power-managed and MFMA power depends on the operand bits), and torch's own bf16 linear layer on
-        # the same shape with both operands already bf16 in memory (no decode, no conversion).
-        x0 = torch.zeros_like(x)
-        t0 = time_launches(torch, lambda i: self.q2k.q2k_matmul(x0, w, y, c.M, c.N, c.K, stream=self.stream), n,
-                           n // 10)
-        x16 = x.to(torch.bfloat16)
-        w16 = torch.randn((c.N, c.K), dtype=torch.float32, device=self.dev).to(torch.bfloat16)
-        tv = time_launches(torch, lambda i: torch.nn.functional.linear(x16, w16), n, n // 10)
-        log("  same call, zero activations: %.2f us; torch bf16 linear, same shape: %.2f us" % (t0 * 1e6, tv * 1e6))
-        del x0, x16, w16
         return {"workload": "M=512 N=14336 K=4096 (one call: bf16(x) pre-pass + GEMM)", "us": t * 1e6,
                 "flop": f, "TFLOP/s": f / t / 1e12, "bound": "mfma",
-                "frac_bf16_mfma": f / t / 1e12 / BF16_PEAK_TFLOPS,
-                "context": {"zero_activations_us": t0 * 1e6,
-                            "torch_bf16_linear_same_shape": {"us": tv * 1e6, "TFLOP/s": f / tv / 1e12,
-                                                             "frac_bf16_mfma": f / tv / 1e12 / BF16_PEAK_TFLOPS}}}
+                "frac_bf16_mfma": f / t / 1e12 / BF16_PEAK_TFLOPS}
+
+    def mfma_context(self, n=400):
+        """Context for the M=512 row, not part of the path: the same call with all-zero activations (the
+        part's clock is power-managed and matrix-core power depends on the operand bits), and torch's own
+        bf16 linear layer on the same shape with both operands already bf16 in memory (no decode, no
+        conversion)."""
+        torch = self.torch
+        inp = self.synth.make_inputs(4)
+        c = inp.config
+        w = torch.from_numpy(inp.blocks).to(self.dev)
+        x0 = torch.zeros((c.M, c.K), dtype=torch.float32, device=self.dev)
+        y = torch.empty((c.M, c.N), dtype=torch.float32, device=self.dev)
+        t0 = time_launches(torch, lambda i: self.q2k.q2k_matmul(x0, w, y, c.M, c.N, c.K, stream=self.stream), n,
+                           n // 10)
+        x16 = torch.from_numpy(inp.x).to(self.dev).to(torch.bfloat16)
+        w16 = torch.randn((c.N, c.K), dtype=torch.float32, device=self.dev).to(torch.bfloat16)
+        tv = time_launches(torch, lambda i: torch.nn.functional.linear(x16, w16), n, n // 10)
+        f = 2.0 * c.M * c.N * c.K
+        log("M=512 context: same call on zero activations %.2f us; torch bf16 linear, same shape %.2f us" % (
+            t0 * 1e6, tv * 1e6))
+        return {"zero_activations_us": t0 * 1e6,
+                "torch_bf16_linear_same_shape": {"us": tv * 1e6, "TFLOP/s": f / tv / 1e12,
+                                                 "frac_bf16_mfma": f / tv / 1e12 / BF16_PEAK_TFLOPS}}
 
     def batched(self, n=200):
         """Batched mat-vec: 8 independent decode GEMVs (M=1, N=K=4096) in one call, cold weights."""
@@ -526,6 +546,7 @@ def main() -> int:
         rows["gather"] = b.gather()
         rows["gemv_m8"] = b.gemv8()
         rows["mfma_m512"] = b.mfma()
+        rows["mfma_m512"]["context"] = b.mfma_context()
         rows["batched_mv"] = b.batched()
         rows["argmax_candidates"] = b.sample()
         rows["moe_decode"] = b.moe_decode()

@@ -14,6 +14,8 @@ Functions carry the C names:
   per matrix of a batch-major stack (1 <= M <= 8).
 * ``q2k_embedding_gather(table, ids, out, vocab, embed_dim, n_tokens)`` — rows
   of a Q2_K table; raises ``Q2KIdOutOfRange`` for an id >= vocab.
+* ``q2k_embedding_gather_async(table, ids, out, vocab, embed_dim, n_tokens,
+  status)`` — the same without waiting; a bad id sets the device int ``status``.
 * ``q2k_argmax_candidates(logits, n_slots, vocab, cap, top1_idx, top1_val,
   cand_count, overflow, cand_ids)`` — first-max argmax and the logits within
   0.5 of it, per slot.
@@ -59,6 +61,7 @@ EXPORTS = (
     "q2k_matmul_path",
     "q2k_matmul_batched",
     "q2k_embedding_gather",
+    "q2k_embedding_gather_async",
     "q2k_argmax_candidates",
     "q2k_matmul_id",
     "q2k_matmul_id_path",
@@ -136,7 +139,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.q2k_matmul_path.argtypes = [P, P, P, U32, U32, U32, ctypes.c_int, P]
     lib.q2k_matmul_batched.argtypes = [P, P, P, U32, U32, U32, U32, P]
     lib.q2k_embedding_gather.argtypes = [P, P, P, U32, U32, U32, P]
-    for name in ("q2k_dequantize", "q2k_matmul", "q2k_matmul_path", "q2k_matmul_batched", "q2k_embedding_gather"):
+    lib.q2k_embedding_gather_async.argtypes = [P, P, P, U32, U32, U32, P, P]
+    for name in ("q2k_dequantize", "q2k_matmul", "q2k_matmul_path", "q2k_matmul_batched", "q2k_embedding_gather",
+                 "q2k_embedding_gather_async"):
         getattr(lib, name).restype = ctypes.c_int
     lib.q2k_argmax_candidates.argtypes = [P, U32, U32, U32, P, P, P, P, P, P]
     lib.q2k_argmax_candidates.restype = ctypes.c_int
@@ -237,6 +242,13 @@ def q2k_embedding_gather(table, ids, out, vocab: int, embed_dim: int, n_tokens: 
     """out[t, :] = decoded row ids[t] of ``table``; raises Q2KIdOutOfRange for any id >= vocab."""
     _check(load_library().q2k_embedding_gather(_ptr(table), _ptr(ids), _ptr(out), vocab, embed_dim, n_tokens,
                                                _stream(stream)))
+
+
+def q2k_embedding_gather_async(table, ids, out, vocab: int, embed_dim: int, n_tokens: int, status,
+                               stream=None) -> None:
+    """q2k_embedding_gather without the wait: an id >= vocab sets ``status`` (a device int32 tensor) to 1."""
+    _check(load_library().q2k_embedding_gather_async(_ptr(table), _ptr(ids), _ptr(out), vocab, embed_dim, n_tokens,
+                                                     _ptr(status), _stream(stream)))
 
 
 def q2k_argmax_candidates(logits, n_slots: int, vocab: int, cap: int, top1_idx, top1_val, cand_count, overflow,

@@ -90,6 +90,27 @@ struct StatusWord {
 std::mutex g_status_mu;
 std::vector<StatusWord *> g_status;  // indexed by device ordinal; never freed
 
+// Argument rules shared by both gather entry points (sizes, alignment, overlap).
+q2k_status check_gather(const char *fn, const void *table, const uint32_t *ids, float *out, uint32_t vocab,
+                        uint32_t embed_dim, uint32_t n_tokens) {
+    if (!table || !ids || !out) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+    if (vocab == 0 || embed_dim == 0 || n_tokens == 0)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: vocab, embed_dim, n_tokens must be >= 1 (got %u, %u, %u)", fn,
+                    vocab, embed_dim, n_tokens);
+    if (embed_dim % q2k::kQK != 0)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: embed_dim=%u is not a multiple of 256", fn, embed_dim);
+    const uint32_t bpr = embed_dim / q2k::kQK;
+    uint64_t tb, ob, ib, t;
+    if (!mul_ok(vocab, bpr, &t) || !mul_ok(t, q2k::kBlockBytes, &tb) || !mul_ok(n_tokens, embed_dim, &t) ||
+        !mul_ok(t, 4, &ob) || !mul_ok(n_tokens, 4, &ib))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: size overflow", fn);
+    if (!aligned(table, 4) || !aligned(ids, 4) || !aligned(out, 16))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: table and ids must be 4-byte aligned, out 16-byte aligned", fn);
+    if (overlap(out, ob, table, tb) || overlap(out, ob, ids, ib))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: out overlaps an input", fn);
+    return Q2K_OK;
+}
+
 q2k_status status_word(StatusWord **out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -492,34 +513,37 @@ q2k_status q2k_read_probe(const void *data, size_t bytes, uint32_t *sink, size_t
 
 q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *out, uint32_t vocab,
                                 uint32_t embed_dim, uint32_t n_tokens, void *stream) {
-    if (!table || !ids || !out) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_embedding_gather: null pointer");
-    if (vocab == 0 || embed_dim == 0 || n_tokens == 0)
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_embedding_gather: vocab, embed_dim, n_tokens must be >= 1 (got %u, %u, %u)",
-                    vocab, embed_dim, n_tokens);
-    if (embed_dim % q2k::kQK != 0)
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_embedding_gather: embed_dim=%u is not a multiple of 256", embed_dim);
-    const uint32_t bpr = embed_dim / q2k::kQK;
-    uint64_t tb, ob, ib, t;
-    if (!mul_ok(vocab, bpr, &t) || !mul_ok(t, q2k::kBlockBytes, &tb) || !mul_ok(n_tokens, embed_dim, &t) ||
-        !mul_ok(t, 4, &ob) || !mul_ok(n_tokens, 4, &ib))
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_embedding_gather: size overflow");
-    if (!aligned(table, 4) || !aligned(ids, 4) || !aligned(out, 16))
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_embedding_gather: table and ids must be 4-byte aligned, out 16-byte aligned");
-    if (overlap(out, ob, table, tb) || overlap(out, ob, ids, ib))
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_embedding_gather: out overlaps an input");
-
+    q2k_status s = check_gather("q2k_embedding_gather", table, ids, out, vocab, embed_dim, n_tokens);
+    if (s != Q2K_OK) return s;
     StatusWord *sw = nullptr;
-    q2k_status s = status_word(&sw);
+    s = status_word(&sw);
     if (s != Q2K_OK) return s;
     std::lock_guard<std::mutex> lock(sw->mu);
     *sw->host = 0;
     const auto st = static_cast<hipStream_t>(stream);
-    hipError_t e = q2k::launch_gather(static_cast<const uint8_t *>(table), ids, out, vocab, bpr, n_tokens, sw->dev, st);
+    hipError_t e = q2k::launch_gather(static_cast<const uint8_t *>(table), ids, out, vocab, embed_dim / q2k::kQK,
+                                      n_tokens, sw->dev, st);
     if (e != hipSuccess) return device_error("q2k_embedding_gather launch", e);
     e = hipStreamSynchronize(st);
     if (e != hipSuccess) return device_error("q2k_embedding_gather sync", e);
     const int bad = __atomic_load_n(sw->host, __ATOMIC_ACQUIRE);
     if (bad) return fail(Q2K_ERR_ID_OUT_OF_RANGE, "q2k_embedding_gather: a token id is >= vocab (%u)", vocab);
+    return ok();
+}
+
+q2k_status q2k_embedding_gather_async(const void *table, const uint32_t *ids, float *out, uint32_t vocab,
+                                      uint32_t embed_dim, uint32_t n_tokens, int *status, void *stream) {
+    q2k_status s = check_gather("q2k_embedding_gather_async", table, ids, out, vocab, embed_dim, n_tokens);
+    if (s != Q2K_OK) return s;
+    if (!status) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_embedding_gather_async: status is required");
+    if (!aligned(status, 4)) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_embedding_gather_async: status must be 4-byte aligned");
+    const uint64_t ob = static_cast<uint64_t>(n_tokens) * embed_dim * 4;
+    const uint64_t tb = static_cast<uint64_t>(vocab) * (embed_dim / q2k::kQK) * q2k::kBlockBytes;
+    if (overlap(status, 4, out, ob) || overlap(status, 4, table, tb) || overlap(status, 4, ids, 4ull * n_tokens))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_embedding_gather_async: status overlaps an input or out");
+    hipError_t e = q2k::launch_gather(static_cast<const uint8_t *>(table), ids, out, vocab, embed_dim / q2k::kQK,
+                                      n_tokens, status, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_error("q2k_embedding_gather_async launch", e);
     return ok();
 }
 

@@ -239,6 +239,25 @@ q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *o
                                 uint32_t embed_dim, uint32_t n_tokens, void *stream);
 
 /*
+ * q2k_embedding_gather_async — the same gather without the wait, for callers
+ * that issue many gathers and check the ids once (a serving loop).
+ * Page: the same test as q2k_embedding_gather; the bad id is still rejected,
+ * but reported through *status instead of the return value.
+ *   table, ids, out, vocab, embed_dim, n_tokens  as for q2k_embedding_gather.
+ *   status  device int (or device-mapped host int), 4-byte aligned, not
+ *           overlapping the other buffers; required. If any id is >= vocab the
+ *           kernel sets *status to 1; libq2k never clears it (the caller zeroes
+ *           it before the first call and reads it after the stream has passed
+ *           the calls it covers).
+ * Rows of valid ids are bit-identical to q2k_embedding_gather's; rows of bad
+ * ids are left unwritten. Returns Q2K_OK once the kernel is enqueued
+ * (asynchronous on `stream`); argument errors are reported as for
+ * q2k_embedding_gather and enqueue nothing. Allocates nothing.
+ */
+q2k_status q2k_embedding_gather_async(const void *table, const uint32_t *ids, float *out, uint32_t vocab,
+                                      uint32_t embed_dim, uint32_t n_tokens, int *status, void *stream);
+
+/*
  * q2k_argmax_candidates — per slot of [n_slots, vocab] f32 logits: the first
  * maximum and the indices within 0.5 of it.
  * Page: docs.rs source page of mlx-native 0.9.5, src/mlx_native/ops/gpu_sample.rs

@@ -130,6 +130,22 @@ def test_gather_rejects_null_misaligned_and_overlap(lib):
     _err(lib, lib.q2k_embedding_gather(A, C + 4, C, 3, 256, 2, None), "overlaps")
 
 
+D = 4 << 32
+
+
+def test_gather_async_rejects_like_the_gather_and_checks_status(lib):
+    f = lib.q2k_embedding_gather_async
+    _err(lib, f(None, B, C, 3, 256, 2, D, None), "null")
+    _err(lib, f(A, B, C, 3, 255, 2, D, None), "multiple of 256")
+    _err(lib, f(A, B, C + 8, 3, 256, 2, D, None), "aligned")
+    _err(lib, f(A, B, A, 3, 256, 2, D, None), "overlaps")
+    _err(lib, f(A, B, C, 3, 256, 2, None, None), "status is required")
+    _err(lib, f(A, B, C, 3, 256, 2, D + 2, None), "aligned")
+    _err(lib, f(A, B, C, 3, 256, 2, C + 1024, None), "status overlaps")    # inside out (2 rows x 1 KiB)
+    _err(lib, f(A, B, C, 3, 256, 2, B + 4, None), "status overlaps")       # the second id
+    _err(lib, f(A, B, C, 3, 256, 2, A + 84, None), "status overlaps")      # inside the table
+
+
 D, E, F, G = 4 << 32, 5 << 32, 6 << 32, 7 << 32
 
 

@@ -178,7 +178,7 @@ def test_gather_ragged_multi_block_rows_with_duplicates():
 
 
 def test_gather_rows_longer_than_one_run():
-    # 70 blocks per row: one run of 64 blocks and a ragged run of 6 per token.
+    # 70 blocks per row: 17 runs of 4 blocks and a ragged run of 2 per token.
     rng = np.random.Generator(np.random.PCG64(38))
     vocab, dim = 3, 70 * QK_K
     table = synth.random_blocks(rng, vocab * dim // QK_K)
@@ -207,6 +207,37 @@ def test_gather_config2_full_size_and_bad_id():
     keep = np.arange(c.n_tokens) != c.bad_id_pos
     assert bits_equal(got[keep], want[keep])      # valid rows are still written
     assert np.all(np.isnan(got[c.bad_id_pos]))    # the bad row is never touched
+
+
+def test_gather_async_matches_the_gather_and_reports_bad_ids():
+    # The asynchronous gather writes the same rows; a bad id sets the caller's
+    # status word (which no later call clears) and leaves its row untouched.
+    rng = np.random.Generator(np.random.PCG64(39))
+    vocab, dim, nt = 300, 1280, 40
+    table_h = synth.random_blocks(rng, vocab * dim // QK_K)
+    ids_h = rng.integers(0, vocab, nt).astype(np.uint32)
+    ids_h[5] = ids_h[9]
+    table, status = dev(table_h), torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    out = torch.full((nt, dim), float("nan"), dtype=torch.float32, device="cuda:0")
+    q2k.q2k_embedding_gather_async(table, dev(ids_h), out, vocab, dim, nt, status)
+    torch.cuda.synchronize()
+    want = oracle.gather(table_h, ids_h, vocab, dim, nt)
+    assert bits_equal(out.cpu().numpy(), want) and int(status.item()) == 0
+    assert bits_equal(gpu_gather(table_h, ids_h, vocab, dim, nt), out.cpu().numpy())
+
+    bad = ids_h.copy()
+    bad[[3, 17]] = [vocab, 0xFFFFFFFF]
+    out.fill_(float("nan"))
+    q2k.q2k_embedding_gather_async(table, dev(bad), out, vocab, dim, nt, status)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    keep = np.ones(nt, bool)
+    keep[[3, 17]] = False
+    assert int(status.item()) == 1
+    assert bits_equal(got[keep], want[keep]) and np.all(np.isnan(got[~keep]))
+    q2k.q2k_embedding_gather_async(table, dev(ids_h), out, vocab, dim, nt, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1 and bits_equal(out.cpu().numpy(), want)
 
 
 def test_gather_last_row_of_table():
