@@ -16,6 +16,8 @@ Other modes (used to collect rocprofv3 counters; they print one short JSON line)
   --only ROW         run only one row's timed loop (gemv1, dequant, gather, gemv8, mfma, mfma_context,
                      batched, sample, moe_decode, moe_prefill)
   --copy-probe       also run a device-to-device copy of COPY_BYTES (counter calibration)
+  --no-context       skip the M=512 context timings (used when profiling every kernel, so the
+                     GEMM's statistics hold only the row's own calls)
   --sweep            M=1 GEMV over N = 4096 .. 131072 (K = 4096, cold) beside the plain-read ceiling
   --derive-traffic FETCH_CSV WRITE_CSV
                      turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
@@ -449,6 +451,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the M=512 context timings (zero activations, torch bf16 linear)")
     ap.add_argument("--only", choices=ROWS, help="run only this row's timed loop")
     ap.add_argument("--copy-probe", action="store_true", help="also run the calibration copy")
     ap.add_argument("--derive-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -546,7 +550,8 @@ def main() -> int:
         rows["gather"] = b.gather()
         rows["gemv_m8"] = b.gemv8()
         rows["mfma_m512"] = b.mfma()
-        rows["mfma_m512"]["context"] = b.mfma_context()
+        if not args.no_context:
+            rows["mfma_m512"]["context"] = b.mfma_context()
         rows["batched_mv"] = b.batched()
         rows["argmax_candidates"] = b.sample()
         rows["moe_decode"] = b.moe_decode()
