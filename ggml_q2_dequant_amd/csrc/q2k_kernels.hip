@@ -396,7 +396,9 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
 // block with k = sub-block (lane l: sub-blocks 4 (l / 16) .. +3).
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kMvTiles = 4;             // 16-column tiles per workgroup
 constexpr uint32_t kMvWaves = 16;
@@ -500,31 +502,38 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const float *__restrict__ x,
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        // Row maximum of |x| over the block and the sum of each of this
-        // lane's four sub-blocks (pairwise, in element order).
-        float mx = 0.0f, ssum[4];
+        // Lanes col and col ^ 8 hold the same activation row m (pieces 1 and 2)
+        // and share the work: each takes half and the halves are exchanged by a
+        // DPP rotation of its 16-lane row by 8.
+        const uint32_t half = second ? 1u : 0u;
+        // Row maximum of |x| over the block, and the sums (pairwise, in element
+        // order) of sub-blocks p = 2 half and 2 half + 1 of this lane's four.
+        float mx = 0.0f, s01[2];
 #pragma unroll
-        for (uint32_t p = 0; p < 4; ++p) {
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(xw + xbase + 32u * p);
+        for (uint32_t q = 0; q < 2; ++q) {
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(xw + xbase + 32u * (2u * half + q));
             float v[16];
 #pragma unroll
-            for (uint32_t q = 0; q < 4; ++q) {
-                const f32x4 t4 = src[q];
-                v[4 * q] = t4[0];
-                v[4 * q + 1] = t4[1];
-                v[4 * q + 2] = t4[2];
-                v[4 * q + 3] = t4[3];
+            for (uint32_t r4 = 0; r4 < 4; ++r4) {
+                const f32x4 t4 = src[r4];
+                v[4 * r4] = t4[0];
+                v[4 * r4 + 1] = t4[1];
+                v[4 * r4 + 2] = t4[2];
+                v[4 * r4 + 3] = t4[3];
             }
 #pragma unroll
-            for (uint32_t i = 0; i < 16; ++i) mx = p == 0 && i == 0 ? __builtin_fabsf(v[0]) : __builtin_fmaxf(mx, __builtin_fabsf(v[i]));
+            for (uint32_t i = 0; i < 16; ++i) mx = q == 0 && i == 0 ? __builtin_fabsf(v[0]) : __builtin_fmaxf(mx, __builtin_fabsf(v[i]));
             float s2[8], s4[4];
 #pragma unroll
             for (uint32_t i = 0; i < 8; ++i) s2[i] = v[2 * i] + v[2 * i + 1];
 #pragma unroll
             for (uint32_t i = 0; i < 4; ++i) s4[i] = s2[2 * i] + s2[2 * i + 1];
-            ssum[p] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-            __builtin_amdgcn_sched_barrier(0);
+            s01[q] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+            // Pin the sums here: left to the compiler they sink to their use after
+            // the fragments, keeping all 32 activations live.
+            asm volatile("" : "+v"(s01[q]), "+v"(mx));
         }
+        mx = __builtin_fmaxf(mx, dpp<kDppRowRor8>(mx));
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
         // s = 13 - floor(log2 max): the scaled row lies in [2^13, 2^14). A subnormal
@@ -539,33 +548,42 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const float *__restrict__ x,
         const float inv = __builtin_bit_cast(float, static_cast<uint32_t>(127 - sx) << 23);
 
         // A fragments: MFMA j takes elements 8 (j % 2) .. +7 of sub-block p = j / 2,
-        // scaled by 2^s and by the position factor 1, 1/4, 1/16, 1/4.
+        // scaled by 2^s and by the position factor 1, 1/4, 1/16, 1/4. This lane
+        // splits elements 4 half .. +3 into h1 = f16(v) and h2 = f16(v - h1) (two at
+        // a time, rounded to nearest even), keeps its own piece and hands the
+        // other to its partner, which split the other four elements.
         f16x8 af[8];
 #pragma unroll
         for (uint32_t j = 0; j < 8; ++j) {
             const uint32_t p = j >> 1;
-            const float c = p == 0 ? 1.0f : (p == 2 ? 0.0625f : 0.25f);
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(xw + xbase + 32u * p + 8u * (j & 1u));
-            const f32x4 lo = src[0], hi = src[1];
-            const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            // 2^s times the position factor, one exact power of two: the product
+            // differs from scaling twice only below f32's normal range, where both
+            // pieces are zero in f16 anyway.
+            const float c = fwd * (p == 0 ? 1.0f : (p == 2 ? 0.0625f : 0.25f));
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(xw + xbase + 32u * p + 8u * (j & 1u) + 4u * half);
+            uint32_t own[2], got[2];
 #pragma unroll
-            for (uint32_t i = 0; i < 8; ++i) {
-                _Float16 h1, h2;
-                f16_pieces(v[i] * fwd * c, &h1, &h2);
-                af[j][i] = second ? h2 : h1;
+            for (uint32_t i = 0; i < 2; ++i) {
+                const f32x2 a = {v[2 * i] * c, v[2 * i + 1] * c};
+                const f16x2 h1 = __builtin_convertvector(a, f16x2);
+                const f16x2 h2 = __builtin_convertvector(a - __builtin_convertvector(h1, f32x2), f16x2);
+                const uint32_t b1 = __builtin_bit_cast(uint32_t, h1), b2 = __builtin_bit_cast(uint32_t, h2);
+                own[i] = second ? b2 : b1;
+                got[i] = __builtin_bit_cast(uint32_t, dpp<kDppRowRor8>(__builtin_bit_cast(float, second ? b1 : b2)));
             }
-            if (j & 1u) __builtin_amdgcn_sched_barrier(0);
+            af[j] = __builtin_bit_cast(f16x8, second ? u32x4{got[0], got[1], own[0], own[1]}
+                                                     : u32x4{own[0], own[1], got[0], got[1]});
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // Min-term fragment: sub-blocks 4 G .. 4 G + 3 of row m, whose sums lie
-        // with lanes 16 (2 (G / 2) + i % 2) + col, as their sum number
-        // 2 (G % 2) + i / 2.
+        // Min-term fragment: sub-blocks 4 G .. 4 G + 3 of row m. Sub-block 4 G + i
+        // is sum number i / 2 of lane 16 (2 (G / 2) + i % 2) + m + 8 (G % 2).
         f16x4 am;
 #pragma unroll
         for (uint32_t i = 0; i < 4; ++i) {
-            const int src = static_cast<int>(16u * (2u * (G >> 1) + (i & 1u)) + col);
-            const float s0 = __shfl(ssum[i >> 1], src, 64), s1 = __shfl(ssum[2 + (i >> 1)], src, 64);
+            const int src = static_cast<int>(16u * (2u * (G >> 1) + (i & 1u)) + m + 8u * (G & 1u));
+            const float sub = __shfl(s01[i >> 1], src, 64);
             _Float16 h1, h2;
-            f16_pieces((G & 1u ? s1 : s0) * fwd * 0.03125f, &h1, &h2);  // |sum| < 2^18: scaled by 2^-5 into f16 range
+            f16_pieces(sub * fwd * 0.03125f, &h1, &h2);  // |sum| < 2^18: scaled by 2^-5 into f16 range
             am[i] = second ? h2 : h1;
         }
         // Inverse scales of D rows 4 (G % 2) .. +3 (activation rows of lanes 0..7).
