@@ -171,8 +171,9 @@ struct GemvRoute {
 // code segment g = l % 4: the 16 code bytes qs[32h + 16s ..] with h = g / 2,
 // s = g % 2, at all four 2-bit positions p -- that is, all of sub-blocks
 // 8h + 2p + s (64 weights). The lane's 64 activations depend only on
-// (block, segment), so a chunk's activations are loaded once per workgroup
-// and stay in registers for all 4 * NI rows. All of a chunk's loads are issued
+// (block, segment): each wavefront copies its four blocks' activations into
+// LDS once per chunk, and each lane reads its 64 from there into registers,
+// where they stay for all 4 * NI rows. All of a chunk's loads are issued
 // before any arithmetic, so the workgroup's whole share of the matrix is in
 // flight at once.
 //
@@ -223,11 +224,23 @@ __device__ __forceinline__ SegLoads load_seg(__amdgpu_buffer_rsrc_t rs, uint32_t
     return t;
 }
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Wait until at most N vector-memory operations of this wavefront are still in
+// flight (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14, the other counters at
+// their "no wait" maxima).
+template <uint32_t N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N < 64, "vmcnt has six bits");
+    __builtin_amdgcn_s_waitcnt(static_cast<int>((N & 15u) | ((N >> 4) << 14) | 0x0F70u));
+}
+
 template <int M, int NI, bool kRouted>
 __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, const uint8_t *__restrict__ w,
                                                   float *__restrict__ y, uint32_t N, uint32_t K, GemvBatch bt,
                                                   GemvRoute rt) {
     __shared__ float red[4][NI * 4 * M];
+    __shared__ __attribute__((aligned(16))) float xl[4][M][1024];  // per wavefront: x of its four blocks
     const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1);
     const uint32_t row0 = blockIdx.x * (4 * NI);
     if constexpr (kRouted) {
@@ -276,10 +289,33 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
         // (they read zeros) and their activation loads beyond K (zeros too).
         const uint32_t boff = kb < nb ? kb * kBlockBytes : 0x80000000u;
 
-        // Activations first (L2-resident, needed by every row), then each row
-        // quadruple's weights in the order they are used, so the arithmetic on
-        // the first rows overlaps the arrival of the later ones.
-        const uint32_t xoff = 4 * (kb * 256u + 128 * h + 16 * s);
+        // The wavefront's activations (its four blocks: 4 KiB per row of x) go
+        // to its own LDS region by direct buffer-to-LDS loads, then each row
+        // quadruple's weights are requested in the order they are used. The
+        // four lanes of a (block, segment) read the same activations, so loading
+        // them once into LDS instead of once per lane keeps three quarters of
+        // the activation bytes off the vector-memory path, ahead of the weights.
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (uint32_t j = 0; j < 4; ++j) {
+                const uint32_t u = __builtin_amdgcn_readfirstlane(4u * (kb0 + 4u * wave) * 256u + 1024u * j);
+                // (A descriptor held in a local: this compiler drops the host-side
+                // kernel stub when the LDS load takes an element of xr.)
+                const __amdgpu_buffer_rsrc_t xm = xr[m];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xm, (__attribute__((address_space(3))) void *)(xl[wave][m] + 256u * j), 16,
+                    static_cast<int>(u + 16u * lane), 0, 0, 0);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        SegLoads wl[NI];
+#pragma unroll
+        for (int it = 0; it < NI; ++it) wl[it] = load_seg(wrs, wrow[it] + boff, g, h);
+        __builtin_amdgcn_sched_barrier(0);
+        // Loads complete in issue order: the activations are in once at most the
+        // 3 NI weight loads are still in flight.
+        vm_wait<3u * NI>();
+        __builtin_amdgcn_sched_barrier(0);
         float xv[M][4][16], xs[M][4];
 #pragma unroll
         for (int m = 0; m < M; ++m)
@@ -287,18 +323,11 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
             for (int p = 0; p < 4; ++p)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr[m], xoff + 128 * p + 16 * i, 0, 0);
-                    // (Element copies go through a named temporary: this compiler folds
-                    // __builtin_bit_cast of a vector subscript to element 0.)
+                    const f32x4v v = *reinterpret_cast<const f32x4v *>(xl[wave][m] + bq * 256u + 128u * h + 16u * s +
+                                                                      32u * p + 4u * i);
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const uint32_t e = v[c];
-                        xv[m][p][4 * i + c] = __builtin_bit_cast(float, e);
-                    }
+                    for (int c = 0; c < 4; ++c) xv[m][p][4 * i + c] = v[c];
                 }
-        SegLoads wl[NI];
-#pragma unroll
-        for (int it = 0; it < NI; ++it) wl[it] = load_seg(wrs, wrow[it] + boff, g, h);
         // Keep the scheduler from sinking these loads towards their uses.
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
