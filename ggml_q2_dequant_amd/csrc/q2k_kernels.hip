@@ -184,9 +184,20 @@ struct GemvRoute {
 // T = sum q*x; the row gains d * sc * T - dmin * mn * sum(x). Partial sums are
 // reduced over the 16 lanes of a row with DPP and over the four wavefronts
 // through LDS, in a fixed order.
-#ifndef Q2K_GEMV_SEG_ITERS
-#define Q2K_GEMV_SEG_ITERS 4  // row quadruples per workgroup
-#endif
+// Row quadruples per workgroup. Four (16 rows) keep a decode-sized matrix
+// (N = 4096: 256 workgroups) spread over every CU; once a launch has at least
+// two 24-row workgroups per CU, six (24 rows) amortize each workgroup's
+// activation loads and reduction over more rows (expert-routed decode over
+// 6 x 14336 rows: 33 us against 39 us). A row's arithmetic does not depend on
+// the choice, so both give bit-identical rows.
+constexpr int kSegItersSmall = 4, kSegItersLarge = 6;
+constexpr uint64_t kSegLargeMinWorkgroups = 512;
+static_assert(4ull * kSegItersLarge * (kMaxK / 256) * 84 < (1ull << 31), "a workgroup's rows fit a 31-bit offset");
+
+inline bool seg_iters_large(uint32_t N, uint64_t problems) {
+    return static_cast<uint64_t>((N + 4 * kSegItersLarge - 1) / (4 * kSegItersLarge)) * problems >=
+           kSegLargeMinWorkgroups;
+}
 
 __device__ __forceinline__ void e4m3x4(uint32_t c, float *q) {
     const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c), false);
@@ -1124,14 +1135,20 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
     else finish(2, false);
 }
 
-template <int M>
-hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, uint32_t batches,
-                           GemvBatch bt, hipStream_t stream) {
-    constexpr int NI = Q2K_GEMV_SEG_ITERS;
+template <int M, int NI>
+hipError_t launch_gemv_seg_ni(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, uint32_t batches,
+                              GemvBatch bt, hipStream_t stream) {
     const uint32_t blocks = (N + 4 * NI - 1) / (4 * NI);
     hipLaunchKernelGGL((k_gemv_seg<M, NI, false>), dim3(blocks, batches), dim3(256), 0, stream, x, w, y, N, K, bt,
                        GemvRoute{});
     return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, uint32_t batches,
+                           GemvBatch bt, hipStream_t stream) {
+    return seg_iters_large(N, batches) ? launch_gemv_seg_ni<M, kSegItersLarge>(x, w, y, N, K, batches, bt, stream)
+                                       : launch_gemv_seg_ni<M, kSegItersSmall>(x, w, y, N, K, batches, bt, stream);
 }
 
 }  // namespace
@@ -1197,13 +1214,17 @@ hipError_t launch_gemm_mfma(const float *x, const uint8_t *w, float *y, uint32_t
 hipError_t launch_moe_gemv(const float *x, const uint8_t *w, const uint32_t *ids, float *y, uint32_t routes,
                            uint32_t x_div, uint32_t N, uint32_t K, uint32_t n_experts, uint64_t expert_stride,
                            int *status, hipStream_t stream) {
-    constexpr int NI = Q2K_GEMV_SEG_ITERS;
-    const uint32_t blocks = (N + 4 * NI - 1) / (4 * NI);
+    const bool large = seg_iters_large(N, routes);
+    const uint32_t rows = 4 * (large ? kSegItersLarge : kSegItersSmall), blocks = (N + rows - 1) / rows;
     for (uint32_t r0 = 0; r0 < routes; r0 += kMaxGridY) {
         const uint32_t nr = routes - r0 < kMaxGridY ? routes - r0 : kMaxGridY;
         const GemvRoute rt{ids, status, expert_stride, r0, x_div, n_experts};
-        hipLaunchKernelGGL((k_gemv_seg<1, NI, true>), dim3(blocks, nr), dim3(256), 0, stream, x, w, y, N, K,
-                           GemvBatch{}, rt);
+        if (large)
+            hipLaunchKernelGGL((k_gemv_seg<1, kSegItersLarge, true>), dim3(blocks, nr), dim3(256), 0, stream, x, w, y,
+                               N, K, GemvBatch{}, rt);
+        else
+            hipLaunchKernelGGL((k_gemv_seg<1, kSegItersSmall, true>), dim3(blocks, nr), dim3(256), 0, stream, x, w, y,
+                               N, K, GemvBatch{}, rt);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
