@@ -72,6 +72,7 @@ __device__ __forceinline__ float4 decode_quad(const uint8_t *blk, uint32_t e0) {
 // needed. A wavefront only touches its own region, so there are no barriers.
 constexpr uint32_t kRunBlocks = 64;                           // blocks per dequantize wavefront
 constexpr uint32_t kRunDwords = kRunBlocks * kBlockBytes / 4;  // 1344 = 21 loads of 64 dwords
+static_assert(kRunDwords % kWave == 0, "stage_blocks fills whole loads of 64 dwords: the region must hold them");
 
 // Copies blocks src[0 .. nb) into r (ceil(21 nb / 64) * 64 dwords, which r
 // must hold) and waits until they are in. Loads past the last block lie
