@@ -1127,7 +1127,10 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
                     const float sum = lower_is_mine ? mine + other : other + mine;
                     const uint32_t m = 32u * i + 8u * (v >> 2) + 4u * kh + (v & 3);
                     const uint32_t dst = kRouted ? rowmap[m] : m0 + m;
-                    if (full || (m < rows && n < N)) y[static_cast<uint64_t>(dst) * N + n] = sum;
+                    // Non-temporal: 29 MB of y per M=512 call cannot stay in L2 anyway, and
+                    // the streaming hint took about 1.5 us off the store phase at the end.
+                    if (full || (m < rows && n < N))
+                        __builtin_nontemporal_store(sum, &y[static_cast<uint64_t>(dst) * N + n]);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // one 16-value group live at a time
             }
