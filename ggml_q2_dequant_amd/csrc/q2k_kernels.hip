@@ -833,7 +833,18 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
     const uint32_t grp = wave >> 2, wq = wave & 3u;
     const uint32_t kh = lane >> 5, col = lane & 31u;
     uint32_t tm, tn;
-    gemm_tile(blockIdx.x, tiles_m, (N + kGN - 1) / kGN, &tm, &tn);
+    if constexpr (kRouted) {
+        // Routing tiles in list order (full tiles first, partial ones last), all N
+        // tiles of one routing tile in turn: the short tiles run at the end and
+        // fill the last round of workgroups. With a multiple of 8 N tiles, N tile
+        // tn always lands on XCD tn % 8, so an expert's weight rows stay in one
+        // XCD's L2.
+        const uint32_t tiles_n = (N + kGN - 1) / kGN;
+        tm = blockIdx.x / tiles_n;
+        tn = blockIdx.x % tiles_n;
+    } else {
+        gemm_tile(blockIdx.x, tiles_m, (N + kGN - 1) / kGN, &tm, &tn);
+    }
     const uint32_t n0 = tn * kGN;
     const uint32_t nb = K >> 8, row_bytes = nb * kBlockBytes;
     // rows: valid rows of the tile; xt, wt: its activations and weight matrix.
@@ -1020,10 +1031,15 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
                 decode(rn, 0, bf[0]);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                // A partial routing tile skips the row blocks it does not fill (their
+                // rows are never stored). The dense path keeps every MFMA: the
+                // branch cost it 2 us there.
+                if (kRouted && i > 0 && 32u * i >= rows) continue;
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
                     acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kq & 1][i], bf[kq & 1][jj], acc[i][jj], 0, 0, 0);
+            }
         }
     };
 

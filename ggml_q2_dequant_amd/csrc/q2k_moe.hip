@@ -67,6 +67,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const uint32_t *__r
     __shared__ uint32_t next[kMoeMaxExperts];             // per expert: count, then next free row
     __shared__ uint32_t first_row[kMoeMaxExperts + 1];
     __shared__ uint32_t first_tile[kMoeMaxExperts + 1];
+    __shared__ uint32_t first_part[kMoeMaxExperts + 1];
     __shared__ uint32_t group[kRouteWaves][kMoeMaxExperts];  // (round tag << 16) | lanes of that expert
     __shared__ uint32_t wsum[kRouteWaves];
     __shared__ uint32_t nbad, bad_next;
@@ -89,33 +90,50 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const uint32_t *__r
     const uint32_t c = tid < n_experts ? next[tid] : 0u;
     uint32_t n_valid, n_tiles;
     const uint32_t row = block_exclusive_scan(c, wsum, &n_valid);
-    const uint32_t tile = block_exclusive_scan((c + kMoeTileRows - 1) / kMoeTileRows, wsum, &n_tiles);
+    // Tiles: every expert's full tiles first (expert-major), then the partial
+    // tiles, so the short ones run last.
+    uint32_t n_full, n_part;
+    const uint32_t full = c / kMoeTileRows, part = c % kMoeTileRows;
+    const uint32_t tile_f = block_exclusive_scan(full, wsum, &n_full);
+    const uint32_t tile_p = block_exclusive_scan(part != 0u ? 1u : 0u, wsum, &n_part);
+    n_tiles = n_full + n_part;
     if (tid < n_experts) {
         first_row[tid] = row;
-        first_tile[tid] = tile;
+        first_tile[tid] = tile_f;
+        first_part[tid] = tile_p;
         next[tid] = row;
     }
     if (tid == 0) {
         first_row[n_experts] = n_valid;
-        first_tile[n_experts] = n_tiles;
+        first_tile[n_experts] = n_full;
+        first_part[n_experts] = n_part;
     }
     __syncthreads();
 
-    // Tile list: tile t belongs to the expert e with first_tile[e] <= t < first_tile[e + 1].
+    // Tile t < n_full: full tile t - first_tile[e] of the expert e with
+    // first_tile[e] <= t < first_tile[e + 1]; tile n_full + u: the partial tile of
+    // the expert e with first_part[e] <= u < first_part[e + 1].
     for (uint32_t t = tid; t < tiles_max; t += kRouteThreads) {
         MoeTile mt{0u, 0u, 0u};
         if (t < n_tiles) {
-            uint32_t lo = 0, hi = n_experts;  // first_tile[lo] <= t < first_tile[hi]
+            const bool is_full = t < n_full;
+            const uint32_t *first = is_full ? first_tile : first_part;
+            const uint32_t key = is_full ? t : t - n_full;
+            uint32_t lo = 0, hi = n_experts;  // first[lo] <= key < first[hi]
             while (hi - lo > 1) {
                 const uint32_t mid = (lo + hi) / 2;
-                if (first_tile[mid] <= t) lo = mid;
+                if (first[mid] <= key) lo = mid;
                 else hi = mid;
             }
-            const uint32_t j = t - first_tile[lo];
-            const uint32_t rest = first_row[lo + 1] - first_row[lo] - j * kMoeTileRows;
+            const uint32_t cnt = first_row[lo + 1] - first_row[lo];
             mt.expert = lo;
-            mt.p0 = first_row[lo] + j * kMoeTileRows;
-            mt.count = rest < kMoeTileRows ? rest : kMoeTileRows;
+            if (is_full) {
+                mt.p0 = first_row[lo] + (key - first_tile[lo]) * kMoeTileRows;
+                mt.count = kMoeTileRows;
+            } else {
+                mt.p0 = first_row[lo] + cnt / kMoeTileRows * kMoeTileRows;
+                mt.count = cnt % kMoeTileRows;
+            }
         }
         s.tiles[t] = mt;
     }
