@@ -300,6 +300,26 @@ def test_slotted_on_seeded_routing_equals_flattened_and_oracle():
     check_mfma(ys, x, w, ids, slot.p, slotted=True)
 
 
+def test_matrix_core_tiles_with_exact_multiples_and_partial_only_experts():
+    # Expert 0 fills exactly two 128-row tiles, expert 1 is empty, experts 2
+    # and 3 have only partial tiles: the tile list holds the full tiles first
+    # and the partial ones after them.
+    tokens, top_k, experts, n, K = 200, 2, 4, 136, 512
+    rng = np.random.Generator(np.random.PCG64(91))
+    rb = (K // QK_K) * BB
+    w = synth.random_blocks(rng, experts * n * K // QK_K)
+    x = rng.standard_normal((tokens, K)).astype(np.float32)
+    ids = np.array([0] * 256 + [2] * 100 + [3] * 44, dtype=np.uint32)
+    rng.shuffle(ids)
+    p = params(tokens, top_k, n, K, experts, n * rb)
+    run = Run(x, w, ids, p)
+    y = run.plain(q2k.PATH_MFMA)
+    check_mfma(y, x, w, ids, p)
+    assert run.flagged() == 0
+    assert bits_equal(y, run.pooled())
+    check_routes_match_dense(y, x, w, ids, p, q2k.PATH_MFMA)
+
+
 def test_single_token_and_single_expert_edges():
     for tokens, top_k, experts in ((1, 1, 1), (1, 6, 8), (33, 1, 1)):
         x, w, ids, p = _random(81 + tokens + top_k, tokens, top_k, experts, 40, 256)
