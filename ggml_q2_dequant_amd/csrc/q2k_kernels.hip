@@ -535,11 +535,10 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const float *__restrict__ x,
             // Loads complete in issue order: the activation rows are in once at
             // most the 4 kMvTiles weight loads issued after them are in flight,
             // so the scaling below overlaps the weights' memory latency.
-            constexpr uint32_t kAfter = 4 * kMvTiles;
-            __builtin_amdgcn_s_waitcnt(static_cast<int>((kAfter & 15u) | ((kAfter >> 4) << 14) | 0x0F70u));
+            vm_wait<4 * kMvTiles>();
         } else {
             // The weight loads depend on the plan here, so wait for all of them.
-            __builtin_amdgcn_s_waitcnt(0x0F70);
+            vm_wait<0>();
         }
         __builtin_amdgcn_sched_barrier(0);
 
