@@ -10,7 +10,9 @@
 //   1. k_moe_route (one workgroup) counts the routes of every expert, orders
 //      them by expert with a stable counting sort (routes of one expert keep
 //      increasing r, so the order depends on ids alone) and lists the tiles:
-//      runs of at most 128 consecutive rows of one expert.
+//      runs of at most 128 consecutive rows of one expert, every expert's full
+//      128-row tiles first and the partial tiles after them (the GEMM takes
+//      them in list order, so the short tiles run last).
 //   2. k_moe_gather rounds each route's activation row to bf16 (nearest even)
 //      into its row of the expert order, and fills the output rows of routes
 //      whose id is out of range (listed after the valid rows of perm) with NaN.
