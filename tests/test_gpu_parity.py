@@ -316,6 +316,20 @@ def test_gemv_rows_do_not_depend_on_other_rows():
         assert bits_equal(gpu_matmul(inp.x[3 + m:4 + m], inp.blocks, 1, c.N, c.K), y2[m:m + 1])
 
 
+@pytest.mark.parametrize("M,path", [(1, q2k.PATH_GEMV), (2, q2k.PATH_GEMV), (8, q2k.PATH_GEMV), (9, q2k.PATH_MFMA)])
+def test_largest_k_every_path(M, path):
+    # K at the library's limit (2^21, 8192 blocks a row): the longest walks
+    # over K and the largest per-workgroup offsets any call can reach, on a
+    # ragged N.
+    K, N = 1 << 21, 17
+    rng = np.random.Generator(np.random.PCG64(2100 + M))
+    blocks = synth.random_blocks(rng, N * K // QK_K)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    y = gpu_matmul(x, blocks, M, N, K, path)
+    worst = (check_gemv if path == q2k.PATH_GEMV else check_mfma)(y, x, blocks, M, N, K)
+    print("K = 2^21, M=%d: max |y - y_ref| / A = %.3g" % (M, worst))
+
+
 def test_gemv_one_hot_returns_weights_bitwise():
     rng = np.random.Generator(np.random.PCG64(35))
     N, K = 40, 1024
