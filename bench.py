@@ -30,6 +30,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import csv
 import hashlib
 import json
@@ -49,6 +50,9 @@ COLD_BYTES = 512 << 20          # rotate replicas over at least this many bytes
 COPY_BYTES = 256 << 20          # size of the calibration copy
 KERNEL_SRC = os.path.join(ROOT, "ggml_q2_dequant_amd", "csrc", "q2k_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PROBE_LIB = os.path.join(ROOT, "ggml_q2_dequant_amd", "libq2k_probe.so")
+PROBE_GRIDS = (256, 512, 1024, 2048, 4096, 8192, 16384)
+PROBE_UNROLLS = (1, 2, 4, 8, 16)
 GEMV_KERNEL = "k_gemv_seg<1"    # name prefix of the M = 1 GEMV kernel in rocprofv3 output
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 ROWS = ("gemv1", "dequant", "gather", "gemv8", "mfma", "mfma_context", "batched", "sample", "moe_decode",
@@ -75,6 +79,25 @@ def measured_traffic(kernel: str):
     if not ent or ent.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+_probe = None
+
+
+def load_probe():
+    """libq2k_probe.so: the plain-read kernel timed beside the path (a measurement aid, not the C ABI)."""
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError("libq2k_probe.so is not built; run `python -m ggml_q2_dequant_amd.build`")
+        lib = ctypes.CDLL(PROBE_LIB)
+        P, U32, SZ = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_size_t
+        lib.q2k_probe_read.argtypes = [P, SZ, P, SZ, U32, U32, P]
+        lib.q2k_probe_read.restype = ctypes.c_int
+        lib.q2k_probe_default_grid.argtypes = [SZ, U32]
+        lib.q2k_probe_default_grid.restype = U32
+        _probe = lib
+    return _probe
 
 
 def time_launches(torch, launch, n: int, warmup: int):
@@ -238,16 +261,48 @@ class Bench:
         g["make_step"] = make_step
         return make_step(self.stream)
 
-    def read_ceiling(self, replicas, n=200):
-        """Plain streaming read of the same cold replicas (q2k_read_probe): the bandwidth a transfer of this size
-        can reach at all."""
+    def read_ceiling(self, replicas, n=200, sweep=False):
+        """Plain streaming read of the same cold replicas (libq2k_probe): the bandwidth a transfer of this size
+        can reach at all. The default shape is the GEMV's (a few hundred 256-thread workgroups, four 16-byte
+        loads per thread); with sweep=True every workgroup count x loads-per-thread pair that covers the bytes
+        is timed, and a device-to-device copy of the same bytes (it also writes them) is timed beside it; the
+        fastest read shape is the ceiling reported."""
         torch = self.torch
-        sink = torch.empty(self.q2k.READ_PROBE_SINK_WORDS, dtype=torch.int32, device=self.dev)
+        probe = load_probe()
+        sink = torch.empty(max(PROBE_GRIDS), dtype=torch.int32, device=self.dev)
         views = [r[: r.numel() // 16 * 16] for r in replicas]
-        t = time_launches(torch, lambda i: self.q2k.q2k_read_probe(views[i % len(views)], sink, stream=self.stream),
-                          n, 20)
         b = views[0].numel()
-        return {"bytes": b, "us": t * 1e6, "GB/s": b / t / 1e9}
+        st = self.stream
+
+        def timed(grid, unroll):
+            def launch(i):
+                rc = probe.q2k_probe_read(views[i % len(views)].data_ptr(), b, sink.data_ptr(), sink.numel(), grid,
+                                          unroll, st)
+                if rc:
+                    raise RuntimeError("q2k_probe_read rejected its arguments (%d)" % rc)
+            return time_launches(torch, launch, n, 20)
+
+        t = timed(0, 4)
+        out = {"bytes": b, "us": t * 1e6, "GB/s": b / t / 1e9,
+               "shape": {"grid": int(probe.q2k_probe_default_grid(b, 4)), "loads_per_thread": 4}}
+        if not sweep:
+            return out
+        shapes = []
+        for grid in PROBE_GRIDS:
+            for unroll in PROBE_UNROLLS:
+                if grid * 256 * unroll * 16 > 4 * b and unroll > 1:
+                    continue  # more loads in flight than the buffer holds: same as a smaller unroll
+                ts = timed(grid, unroll)
+                shapes.append({"grid": grid, "loads_per_thread": unroll, "us": round(ts * 1e6, 3),
+                               "GB/s": round(b / ts / 1e9, 1)})
+        best = min(shapes, key=lambda e: e["us"])
+        dst = torch.empty_like(views[0])
+        tc = time_launches(torch, lambda i: dst.copy_(views[i % len(views)]), n, 20)
+        out.update(sweep=shapes, best={"grid": best["grid"], "loads_per_thread": best["loads_per_thread"],
+                                       "us": best["us"], "GB/s": best["GB/s"]},
+                   d2d_copy={"us": round(tc * 1e6, 3), "read_GB/s": round(b / tc / 1e9, 1),
+                             "note": "hipMemcpyAsync device to device of the same bytes (reads and writes them)"})
+        return out
 
     def write_ceiling(self, outs, n=200):
         """torch's own fill kernel over the same output buffers: the bandwidth a plain write of this size reaches."""
@@ -317,7 +372,7 @@ class Bench:
         return {"workload": "M=8 N=14336 K=4096 (%d cold weight replicas)" % reps, "us": t * 1e6,
                 "algorithmic_bytes": b, "flop": f, "GB/s": b / t / 1e9, "TFLOP/s": f / t / 1e12,
                 "bound": "hbm", "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
-                "frac_fp32": f / t / 1e12 / FP32_PEAK_TFLOPS, "read_ceiling": self.read_ceiling(wr)}
+                "frac_fp32": f / t / 1e12 / FP32_PEAK_TFLOPS, "read_ceiling": self.read_ceiling(wr, 100, sweep=True)}
 
     def mfma(self, n=400):
         torch = self.torch
@@ -389,7 +444,7 @@ class Bench:
         log("batched mat-vec 8 x (M=1, N=K=4096): %.2f us, %.1f GB/s" % (t * 1e6, b / t / 1e9))
         return {"workload": "8 matrices x (M=1, N=K=4096) in one call, %d cold weight replicas" % reps,
                 "us": t * 1e6, "algorithmic_bytes": b, "GB/s": b / t / 1e9, "bound": "hbm",
-                "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS, "read_ceiling": self.read_ceiling(wr)}
+                "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS, "read_ceiling": self.read_ceiling(wr, 100, sweep=True)}
 
     def sample(self, n=200):
         """First-max argmax + threshold candidates over 8 slots x 262144 logits (cap 64)."""
@@ -557,9 +612,12 @@ def main() -> int:
     # Per-call spread (runs of 20 calls) and graph replay of the same launches, after the timed region.
     dist = time_blocks(torch, step, 50, 20)
     graph_s = time_graph(torch, g["make_step"], min(args.steps, 500))
-    ceiling = b.read_ceiling(g["replicas"])
-    log("GEMV M=1 per call p10/p50/p90 %.2f/%.2f/%.2f us, graph %.2f us; read ceiling %.2f us (%.0f GB/s)" % (
-        dist["p10"] * 1e6, dist["p50"] * 1e6, dist["p90"] * 1e6, graph_s * 1e6, ceiling["us"], ceiling["GB/s"]))
+    ceiling = b.read_ceiling(g["replicas"], sweep=True)
+    log("GEMV M=1 per call p10/p50/p90 %.2f/%.2f/%.2f us, graph %.2f us; read ceiling %.2f us (%.0f GB/s), best "
+        "read shape %s: %.2f us; d2d copy %.2f us" % (
+            dist["p10"] * 1e6, dist["p50"] * 1e6, dist["p90"] * 1e6, graph_s * 1e6, ceiling["us"], ceiling["GB/s"],
+            (ceiling["best"]["grid"], ceiling["best"]["loads_per_thread"]), ceiling["best"]["us"],
+            ceiling["d2d_copy"]["us"]))
 
     rows = {}
     if not args.no_rows:

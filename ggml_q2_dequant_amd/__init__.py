@@ -9,7 +9,9 @@ Functions carry the C names:
 
 * ``q2k_dequantize(blocks, out)`` — decode whole 84-byte blocks to f32.
 * ``q2k_matmul(x, w, y, M, N, K)`` — y[M, N] = x[M, K] * W[N, K]^T, W in Q2_K.
-* ``q2k_matmul_path(x, w, y, M, N, K, path)`` — same with a forced kernel.
+* ``q2k_matmul_path(x, w, y, M, N, K, path)`` — same with a forced kernel;
+  ``q2k_matmul_pooled`` takes caller-held scratch of ``q2k_matmul_scratch_bytes``
+  bytes instead of the library's per-stream workspace.
 * ``q2k_matmul_batched(x, w, y, batches, M, N, K)`` — independent products, one
   per matrix of a batch-major stack (1 <= M <= 8).
 * ``q2k_embedding_gather(table, ids, out, vocab, embed_dim, n_tokens)`` — rows
@@ -18,7 +20,7 @@ Functions carry the C names:
   status)`` — the same without waiting; a bad id sets the device int ``status``.
 * ``q2k_argmax_candidates(logits, n_slots, vocab, cap, top1_idx, top1_val,
   cand_count, overflow, cand_ids)`` — first-max argmax and the logits within
-  0.5 of it, per slot.
+  0.5 of it, per slot; ``q2k_argmax_candidates_pooled`` with caller-held scratch.
 * ``q2k_matmul_id(x, w, ids, y, params, status=None)`` — the expert-routed
   product (route token*top_k+slot uses expert ids[route]); ``q2k_matmul_id_path``
   forces a schedule; ``q2k_matmul_id_pooled``, ``..._pooled_pair`` and
@@ -59,17 +61,20 @@ EXPORTS = (
     "q2k_dequantize",
     "q2k_matmul",
     "q2k_matmul_path",
+    "q2k_matmul_scratch_bytes",
+    "q2k_matmul_pooled",
     "q2k_matmul_batched",
     "q2k_embedding_gather",
     "q2k_embedding_gather_async",
     "q2k_argmax_candidates",
+    "q2k_argmax_candidates_scratch_bytes",
+    "q2k_argmax_candidates_pooled",
     "q2k_matmul_id",
     "q2k_matmul_id_path",
     "q2k_matmul_id_scratch_bytes",
     "q2k_matmul_id_pooled",
     "q2k_matmul_id_pooled_pair",
     "q2k_matmul_id_pooled_slotted",
-    "q2k_read_probe",
     "q2k_gguf_open",
     "q2k_gguf_close",
     "q2k_gguf_tensor_count",
@@ -145,8 +150,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).restype = ctypes.c_int
     lib.q2k_argmax_candidates.argtypes = [P, U32, U32, U32, P, P, P, P, P, P]
     lib.q2k_argmax_candidates.restype = ctypes.c_int
-    lib.q2k_read_probe.argtypes = [P, SZ, P, SZ, P]
-    lib.q2k_read_probe.restype = ctypes.c_int
+    U64, PU64 = ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)
+    lib.q2k_matmul_scratch_bytes.argtypes = [U32, U32, U32, ctypes.c_int, PU64]
+    lib.q2k_matmul_pooled.argtypes = [P, P, P, U32, U32, U32, ctypes.c_int, P, U64, P]
+    lib.q2k_argmax_candidates_scratch_bytes.argtypes = [U32, U32, PU64]
+    lib.q2k_argmax_candidates_pooled.argtypes = [P, U32, U32, U32, P, P, P, P, P, P, U64, P]
+    for name in ("q2k_matmul_scratch_bytes", "q2k_matmul_pooled", "q2k_argmax_candidates_scratch_bytes",
+                 "q2k_argmax_candidates_pooled"):
+        getattr(lib, name).restype = ctypes.c_int
     PP = ctypes.POINTER(MatmulIdParams)
     lib.q2k_matmul_id.argtypes = [P, P, P, P, PP, P, P]
     lib.q2k_matmul_id_path.argtypes = [P, P, P, P, PP, P, ctypes.c_int, P]
@@ -233,6 +244,21 @@ def q2k_matmul_path(x, w, y, M: int, N: int, K: int, path: int, stream=None) -> 
     _check(load_library().q2k_matmul_path(_ptr(x), _ptr(w), _ptr(y), M, N, K, int(path), _stream(stream)))
 
 
+def q2k_matmul_scratch_bytes(M: int, N: int, K: int, path: int = PATH_AUTO) -> int:
+    """Device scratch bytes q2k_matmul_pooled needs (0 for the GEMV path)."""
+    n = ctypes.c_uint64()
+    _check(load_library().q2k_matmul_scratch_bytes(M, N, K, int(path), ctypes.byref(n)))
+    return int(n.value)
+
+
+def q2k_matmul_pooled(x, w, y, M: int, N: int, K: int, scratch, path: int = PATH_AUTO, stream=None,
+                      scratch_bytes: int | None = None) -> None:
+    """q2k_matmul_path with caller-held scratch (a device tensor, or None when the path needs none)."""
+    nb = (0 if scratch is None else _nbytes(scratch)) if scratch_bytes is None else int(scratch_bytes)
+    _check(load_library().q2k_matmul_pooled(_ptr(x), _ptr(w), _ptr(y), M, N, K, int(path), _ptr(scratch), nb,
+                                            _stream(stream)))
+
+
 def q2k_matmul_batched(x, w, y, batches: int, M: int, N: int, K: int, stream=None) -> None:
     """y[b] = x[b] * W[b]^T for each of ``batches`` stacked problems (1 <= M <= 8)."""
     _check(load_library().q2k_matmul_batched(_ptr(x), _ptr(w), _ptr(y), batches, M, N, K, _stream(stream)))
@@ -256,6 +282,22 @@ def q2k_argmax_candidates(logits, n_slots: int, vocab: int, cap: int, top1_idx, 
     """Per slot: first-max index/value, candidate count (may exceed cap), overflow flag, candidate ids."""
     _check(load_library().q2k_argmax_candidates(_ptr(logits), n_slots, vocab, cap, _ptr(top1_idx), _ptr(top1_val),
                                                 _ptr(cand_count), _ptr(overflow), _ptr(cand_ids), _stream(stream)))
+
+
+def q2k_argmax_candidates_scratch_bytes(n_slots: int, vocab: int) -> int:
+    """Device scratch bytes q2k_argmax_candidates_pooled needs."""
+    n = ctypes.c_uint64()
+    _check(load_library().q2k_argmax_candidates_scratch_bytes(n_slots, vocab, ctypes.byref(n)))
+    return int(n.value)
+
+
+def q2k_argmax_candidates_pooled(logits, n_slots: int, vocab: int, cap: int, top1_idx, top1_val, cand_count,
+                                 overflow, cand_ids, scratch, stream=None, scratch_bytes: int | None = None) -> None:
+    """q2k_argmax_candidates with caller-held scratch (a device tensor)."""
+    nb = _nbytes(scratch) if scratch_bytes is None else int(scratch_bytes)
+    _check(load_library().q2k_argmax_candidates_pooled(_ptr(logits), n_slots, vocab, cap, _ptr(top1_idx),
+                                                       _ptr(top1_val), _ptr(cand_count), _ptr(overflow),
+                                                       _ptr(cand_ids), _ptr(scratch), nb, _stream(stream)))
 
 
 def q2k_matmul_id(x, w, ids, y, params, status=None, stream=None) -> None:
@@ -303,14 +345,6 @@ def q2k_matmul_id_pooled_slotted(x, w, ids, y, params, scratch, status=None, str
     nb = _nbytes(scratch) if scratch_bytes is None else int(scratch_bytes)
     _check(load_library().q2k_matmul_id_pooled_slotted(_ptr(x), _ptr(w), _ptr(ids), _ptr(y), ctypes.byref(p),
                                                        _ptr(scratch), nb, _ptr(status), _stream(stream)))
-
-
-READ_PROBE_SINK_WORDS = 2048
-
-
-def q2k_read_probe(data, sink, stream=None) -> None:
-    """Measurement aid: read ``data`` (a device tensor, 16-byte multiple) once; one word per workgroup to sink."""
-    _check(load_library().q2k_read_probe(_ptr(data), _nbytes(data), _ptr(sink), sink.numel(), _stream(stream)))
 
 
 class GGUFFile:

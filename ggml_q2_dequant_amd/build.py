@@ -1,8 +1,10 @@
 """Build step for libq2k.so: hipcc for gfx950, in-tree.
 
-Produces ``ggml_q2_dequant_amd/libq2k.so`` from ``csrc/q2k_kernels.hip`` and
-``csrc/q2k_api.cpp`` and ``csrc/q2k_gguf.cpp`` with the public header in ``include/``. Run
-``python -m ggml_q2_dequant_amd.build`` (or ``__graft_entry__.build()``).
+Produces ``ggml_q2_dequant_amd/libq2k.so`` (the library behind ``include/q2k.h``)
+from the HIP and C++ sources in ``csrc/``, and ``libq2k_probe.so``, the
+plain-read measurement kernel the benchmark times beside the path (not part of
+the C ABI). Run ``python -m ggml_q2_dequant_amd.build`` (or
+``__graft_entry__.build()``).
 """
 from __future__ import annotations
 
@@ -15,7 +17,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libq2k.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("q2k_kernels.hip", "q2k_sample.hip", "q2k_moe.hip", "q2k_probe.hip", "q2k_api.cpp", "q2k_gguf.cpp")]
+SOURCES = [os.path.join(CSRC, n) for n in ("q2k_kernels.hip", "q2k_sample.hip", "q2k_moe.hip", "q2k_api.cpp", "q2k_gguf.cpp")]
+PROBE_LIB = os.path.join(PKG, "libq2k_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "q2k_probe.hip")]
 ARCH = os.environ.get("Q2K_OFFLOAD_ARCH", "gfx950")
 
 # -ffp-contract=off: only FMAs written as such are fused, so every kernel's
@@ -36,9 +40,9 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I" + INCLUDE, "-I" + CSRC, *SOURCES, "-o", tmp]
+def _compile(sources, out, verbose: bool) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I" + INCLUDE, "-I" + CSRC, *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,8 +51,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, "\n".join(msgs)))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libq2k.so and the measurement library; returns the path of libq2k.so."""
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

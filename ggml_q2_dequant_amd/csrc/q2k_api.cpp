@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -136,38 +137,78 @@ q2k_status status_word(StatusWord **out) {
     return Q2K_OK;
 }
 
-// The matrix-core path (bf16(x)) and the argmax/candidate call (per-chunk
-// partials) stage data in a device workspace. One grow-only workspace is kept
-// per (device, stream) and used only inside one call; calls on one stream run
-// in order, so they can share it. Growth frees and reallocates it in stream
-// order, so work already queued on that stream keeps its buffer, and calls on
-// different streams never share one.
+// The matrix-core path (bf16(x)), the matrix-core expert-routed schedule
+// (routing tables and bf16 rows) and the argmax/candidate call (per-chunk
+// partials) stage data in device scratch. The *_pooled entry points take it
+// from the caller; the others use a workspace libq2k keeps per (device,
+// stream):
+//  - a call holds that workspace's lock from its size check until its
+//    launches are enqueued, so a call from another host thread on the same
+//    stream cannot replace the buffer between the two;
+//  - the workspace only grows, and a buffer that a larger request replaces is
+//    never freed: a HIP graph captured earlier may still hold its address.
+//    Retired buffers stay allocated until the process ends; growth at least
+//    doubles the size, so together they never exceed the live buffer;
+//  - growth is refused while the stream is capturing a graph (the allocation
+//    would not be part of the graph's own memory): one eager call of the
+//    largest size first, or the pooled form, avoids it.
 struct Workspace {
+    std::mutex mu;
     void *ptr = nullptr;
     size_t bytes = 0;
+    std::vector<void *> retired;
 };
 
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::mutex g_ws_mu;  // guards the map, not the workspaces
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<Workspace>> g_ws;
 
-q2k_status stream_workspace(hipStream_t st, size_t bytes, void **out) {
+// Calls launch(buffer) with the stream's workspace grown to at least `bytes`,
+// holding the workspace's lock until launch returns. launch returns a status.
+template <class F>
+q2k_status with_workspace(const char *fn, hipStream_t st, size_t bytes, F &&launch) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return device_error("hipGetDevice", e);
-    std::lock_guard<std::mutex> lock(g_ws_mu);
-    Workspace &w = g_ws[{dev, st}];
-    if (w.bytes < bytes) {
-        if (w.ptr) {
-            e = hipFreeAsync(w.ptr, st);
-            if (e != hipSuccess) return device_error("hipFreeAsync(workspace)", e);
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        e = hipMallocAsync(&w.ptr, bytes, st);
-        if (e != hipSuccess) return device_error("hipMallocAsync(workspace)", e);
-        w.bytes = bytes;
+    Workspace *w;
+    {
+        std::lock_guard<std::mutex> lock(g_ws_mu);
+        std::unique_ptr<Workspace> &slot = g_ws[{dev, st}];
+        if (!slot) slot.reset(new Workspace);
+        w = slot.get();
     }
-    *out = w.ptr;
+    std::lock_guard<std::mutex> lock(w->mu);
+    if (w->bytes < bytes) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(st, &cs);
+        if (e != hipSuccess) return device_error("hipStreamIsCapturing", e);
+        if (cs != hipStreamCaptureStatusNone)
+            return fail(Q2K_ERR_INVALID_ARGUMENT,
+                        "%s: the stream's workspace must grow to %zu bytes, which is not done during graph capture; "
+                        "make one call of this size before capturing, or pass scratch to the pooled form",
+                        fn, bytes);
+        const size_t want = bytes > 2 * w->bytes ? bytes : 2 * w->bytes;
+        void *p = nullptr;
+        e = hipMalloc(&p, want);
+        if (e != hipSuccess) return device_error("hipMalloc(workspace)", e);
+        if (w->ptr) w->retired.push_back(w->ptr);
+        w->ptr = p;
+        w->bytes = want;
+    }
+    return launch(w->ptr);
+}
+
+// Caller scratch: non-null, 256-byte aligned, at least `need` bytes, and
+// disjoint from every other argument.
+q2k_status check_caller_scratch(const char *fn, const void *scratch, uint64_t scratch_bytes, uint64_t need,
+                                const Range *args, int n_args) {
+    if (!scratch) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: null scratch", fn);
+    if (!aligned(scratch, 256)) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: scratch must be 256-byte aligned", fn);
+    if (scratch_bytes < need)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: scratch holds %llu bytes, %llu needed", fn,
+                    static_cast<unsigned long long>(scratch_bytes), static_cast<unsigned long long>(need));
+    for (int i = 0; i < n_args; ++i)
+        if (overlap(scratch, need, args[i].p, args[i].bytes))
+            return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: scratch overlaps another argument", fn);
     return Q2K_OK;
 }
 
@@ -257,16 +298,95 @@ q2k_status run_moe_mfma(const char *fn, const MoeShape &sh, const q2k_matmul_id_
 
 q2k_status check_scratch(const char *fn, const MoeShape &sh, const q2k_matmul_id_params *p, const void *scratch,
                          uint64_t scratch_bytes, const Range *args, int n_args) {
-    const uint64_t need = q2k::moe_scratch_bytes(sh.routes, p->n_experts, p->k);
-    if (!scratch) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: null scratch", fn);
-    if (!aligned(scratch, 256)) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: scratch must be 256-byte aligned", fn);
-    if (scratch_bytes < need)
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: scratch holds %llu bytes, %llu needed", fn,
-                    static_cast<unsigned long long>(scratch_bytes), static_cast<unsigned long long>(need));
-    for (int i = 0; i < n_args; ++i)
-        if (overlap(scratch, need, args[i].p, args[i].bytes))
-            return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: scratch overlaps another argument", fn);
+    return check_caller_scratch(fn, scratch, scratch_bytes, q2k::moe_scratch_bytes(sh.routes, p->n_experts, p->k), args,
+                                n_args);
+}
+
+// Kernel choice of a matmul call: Q2K_PATH_AUTO resolves to the fp32 GEMV for
+// M <= 8 and to the matrix cores above; the GEMV takes M <= 8 only.
+q2k_status resolve_path(const char *fn, uint32_t M, q2k_path *path) {
+    if (*path == Q2K_PATH_AUTO) *path = M <= q2k::kGemvMaxM ? Q2K_PATH_GEMV : Q2K_PATH_MFMA;
+    if (*path == Q2K_PATH_GEMV && M > q2k::kGemvMaxM)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: the GEMV path takes M <= 8 (got %u)", fn, M);
+    if (*path != Q2K_PATH_GEMV && *path != Q2K_PATH_MFMA)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: unknown path %d", fn, static_cast<int>(*path));
     return Q2K_OK;
+}
+
+// Scratch bytes of a resolved matmul path: bf16(x) for the matrix cores.
+uint64_t matmul_scratch(uint32_t M, uint32_t K, q2k_path path) {
+    return path == Q2K_PATH_MFMA ? 2ull * M * K : 0;
+}
+
+// Enqueues a validated matmul; scratch (for the matrix-core path) is caller
+// memory, or null for the stream's workspace.
+q2k_status run_matmul(const char *fn, const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
+                      q2k_path path, void *scratch, hipStream_t st) {
+    hipError_t e;
+    if (path == Q2K_PATH_GEMV) {
+        e = q2k::launch_gemv(x, w, y, M, N, K, 1, st);
+    } else if (scratch) {
+        e = q2k::launch_gemm_mfma(x, w, y, M, N, K, scratch, st);
+    } else {
+        e = hipSuccess;
+        const q2k_status s = with_workspace(fn, st, matmul_scratch(M, K, path), [&](void *ws) {
+            e = q2k::launch_gemm_mfma(x, w, y, M, N, K, ws, st);
+            return Q2K_OK;
+        });
+        if (s != Q2K_OK) return s;
+    }
+    if (e != hipSuccess) return device_error(fn, e);
+    return ok();
+}
+
+// Argument rules of the argmax/candidate calls.
+q2k_status check_argmax(const char *fn, const float *logits, uint32_t n_slots, uint32_t vocab, uint32_t cap,
+                        const uint32_t *top1_idx, const float *top1_val, const uint32_t *cand_count,
+                        const uint32_t *overflow, const uint32_t *cand_ids, Range *args) {
+    if (!logits || !top1_idx || !top1_val || !cand_count || !overflow || !cand_ids)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+    if (n_slots == 0 || vocab == 0 || cap == 0)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: n_slots, vocab, cap must all be > 0 (got %u, %u, %u)", fn, n_slots,
+                    vocab, cap);
+    if (vocab > q2k::kSampleMaxVocab)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: vocab=%u exceeds the limit %u", fn, vocab, q2k::kSampleMaxVocab);
+    uint64_t lb, cb, t;
+    if (!mul_ok(n_slots, vocab, &t) || !mul_ok(t, 4, &lb) || !mul_ok(n_slots, cap, &t) || !mul_ok(t, 4, &cb))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: size overflow", fn);
+    if (!aligned(logits, 4) || !aligned(top1_idx, 4) || !aligned(top1_val, 4) || !aligned(cand_count, 4) ||
+        !aligned(overflow, 4) || !aligned(cand_ids, 4))
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: every buffer must be 4-byte aligned", fn);
+    const Range outs[5] = {{top1_idx, 4ull * n_slots}, {top1_val, 4ull * n_slots}, {cand_count, 4ull * n_slots},
+                           {overflow, 4ull * n_slots}, {cand_ids, cb}};
+    for (int i = 0; i < 5; ++i) {
+        if (overlap(outs[i].p, outs[i].bytes, logits, lb))
+            return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: an output overlaps the logits", fn);
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
+                return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: outputs overlap each other", fn);
+    }
+    args[0] = {logits, lb};
+    for (int i = 0; i < 5; ++i) args[1 + i] = outs[i];
+    return Q2K_OK;
+}
+
+// Scratch of the argmax/candidate call: the per-chunk partials of the largest
+// launch (at most kMaxGridY slots; later launches of a call reuse it in order).
+uint64_t argmax_scratch(uint32_t n_slots, uint32_t vocab) {
+    return q2k::sample_workspace_bytes(n_slots < q2k::kMaxGridY ? n_slots : q2k::kMaxGridY, vocab);
+}
+
+hipError_t run_argmax(const float *logits, uint32_t n_slots, uint32_t vocab, uint32_t cap, uint32_t *top1_idx,
+                      float *top1_val, uint32_t *cand_count, uint32_t *overflow, uint32_t *cand_ids, void *ws,
+                      hipStream_t st) {
+    for (uint64_t s0 = 0; s0 < n_slots; s0 += q2k::kMaxGridY) {
+        const uint32_t ns = static_cast<uint32_t>(n_slots - s0 < q2k::kMaxGridY ? n_slots - s0 : q2k::kMaxGridY);
+        const hipError_t e = q2k::launch_argmax_candidates(logits + s0 * vocab, ns, vocab, cap, top1_idx + s0,
+                                                           top1_val + s0, cand_count + s0, overflow + s0,
+                                                           cand_ids + s0 * cap, ws, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -321,23 +441,40 @@ q2k_status q2k_matmul_path(const float *x, const void *w, float *y, uint32_t M, 
     Range rx, rw, ry;
     q2k_status s = check_matmul(x, w, y, M, N, K, &rx, &rw, &ry);
     if (s != Q2K_OK) return s;
-    if (path == Q2K_PATH_AUTO) path = M <= q2k::kGemvMaxM ? Q2K_PATH_GEMV : Q2K_PATH_MFMA;
-    hipError_t e;
-    const auto *wb = static_cast<const uint8_t *>(w);
-    const auto st = static_cast<hipStream_t>(stream);
-    if (path == Q2K_PATH_GEMV) {
-        if (M > q2k::kGemvMaxM) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul: the GEMV path takes M <= 8 (got %u)", M);
-        e = q2k::launch_gemv(x, wb, y, M, N, K, 1, st);
-    } else if (path == Q2K_PATH_MFMA) {
-        void *ws = nullptr;
-        s = stream_workspace(st, static_cast<size_t>(M) * K * 2, &ws);
-        if (s != Q2K_OK) return s;
-        e = q2k::launch_gemm_mfma(x, wb, y, M, N, K, ws, st);
-    } else {
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul: unknown path %d", static_cast<int>(path));
-    }
-    if (e != hipSuccess) return device_error("q2k_matmul launch", e);
+    if ((s = resolve_path("q2k_matmul", M, &path)) != Q2K_OK) return s;
+    return run_matmul("q2k_matmul", x, static_cast<const uint8_t *>(w), y, M, N, K, path, nullptr,
+                      static_cast<hipStream_t>(stream));
+}
+
+q2k_status q2k_matmul_scratch_bytes(uint32_t M, uint32_t N, uint32_t K, q2k_path path, uint64_t *bytes) {
+    if (!bytes) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul_scratch_bytes: null pointer");
+    if (M == 0 || N == 0 || K == 0)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul_scratch_bytes: M, N, K must be >= 1 (got %u, %u, %u)", M, N, K);
+    if (K % q2k::kQK != 0 || K > q2k::kMaxK)
+        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_matmul_scratch_bytes: K=%u is not a multiple of 256 in 256..%u", K,
+                    q2k::kMaxK);
+    q2k_status s = resolve_path("q2k_matmul_scratch_bytes", M, &path);
+    if (s != Q2K_OK) return s;
+    *bytes = matmul_scratch(M, K, path);
     return ok();
+}
+
+q2k_status q2k_matmul_pooled(const float *x, const void *w, float *y, uint32_t M, uint32_t N, uint32_t K,
+                             q2k_path path, void *scratch, uint64_t scratch_bytes, void *stream) {
+    static const char fn[] = "q2k_matmul_pooled";
+    Range rx, rw, ry;
+    q2k_status s = check_matmul(x, w, y, M, N, K, &rx, &rw, &ry);
+    if (s != Q2K_OK) return s;
+    if ((s = resolve_path(fn, M, &path)) != Q2K_OK) return s;
+    const uint64_t need = matmul_scratch(M, K, path);
+    if (need == 0) {
+        scratch = nullptr;
+    } else {
+        const Range args[3] = {rx, rw, ry};
+        if ((s = check_caller_scratch(fn, scratch, scratch_bytes, need, args, 3)) != Q2K_OK) return s;
+    }
+    return run_matmul(fn, x, static_cast<const uint8_t *>(w), y, M, N, K, path, scratch,
+                      static_cast<hipStream_t>(stream));
 }
 
 q2k_status q2k_matmul(const float *x, const void *w, float *y, uint32_t M, uint32_t N, uint32_t K, void *stream) {
@@ -378,39 +515,45 @@ q2k_status q2k_matmul_batched(const float *x, const void *w, float *y, uint32_t 
 q2k_status q2k_argmax_candidates(const float *logits, uint32_t n_slots, uint32_t vocab, uint32_t cap,
                                  uint32_t *top1_idx, float *top1_val, uint32_t *cand_count, uint32_t *overflow,
                                  uint32_t *cand_ids, void *stream) {
-    if (!logits || !top1_idx || !top1_val || !cand_count || !overflow || !cand_ids)
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: null pointer");
-    if (n_slots == 0 || vocab == 0 || cap == 0)
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: n_slots, vocab, cap must all be > 0 (got %u, %u, %u)",
-                    n_slots, vocab, cap);
-    if (vocab > q2k::kSampleMaxVocab)
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: vocab=%u exceeds the limit %u", vocab,
-                    q2k::kSampleMaxVocab);
-    uint64_t lb, cb, t;
-    if (!mul_ok(n_slots, vocab, &t) || !mul_ok(t, 4, &lb) || !mul_ok(n_slots, cap, &t) || !mul_ok(t, 4, &cb))
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: size overflow");
-    if (!aligned(logits, 4) || !aligned(top1_idx, 4) || !aligned(top1_val, 4) || !aligned(cand_count, 4) ||
-        !aligned(overflow, 4) || !aligned(cand_ids, 4))
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: every buffer must be 4-byte aligned");
-    const Range outs[5] = {{top1_idx, 4ull * n_slots}, {top1_val, 4ull * n_slots}, {cand_count, 4ull * n_slots},
-                           {overflow, 4ull * n_slots}, {cand_ids, cb}};
-    for (int i = 0; i < 5; ++i) {
-        if (overlap(outs[i].p, outs[i].bytes, logits, lb))
-            return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: an output overlaps the logits");
-        for (int j = 0; j < i; ++j)
-            if (overlap(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
-                return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates: outputs overlap each other");
-    }
+    static const char fn[] = "q2k_argmax_candidates";
+    Range args[6];
+    q2k_status s = check_argmax(fn, logits, n_slots, vocab, cap, top1_idx, top1_val, cand_count, overflow, cand_ids,
+                                args);
+    if (s != Q2K_OK) return s;
     const auto st = static_cast<hipStream_t>(stream);
-    for (uint64_t s0 = 0; s0 < n_slots; s0 += q2k::kMaxGridY) {
-        const uint32_t ns = static_cast<uint32_t>(n_slots - s0 < q2k::kMaxGridY ? n_slots - s0 : q2k::kMaxGridY);
-        void *ws = nullptr;
-        q2k_status s = stream_workspace(st, q2k::sample_workspace_bytes(ns, vocab), &ws);
-        if (s != Q2K_OK) return s;
-        hipError_t e = q2k::launch_argmax_candidates(logits + s0 * vocab, ns, vocab, cap, top1_idx + s0, top1_val + s0,
-                                                     cand_count + s0, overflow + s0, cand_ids + s0 * cap, ws, st);
-        if (e != hipSuccess) return device_error("q2k_argmax_candidates launch", e);
-    }
+    hipError_t e = hipSuccess;
+    s = with_workspace(fn, st, argmax_scratch(n_slots, vocab), [&](void *ws) {
+        e = run_argmax(logits, n_slots, vocab, cap, top1_idx, top1_val, cand_count, overflow, cand_ids, ws, st);
+        return Q2K_OK;
+    });
+    if (s != Q2K_OK) return s;
+    if (e != hipSuccess) return device_error(fn, e);
+    return ok();
+}
+
+q2k_status q2k_argmax_candidates_scratch_bytes(uint32_t n_slots, uint32_t vocab, uint64_t *bytes) {
+    if (!bytes) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_argmax_candidates_scratch_bytes: null pointer");
+    if (n_slots == 0 || vocab == 0 || vocab > q2k::kSampleMaxVocab)
+        return fail(Q2K_ERR_INVALID_ARGUMENT,
+                    "q2k_argmax_candidates_scratch_bytes: need n_slots >= 1 and 1 <= vocab <= %u (got %u, %u)",
+                    q2k::kSampleMaxVocab, n_slots, vocab);
+    *bytes = argmax_scratch(n_slots, vocab);
+    return ok();
+}
+
+q2k_status q2k_argmax_candidates_pooled(const float *logits, uint32_t n_slots, uint32_t vocab, uint32_t cap,
+                                        uint32_t *top1_idx, float *top1_val, uint32_t *cand_count, uint32_t *overflow,
+                                        uint32_t *cand_ids, void *scratch, uint64_t scratch_bytes, void *stream) {
+    static const char fn[] = "q2k_argmax_candidates_pooled";
+    Range args[6];
+    q2k_status s = check_argmax(fn, logits, n_slots, vocab, cap, top1_idx, top1_val, cand_count, overflow, cand_ids,
+                                args);
+    if (s != Q2K_OK) return s;
+    if ((s = check_caller_scratch(fn, scratch, scratch_bytes, argmax_scratch(n_slots, vocab), args, 6)) != Q2K_OK)
+        return s;
+    const hipError_t e = run_argmax(logits, n_slots, vocab, cap, top1_idx, top1_val, cand_count, overflow, cand_ids,
+                                    scratch, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_error(fn, e);
     return ok();
 }
 
@@ -432,10 +575,9 @@ q2k_status q2k_matmul_id_path(const float *x, const void *w, const uint32_t *ids
         return ok();
     }
     if (path != Q2K_PATH_MFMA) return fail(Q2K_ERR_INVALID_ARGUMENT, "%s: unknown path %d", fn, static_cast<int>(path));
-    void *ws = nullptr;
-    s = stream_workspace(st, q2k::moe_scratch_bytes(sh.routes, p->n_experts, p->k), &ws);
-    if (s != Q2K_OK) return s;
-    return run_moe_mfma(fn, sh, p, w, nullptr, y, nullptr, ws, status, st);
+    return with_workspace(fn, st, q2k::moe_scratch_bytes(sh.routes, p->n_experts, p->k), [&](void *ws) {
+        return run_moe_mfma(fn, sh, p, w, nullptr, y, nullptr, ws, status, st);
+    });
 }
 
 q2k_status q2k_matmul_id(const float *x, const void *w, const uint32_t *ids, float *y,
@@ -493,22 +635,6 @@ q2k_status q2k_matmul_id_pooled_slotted(const float *x, const void *w, const uin
     const Range args2[5] = {sh.x, sh.w, sh.ids, sh.y, {scratch, scratch_bytes}};
     if ((s = check_status_word(fn, status, args2, 5)) != Q2K_OK) return s;
     return run_moe_mfma(fn, sh, p, w, nullptr, y, nullptr, scratch, status, static_cast<hipStream_t>(stream));
-}
-
-q2k_status q2k_read_probe(const void *data, size_t bytes, uint32_t *sink, size_t sink_elems, void *stream) {
-    if (!data || !sink) return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_read_probe: null pointer");
-    if (bytes == 0 || bytes % 16 != 0)
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_read_probe: %zu bytes is not a positive multiple of 16", bytes);
-    if (sink_elems < q2k::kReadProbeMaxGrid)
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_read_probe: sink holds %zu words, %u needed", sink_elems,
-                    q2k::kReadProbeMaxGrid);
-    if (!aligned(data, 16) || !aligned(sink, 4))
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_read_probe: data must be 16-byte aligned, sink 4-byte aligned");
-    if (overlap(sink, 4ull * sink_elems, data, bytes))
-        return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_read_probe: sink overlaps data");
-    hipError_t e = q2k::launch_read_probe(data, bytes, sink, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return device_error("q2k_read_probe launch", e);
-    return ok();
 }
 
 q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *out, uint32_t vocab,

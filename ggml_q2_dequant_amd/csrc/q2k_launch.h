@@ -81,10 +81,4 @@ hipError_t launch_moe_gather(const float *x, uint32_t routes, uint32_t x_div, ui
 hipError_t launch_moe_gemm(const uint8_t *w, float *y, uint32_t routes, uint32_t N, uint32_t K, uint32_t n_experts,
                            uint64_t expert_stride, MoeScratch s, hipStream_t stream);
 
-// Streaming-read ceiling (q2k_probe.hip): reads `bytes` (a multiple of 16)
-// once and stores one word per workgroup (at most kReadProbeMaxGrid) in sink.
-constexpr uint32_t kReadProbeMaxGrid = 2048;
-uint32_t read_probe_grid(uint64_t bytes);
-hipError_t launch_read_probe(const void *data, uint64_t bytes, uint32_t *sink, hipStream_t stream);
-
 }  // namespace q2k

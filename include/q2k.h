@@ -34,6 +34,19 @@
  *  - An output range may not overlap any input range.
  *  - Calls on different streams may run concurrently; each call only reads its
  *    inputs and writes its outputs.
+ *  - Device scratch. Three kinds of call stage data in device scratch: the
+ *    matrix-core matmul (bf16(x)), the matrix-core expert-routed schedule and
+ *    the argmax/candidate call. Each has a *_pooled form that takes
+ *    caller-owned scratch and allocates nothing. The plain forms use a
+ *    workspace libq2k keeps per (device, stream): hipMalloc'd when a call needs
+ *    more than it holds (growing to at least twice its size); a call holds it
+ *    from its size check until its kernels are enqueued; a buffer that growth
+ *    replaces is retired but never freed before the process ends, so a graph
+ *    captured earlier keeps a valid address. Growth is refused with
+ *    Q2K_ERR_INVALID_ARGUMENT while the stream is capturing a graph: capture
+ *    after one call of the largest size, or use the pooled form. A replayed
+ *    graph shares the workspace with later calls on its capture stream, so the
+ *    two must not run at the same time.
  */
 #ifndef Q2K_H
 #define Q2K_H
@@ -96,9 +109,8 @@ q2k_status q2k_dequantize(const void *blocks, size_t blocks_bytes, float *out, s
  * run different kernels and may differ in the last bits).
  * M > 8 runs the matrix-core path on bf16(x) and bf16(w) with fp32
  * accumulation: |y - exact| <= 4e-3 * sum_k |x*w| + 1e-6. That path stages
- * bf16(x) (2 * M * K bytes) in a device workspace that libq2k keeps per
- * (device, stream): allocated in stream order on the first call that needs
- * more, reused afterwards, never freed before the process ends.
+ * bf16(x) (2 * M * K bytes) in the stream's workspace (conventions above);
+ * q2k_matmul_pooled takes it from the caller instead.
  * Asynchronous on `stream`.
  */
 q2k_status q2k_matmul(const float *x, const void *w, float *y, uint32_t M, uint32_t N, uint32_t K,
@@ -108,6 +120,23 @@ q2k_status q2k_matmul(const float *x, const void *w, float *y, uint32_t M, uint3
  * rules and guarantees; Q2K_PATH_GEMV with M > 8 is Q2K_ERR_INVALID_ARGUMENT. */
 q2k_status q2k_matmul_path(const float *x, const void *w, float *y, uint32_t M, uint32_t N,
                            uint32_t K, q2k_path path, void *stream);
+
+/* q2k_matmul_scratch_bytes — device scratch q2k_matmul_pooled needs for these
+ * sizes and path: 2 * M * K bytes (bf16(x)) for the matrix-core path, 0 for
+ * the GEMV. Shape rules as for q2k_matmul (pointers aside); *bytes is written
+ * only on success. */
+q2k_status q2k_matmul_scratch_bytes(uint32_t M, uint32_t N, uint32_t K, q2k_path path, uint64_t *bytes);
+
+/* q2k_matmul_pooled — q2k_matmul_path with caller-held scratch and no
+ * allocation (page: the pooled calls' caller-provided IdMmScratch, applied to
+ * the dense product). When the path needs scratch, `scratch` is device memory
+ * of at least q2k_matmul_scratch_bytes bytes, 256-byte aligned, not
+ * overlapping x, w or y; its contents on entry do not matter and it is in use
+ * until the call's work on `stream` ends. When the path needs none (the GEMV),
+ * scratch and scratch_bytes are ignored. Same results, bit for bit, as
+ * q2k_matmul_path with the same path. */
+q2k_status q2k_matmul_pooled(const float *x, const void *w, float *y, uint32_t M, uint32_t N, uint32_t K,
+                             q2k_path path, void *scratch, uint64_t scratch_bytes, void *stream);
 
 /*
  * q2k_matmul_batched — a batch of independent small products,
@@ -177,7 +206,7 @@ typedef struct q2k_matmul_id_params {
 /* q2k_matmul_id — the routed product with libq2k choosing the schedule the way
  * the page's test tolerances do: the matrix-core schedule when n_tokens > 32
  * and top_k is 1, 6 or 8, the fp32 mat-vec otherwise. The matrix-core schedule
- * uses the per-(device, stream) workspace (see q2k_matmul). */
+ * uses the stream's workspace (conventions above). */
 q2k_status q2k_matmul_id(const float *x, const void *w, const uint32_t *ids, float *y,
                          const q2k_matmul_id_params *p, int *status, void *stream);
 
@@ -275,12 +304,25 @@ q2k_status q2k_embedding_gather_async(const void *table, const uint32_t *ids, fl
  *   cand_ids    device u32 [n_slots, cap]: the first min(cand_count, cap)
  *               candidate indices in increasing order; entries past them are
  *               left unwritten.
- * 1 <= vocab <= 2^29. Outputs may not overlap the logits or each other. Uses the per-(device,
- * stream) workspace (about 24 bytes per 8192 logits). Asynchronous on `stream`.
+ * 1 <= vocab <= 2^29. Outputs may not overlap the logits or each other. Uses the stream's
+ * workspace (about 24 bytes per 8192 logits; conventions above). Asynchronous on `stream`.
  */
 q2k_status q2k_argmax_candidates(const float *logits, uint32_t n_slots, uint32_t vocab, uint32_t cap,
                                  uint32_t *top1_idx, float *top1_val, uint32_t *cand_count, uint32_t *overflow,
                                  uint32_t *cand_ids, void *stream);
+
+/* Device scratch q2k_argmax_candidates_pooled needs for n_slots x vocab logits
+ * (n_slots >= 1, 1 <= vocab <= 2^29); *bytes is written only on success. */
+q2k_status q2k_argmax_candidates_scratch_bytes(uint32_t n_slots, uint32_t vocab, uint64_t *bytes);
+
+/* q2k_argmax_candidates with caller-held scratch and no allocation: scratch is
+ * device memory of at least q2k_argmax_candidates_scratch_bytes bytes, 256-byte
+ * aligned, not overlapping any other argument, in use until the call's work on
+ * `stream` ends. Same results as q2k_argmax_candidates. */
+q2k_status q2k_argmax_candidates_pooled(const float *logits, uint32_t n_slots, uint32_t vocab, uint32_t cap,
+                                        uint32_t *top1_idx, float *top1_val, uint32_t *cand_count,
+                                        uint32_t *overflow, uint32_t *cand_ids, void *scratch,
+                                        uint64_t scratch_bytes, void *stream);
 
 /*
  * GGUF tensor directory (host only; no GPU work).
@@ -325,17 +367,6 @@ q2k_status q2k_gguf_tensor_info(const q2k_gguf *f, const char *name, q2k_gguf_in
 /* Host pointer to the tensor's bytes inside the mapping (for upload with
  * hipMemcpy); fails if the type's size is unknown. */
 q2k_status q2k_gguf_tensor_data(const q2k_gguf *f, const char *name, const void **data, uint64_t *byte_len);
-
-/*
- * q2k_read_probe — measurement aid, not part of the Q2_K path: reads `bytes`
- * of device memory once with the grid shape of the decode GEMV and stores
- * one XOR word per workgroup in `sink`, so a benchmark can time the plain
- * streaming-read ceiling for a transfer of a given size.
- *   data        device memory, 16-byte aligned; bytes a positive multiple of 16.
- *   sink        device u32 [sink_elems], sink_elems >= 2048; not overlapping data.
- * Asynchronous on `stream`; allocates nothing.
- */
-q2k_status q2k_read_probe(const void *data, size_t bytes, uint32_t *sink, size_t sink_elems, void *stream);
 
 /* Static English name of a status code ("Q2K_OK", ...). Never NULL. */
 const char *q2k_status_string(q2k_status s);

@@ -237,13 +237,61 @@ def test_matmul_id_pair_rejects_overlapping_outputs(lib):
     _err(lib, pair(A, B, B, C, D, None, ctypes.byref(p), F, need, None, None), "null")
 
 
-def test_read_probe_rejects_bad_arguments(lib):
-    _err(lib, lib.q2k_read_probe(None, 64, B, 2048, None), "null")
-    _err(lib, lib.q2k_read_probe(A, 0, B, 2048, None), "multiple of 16")
-    _err(lib, lib.q2k_read_probe(A, 20, B, 2048, None), "multiple of 16")
-    _err(lib, lib.q2k_read_probe(A, 64, B, 2047, None), "2048 needed")
-    _err(lib, lib.q2k_read_probe(A + 8, 64, B, 2048, None), "aligned")
-    _err(lib, lib.q2k_read_probe(A, 1 << 20, A + 4096, 2048, None), "overlaps")
+# ---------------------------------------------------------------- caller-held scratch
+
+def _u64():
+    return ctypes.c_uint64(0xDEAD)
+
+
+def test_matmul_scratch_bytes_per_path(lib):
+    n = _u64()
+    assert lib.q2k_matmul_scratch_bytes(8, 10, 512, 0, ctypes.byref(n)) == 0 and n.value == 0      # GEMV
+    assert lib.q2k_matmul_scratch_bytes(9, 10, 512, 0, ctypes.byref(n)) == 0 and n.value == 2 * 9 * 512
+    assert lib.q2k_matmul_scratch_bytes(1, 10, 512, 2, ctypes.byref(n)) == 0 and n.value == 2 * 512
+    assert lib.q2k_matmul_scratch_bytes(8, 10, 512, 1, ctypes.byref(n)) == 0 and n.value == 0
+    n = _u64()
+    _err(lib, lib.q2k_matmul_scratch_bytes(9, 10, 512, 1, ctypes.byref(n)), "M <= 8")
+    _err(lib, lib.q2k_matmul_scratch_bytes(0, 10, 512, 0, ctypes.byref(n)), ">= 1")
+    _err(lib, lib.q2k_matmul_scratch_bytes(9, 10, 500, 0, ctypes.byref(n)), "multiple of 256")
+    _err(lib, lib.q2k_matmul_scratch_bytes(9, 10, 512, 5, ctypes.byref(n)), "unknown path")
+    _err(lib, lib.q2k_matmul_scratch_bytes(9, 10, 512, 0, None), "null")
+    assert n.value == 0xDEAD  # untouched on failure
+
+
+def test_matmul_pooled_rejects_bad_scratch(lib):
+    M, N, K = 16, 8, 512
+    need = 2 * M * K
+    pooled = lib.q2k_matmul_pooled
+    _err(lib, pooled(A, B, C, M, N, K, 0, None, need, None), "null scratch")
+    _err(lib, pooled(A, B, C, M, N, K, 0, F + 16, need, None), "256-byte aligned")
+    _err(lib, pooled(A, B, C, M, N, K, 0, F, need - 1, None), "needed")
+    _err(lib, pooled(A, B, C, M, N, K, 0, A + 256, need, None), "scratch overlaps")      # inside x
+    _err(lib, pooled(A, B, C, M, N, K, 0, C - 256, need, None), "scratch overlaps")      # runs into y
+    _err(lib, pooled(A, B, C, M, N, K, 1, F, need, None), "M <= 8")
+    _err(lib, pooled(A, B, C + 4, M, N, K, 0, F, need, None), "aligned")                 # matmul rules first
+    _err(lib, pooled(A, B, C, 0, N, K, 0, F, need, None), ">= 1")
+
+
+def test_argmax_pooled_rejects_bad_scratch(lib):
+    n = _u64()
+    assert lib.q2k_argmax_candidates_scratch_bytes(2, 8, ctypes.byref(n)) == 0 and n.value > 0
+    need = n.value
+    _err(lib, lib.q2k_argmax_candidates_scratch_bytes(0, 8, ctypes.byref(n)), "n_slots >= 1")
+    _err(lib, lib.q2k_argmax_candidates_scratch_bytes(2, (1 << 29) + 1, ctypes.byref(n)), "vocab")
+    pooled = lib.q2k_argmax_candidates_pooled
+    _err(lib, pooled(A, 2, 8, 4, B, C, D, E, F, None, need, None), "null scratch")
+    _err(lib, pooled(A, 2, 8, 4, B, C, D, E, F, G + 4, need, None), "256-byte aligned")
+    _err(lib, pooled(A, 2, 8, 4, B, C, D, E, F, G, need - 1, None), "needed")
+    _err(lib, pooled(A, 2, 8, 4, B, C, D, E, F, F, need, None), "scratch overlaps")
+    _err(lib, pooled(A, 0, 8, 4, B, C, D, E, F, G, need, None), "> 0")
+
+
+def test_argmax_scratch_covers_one_launch_of_slots(lib):
+    # More than 65535 slots run in several launches that reuse the same scratch.
+    a, b = ctypes.c_uint64(), ctypes.c_uint64()
+    assert lib.q2k_argmax_candidates_scratch_bytes(65535, 262144, ctypes.byref(a)) == 0
+    assert lib.q2k_argmax_candidates_scratch_bytes(200000, 262144, ctypes.byref(b)) == 0
+    assert a.value == b.value > 0
 
 
 def test_python_binding_raises_typed_errors(lib):

@@ -438,20 +438,32 @@ def test_mfma_ragged_shapes(M, N, K):
     check_mfma(y, x, blocks, M, N, K)
 
 
-def test_mfma_config4_full_size_sampled():
-    # Full M=512, N=14336, K=4096 launch; the oracle checks a sample of rows and
-    # columns that covers both ends of every tile edge.
+def test_mfma_config4_full_size_every_output():
+    # The full M=512, N=14336, K=4096 launch (224 workgroups in the XCD-banded
+    # tile order), every one of its 7 340 032 outputs against the f64 oracle and
+    # the oracle on bf16-rounded operands.
+    import time
     inp = inputs(4)
     c = inp.config
     y = gpu_matmul(inp.x, inp.blocks, c.M, c.N, c.K)
-    assert np.all(np.isfinite(y))
-    rng = np.random.Generator(np.random.PCG64(36))
-    ms = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 383, 384, 510, 511], rng.integers(0, c.M, 22)]))
-    ns = np.unique(np.concatenate([[0, 1, 127, 128, 7167, 7168, 14334, 14335], rng.integers(0, c.N, 40)]))
-    x_s = inp.x[ms]
-    w_s = synth.rows_of(inp.blocks, c.K, ns)
-    worst = check_mfma(y[np.ix_(ms, ns)], x_s, w_s, len(ms), len(ns), c.K)
-    print("parity cfg4 (%s, %d x %d sampled outputs): max |y - y_ref| / A = %.3g" % (c.name, len(ms), len(ns), worst))
+    t0 = time.perf_counter()
+    worst = check_mfma(y, inp.x, inp.blocks, c.M, c.N, c.K)
+    print("parity cfg4 (%s, all %d outputs): max |y - y_ref| / A = %.3g (oracle %.1f s on %d threads)" % (
+        c.name, c.M * c.N, worst, time.perf_counter() - t0, oracle.host_threads()))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 1024, 512), (512, 1024, 1024), (384, 2048, 512), (200, 1000, 768),
+                                   (1000, 520, 256)])
+def test_mfma_xcd_banded_tile_order_every_output(M, N, K):
+    # Tile counts that are multiples of 8 (2x4, 4x4, 3x8, ragged 2x4, ragged 8x3)
+    # take the XCD-banded block-to-tile order; every output is compared.
+    tiles = ((M + 127) // 128) * ((N + 255) // 256)
+    assert tiles % 8 == 0
+    rng = np.random.Generator(np.random.PCG64(M * 31 + N * 7 + K))
+    blocks = synth.random_blocks(rng, N * K // QK_K)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    y = gpu_matmul(x, blocks, M, N, K)
+    check_mfma(y, x, blocks, M, N, K)
 
 
 def test_mfma_non_finite_scales_give_nan_columns():
@@ -525,12 +537,27 @@ def test_mfma_is_deterministic():
 # ----------------------------------------------------------------- measurement aid
 
 def test_read_probe_reads_every_word():
-    # q2k_read_probe stores one XOR word per workgroup; their XOR is the XOR of all data words.
+    # libq2k_probe (the benchmark's plain-read kernel, not part of the C ABI) stores one XOR word per
+    # workgroup; their XOR is the XOR of all data words, for every launch shape the benchmark sweeps.
+    import ctypes
+    from ggml_q2_dequant_amd import build
+    probe = ctypes.CDLL(build.PROBE_LIB)
+    probe.q2k_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    probe.q2k_probe_read.restype = ctypes.c_int
     rng = np.random.Generator(np.random.PCG64(44))
+    sink = torch.zeros(16384, dtype=torch.int32, device="cuda:0")
     for nbytes in (16, 4096 + 16, 5 * 1024 * 1024 + 48):
         data = rng.integers(0, 2 ** 32, nbytes // 4, dtype=np.uint32)
-        sink = torch.zeros(q2k.READ_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda:0")
-        q2k.q2k_read_probe(dev(data.view(np.int32)), sink)
-        torch.cuda.synchronize()
-        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
-        assert got == np.bitwise_xor.reduce(data)
+        d = dev(data.view(np.int32))
+        for grid, unroll in ((0, 4), (256, 1), (2048, 16), (16384, 2), (7, 8)):
+            sink.zero_()
+            rc = probe.q2k_probe_read(d.data_ptr(), nbytes, sink.data_ptr(), sink.numel(), grid, unroll,
+                                      torch.cuda.current_stream().cuda_stream)
+            assert rc == 0
+            torch.cuda.synchronize()
+            got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+            assert got == np.bitwise_xor.reduce(data), (nbytes, grid, unroll)
+    assert probe.q2k_probe_read(d.data_ptr(), 20, sink.data_ptr(), sink.numel(), 0, 4, None) == 1
+    assert probe.q2k_probe_read(d.data_ptr(), 64, sink.data_ptr(), 8, 16, 4, None) == 1
+    assert probe.q2k_probe_read(d.data_ptr(), 64, sink.data_ptr(), sink.numel(), 0, 3, None) == 1
