@@ -63,6 +63,7 @@ EXPORTS = (
     "q2k_matmul_path",
     "q2k_matmul_scratch_bytes",
     "q2k_matmul_pooled",
+    "q2k_matmul_noalloc",
     "q2k_matmul_batched",
     "q2k_embedding_gather",
     "q2k_embedding_gather_async",
@@ -153,9 +154,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     U64, PU64 = ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)
     lib.q2k_matmul_scratch_bytes.argtypes = [U32, U32, U32, ctypes.c_int, PU64]
     lib.q2k_matmul_pooled.argtypes = [P, P, P, U32, U32, U32, ctypes.c_int, P, U64, P]
+    lib.q2k_matmul_noalloc.argtypes = [P, P, P, U32, U32, U32, P]
     lib.q2k_argmax_candidates_scratch_bytes.argtypes = [U32, U32, PU64]
     lib.q2k_argmax_candidates_pooled.argtypes = [P, U32, U32, U32, P, P, P, P, P, P, U64, P]
-    for name in ("q2k_matmul_scratch_bytes", "q2k_matmul_pooled", "q2k_argmax_candidates_scratch_bytes",
+    for name in ("q2k_matmul_scratch_bytes", "q2k_matmul_pooled", "q2k_matmul_noalloc",
+                 "q2k_argmax_candidates_scratch_bytes",
                  "q2k_argmax_candidates_pooled"):
         getattr(lib, name).restype = ctypes.c_int
     PP = ctypes.POINTER(MatmulIdParams)
@@ -257,6 +260,14 @@ def q2k_matmul_pooled(x, w, y, M: int, N: int, K: int, scratch, path: int = PATH
     nb = (0 if scratch is None else _nbytes(scratch)) if scratch_bytes is None else int(scratch_bytes)
     _check(load_library().q2k_matmul_pooled(_ptr(x), _ptr(w), _ptr(y), M, N, K, int(path), _ptr(scratch), nb,
                                             _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def q2k_matmul_noalloc(x, w, y, M: int, N: int, K: int, stream=None) -> None:
+    """q2k_matmul that allocates nothing (M > 8 needs 2*M*K <= 16 MiB); calls on one GPU must not overlap."""
+    _check(load_library().q2k_matmul_noalloc(_ptr(x), _ptr(w), _ptr(y), M, N, K, _stream(stream)))
 
 
 def q2k_matmul_batched(x, w, y, batches: int, M: int, N: int, K: int, stream=None) -> None:

@@ -477,6 +477,31 @@ q2k_status q2k_matmul_pooled(const float *x, const void *w, float *y, uint32_t M
                       static_cast<hipStream_t>(stream));
 }
 
+q2k_status q2k_matmul_noalloc(const float *x, const void *w, float *y, uint32_t M, uint32_t N, uint32_t K,
+                              void *stream) {
+    static const char fn[] = "q2k_matmul_noalloc";
+    Range rx, rw, ry;
+    q2k_status s = check_matmul(x, w, y, M, N, K, &rx, &rw, &ry);
+    if (s != Q2K_OK) return s;
+    q2k_path path = Q2K_PATH_AUTO;
+    if ((s = resolve_path(fn, M, &path)) != Q2K_OK) return s;
+    const uint64_t need = matmul_scratch(M, K, path);
+    void *scratch = nullptr;
+    if (need > 0) {
+        if (need > q2k::kNoAllocScratchBytes)
+            return fail(Q2K_ERR_INVALID_ARGUMENT,
+                        "%s: M=%u, K=%u needs %llu bytes of bf16 activations; the library's device scratch holds "
+                        "%llu (M * K <= %llu when M > 8)",
+                        fn, M, K, static_cast<unsigned long long>(need),
+                        static_cast<unsigned long long>(q2k::kNoAllocScratchBytes),
+                        static_cast<unsigned long long>(q2k::kNoAllocScratchBytes / 2));
+        const hipError_t e = q2k::noalloc_scratch(&scratch);
+        if (e != hipSuccess) return device_error("q2k_matmul_noalloc: hipGetSymbolAddress(scratch)", e);
+    }
+    return run_matmul(fn, x, static_cast<const uint8_t *>(w), y, M, N, K, path, scratch,
+                      static_cast<hipStream_t>(stream));
+}
+
 q2k_status q2k_matmul(const float *x, const void *w, float *y, uint32_t M, uint32_t N, uint32_t K, void *stream) {
     return q2k_matmul_path(x, w, y, M, N, K, Q2K_PATH_AUTO, stream);
 }

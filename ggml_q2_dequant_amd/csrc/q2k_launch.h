@@ -33,6 +33,12 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, u
 hipError_t launch_gemm_mfma(const float *x, const uint8_t *w, float *y, uint32_t M, uint32_t N, uint32_t K,
                             void *x_bf16, hipStream_t stream);
 
+// q2k_matmul_noalloc (q2k_noalloc.hip): the device address of the library's
+// file-scope scratch array on the current device, kNoAllocScratchBytes long,
+// 256-byte aligned; looked up once per device, never allocated.
+constexpr uint64_t kNoAllocScratchBytes = 16ull << 20;
+hipError_t noalloc_scratch(void **out);
+
 // First-max argmax + threshold candidates over [n_slots, vocab] logits
 // (q2k_sample.hip). workspace holds sample_workspace_bytes(n_slots, vocab)
 // bytes, 8-byte aligned; 1 <= n_slots <= kMaxGridY, vocab, cap >= 1.

@@ -139,6 +139,22 @@ q2k_status q2k_matmul_pooled(const float *x, const void *w, float *y, uint32_t M
                              q2k_path path, void *scratch, uint64_t scratch_bytes, void *stream);
 
 /*
+ * q2k_matmul_noalloc — q2k_matmul for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, kernel choice, rules and results, bit for
+ * bit, as q2k_matmul. It calls no allocating routine: for M > 8 it stages
+ * bf16(x) in a device array compiled into libq2k (16 MiB per GPU, held until
+ * the process ends), so M > 8 requires 2 * M * K <= 16 MiB (M * K <= 8388608);
+ * larger sizes are Q2K_ERR_INVALID_ARGUMENT and enqueue nothing. M <= 8 needs
+ * no scratch and has no such limit. Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (several streams, or several
+ * host threads) race on it; calls in order on one stream do not. Asynchronous
+ * on `stream`.
+ */
+q2k_status q2k_matmul_noalloc(const float *x, const void *w, float *y, uint32_t M, uint32_t N, uint32_t K,
+                              void *stream);
+
+/*
  * q2k_matmul_batched — a batch of independent small products,
  *   y[b][M, N] = x[b][M, K] * W[b][N, K]^T for b = 0 .. batches-1.
  * Page: test q2_k_batched_mv_is_byte_identical_to_independent_dispatches
