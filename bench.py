@@ -5,25 +5,33 @@ Timed step: one q2k_matmul call on the decode GEMV workload (M = 1, N = K =
 4096, Q2_K weights, f32 activations), the workload the headline metric is
 quoted on. Each step reads a different one of R byte-identical weight replicas
 (R * 5.5 MB >= 512 MiB, twice the 256 MiB Infinity Cache), so every step
-streams its weights from HBM. The other rows of the path (dequantize, gather,
+streams its weights from HBM. Before the K timed steps a 768 MiB read of other
+memory leaves nothing they read in a cache; they are then issued back to back
+behind a GPU spin long enough for the host to queue them all, and timed with
+events on the launch stream, so the figure is the GPU's and not the host's
+launch rate. A HIP-graph replay of the same steps and host-paced launches are
+reported beside it. The other rows of the path (dequantize, gather,
 M = 8 GEMV, M = 512 matrix-core GEMM, batched mat-vec, argmax + candidates, expert-routed decode and
 prefill) are timed after the headline region and
-reported under "rows", each against the roofline that bounds it. The CPU
+reported under "rows", each against the roofline that bounds it, timed the
+same way (the synchronous gather, which waits on the host in every call,
+without the spin). The CPU
 oracle is timed on the host cores on a bounded sample and reported as
 "cpu_baseline".
 
 Other modes (used to collect rocprofv3 counters; they print one short JSON line):
-  --only ROW         run only one row's timed loop (gemv1, dequant, gather, gemv8, mfma, mfma_context,
-                     batched, sample, moe_decode, moe_prefill)
+  --only ROW         run only one row's timed loop, launches issued eagerly (gemv1, dequant, gather,
+                     gemv1_wide, gemv8, mfma, mfma_context, batched, sample, moe_decode, moe_prefill)
   --copy-probe       also run a device-to-device copy of COPY_BYTES (counter calibration)
   --no-context       skip the M=512 context timings (used when profiling every kernel, so the
                      GEMM's statistics hold only the row's own calls)
   --sweep            M=1 GEMV over N = 4096 .. 131072 (K = 4096, cold) beside the plain-read ceiling
-  --derive-traffic FETCH_CSV WRITE_CSV
+  --derive-traffic FETCH_CSV WRITE_CSV KEY
                      turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
-                     `--only gemv1 --copy-probe` into profiles/traffic.json: HBM bytes
-                     per GEMV launch, each counter scaled by known bytes / what it
-                     reads for the copy.
+                     `--only ROW --copy-probe` into HBM bytes per launch of that row's kernel,
+                     recorded in profiles/traffic.json under KEY (k_gemv_m1, k_dequantize,
+                     k_gather, k_gemv_m8): each counter scaled by known bytes / what it reads
+                     for the copy.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -53,10 +61,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 PROBE_LIB = os.path.join(ROOT, "ggml_q2_dequant_amd", "libq2k_probe.so")
 PROBE_GRIDS = (256, 512, 1024, 2048, 4096, 8192, 16384)
 PROBE_UNROLLS = (1, 2, 4, 8, 16)
-GEMV_KERNEL = "k_gemv_seg<1"    # name prefix of the M = 1 GEMV kernel in rocprofv3 output
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-ROWS = ("gemv1", "dequant", "gather", "gemv8", "mfma", "mfma_context", "batched", "sample", "moe_decode",
-        "moe_prefill")
+# Rows whose HBM bytes come from counters: key -> (--only row, kernel name fragment in rocprofv3 output,
+# algorithmic bytes per launch).
+TRAFFIC_ROWS = {
+    "k_gemv_m1": ("gemv1", "k_gemv_seg<1", 5537792),
+    "k_dequantize": ("dequant", "k_dequantize", 65536 * 84 + 65536 * 1024),
+    "k_gather": ("gather", "k_gather", 9078784),
+    "k_gemv_m8": ("gemv8", "k_gemv_mfma", 19857408),
+}
+ROWS = ("gemv1", "dequant", "gather", "gemv1_wide", "gemv8", "mfma", "mfma_context", "batched", "sample",
+        "moe_decode", "moe_prefill")
 
 
 def log(msg: str) -> None:
@@ -66,6 +81,14 @@ def log(msg: str) -> None:
 def kernel_source_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_row(key: str):
+    """{hbm_bytes_per_launch, over_algorithmic} from the counters recorded for the current kernel source, else None."""
+    hbm = measured_traffic(key)
+    if hbm is None:
+        return None
+    return {"hbm_bytes_per_launch": hbm, "over_algorithmic": round(hbm / TRAFFIC_ROWS[key][2], 4)}
 
 
 def measured_traffic(kernel: str):
@@ -100,17 +123,87 @@ def load_probe():
     return _probe
 
 
-def time_launches(torch, launch, n: int, warmup: int):
-    """Average time per launch over n back-to-back launches, from events on the launch stream."""
+FLUSH_BYTES = 768 << 20         # read before each timed region: more than the Infinity Cache and the L2s hold
+_flush = {}
+EAGER_ONLY = [False]            # --only: launch eagerly (profiler runs count kernels, they need no graphs)
+
+
+def flush_caches(torch):
+    """Read FLUSH_BYTES of other memory on the current stream, so nothing a timed region reads next is still in
+    the Infinity Cache or an L2 (its inputs are then cold unless the region itself reuses them)."""
+    if "buf" not in _flush:
+        _flush["buf"] = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+        _flush["sink"] = torch.empty(16384, dtype=torch.int32, device="cuda:0")
+    b, sink = _flush["buf"], _flush["sink"]
+    rc = load_probe().q2k_probe_read(b.data_ptr(), b.numel(), sink.data_ptr(), sink.numel(), 0, 4,
+                                     torch.cuda.current_stream().cuda_stream)
+    if rc:
+        raise RuntimeError("flush read rejected (%d)" % rc)
+
+
+_spin = {}
+
+
+def gpu_spin(torch, us: float = 2000.0):
+    """Keep the GPU busy for about `us` microseconds (a spin kernel on the current stream) while the host submits
+    the timed work, so the timer starts with that work already queued and host launch cost does not show in it.
+    The spin's cycles per microsecond are measured once with events."""
+    sleep = getattr(torch.cuda, "_sleep", None)
+    if sleep is None:
+        return
+    if "cyc_per_us" not in _spin:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        sleep(1_000_000)
+        torch.cuda.synchronize()
+        a.record()
+        sleep(4_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _spin["cyc_per_us"] = 4_000_000 / max(a.elapsed_time(b) * 1e3, 1.0)
+    sleep(int(min(us, 200_000.0) * _spin["cyc_per_us"]))
+
+
+def time_launches(torch, launch, n: int, warmup: int, graph: bool = False, spin: bool = True):
+    """Average time per launch over n back-to-back launches on the current stream, from events on that stream.
+
+    The caches are flushed first (the launches' inputs are cold unless they reuse them among themselves). By
+    default the n launches are issued eagerly behind a GPU spin long enough for the host to queue them all, so
+    the figure is the GPU's time for the n calls and not the host's rate of issuing them. graph=True captures the
+    n launches in a HIP graph instead and times one replay (after an untimed one). Calls that wait on the host
+    (the synchronous gather) cannot be queued ahead: EAGER_ONLY or a host wait inside a call makes the spin moot,
+    and the figure then includes the host's part."""
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(n):
-        launch(i)
-    end.record()
+    if EAGER_ONLY[0]:
+        start.record(s)
+        for i in range(n):
+            launch(i)
+        end.record(s)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / n * 1e-3
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                launch(i)
+        g.replay()
+        torch.cuda.synchronize()
+    flush_caches(torch)
+    if spin:
+        gpu_spin(torch, 500.0 + 40.0 * n)
+    start.record(s)
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(n):
+            launch(i)
+    end.record(s)
     torch.cuda.synchronize()
+    del g
     return start.elapsed_time(end) / n * 1e-3  # seconds per launch
 
 
@@ -135,31 +228,6 @@ def time_blocks(torch, launch, blocks: int = 50, per: int = 20, warmup: int = 20
 
 def dist_us(d):
     return {k: round(v * 1e6, 3) for k, v in d.items()}
-
-
-def time_graph(torch, make_launch, n: int):
-    """Seconds per launch when n launches are captured in one graph and replayed. make_launch(stream) returns a
-    launch function bound to that HIP stream (the capture stream)."""
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    with torch.cuda.stream(s):
-        # One eager call on the capture stream first: a call that stages data in the library's
-        # per-stream workspace allocates it here, outside the capture.
-        make_launch(torch.cuda.current_stream().cuda_stream)(0)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=s):
-            launch = make_launch(torch.cuda.current_stream().cuda_stream)
-            for i in range(n):
-                launch(i)
-    g.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    del g
-    return a.elapsed_time(b) * 1e-3 / n
 
 
 def cpu_baseline(inp, budget_s: float):
@@ -198,14 +266,20 @@ def _pick(vals: dict, prefix: str):
     return [x for lst in got for x in lst]
 
 
-def derive_traffic(fetch_csv: str, write_csv: str) -> int:
+def derive_traffic(fetch_csv: str, write_csv: str, key: str) -> int:
+    """HBM bytes per launch of one row's kernel from a FETCH_SIZE and a WRITE_SIZE counter run of
+    `bench.py --only ROW --copy-probe`, each scaled by the known size of the calibration copy over what the same
+    counter reads for it; recorded in profiles/traffic.json under `key` with the kernel source's hash."""
+    if key not in TRAFFIC_ROWS:
+        raise SystemExit("unknown traffic key %r (one of %s)" % (key, ", ".join(TRAFFIC_ROWS)))
+    row, kernel, algo = TRAFFIC_ROWS[key]
     fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _per_dispatch(write_csv, "WRITE_SIZE")
     copy_f = max(_pick(fetch, COPY_KERNEL))   # the calibration copy is the largest copy dispatch
     copy_w = max(_pick(write, COPY_KERNEL))
     known_kib = COPY_BYTES / 1024.0
     rs, ws = known_kib / copy_f, known_kib / copy_w
-    gf, gw = _pick(fetch, GEMV_KERNEL), _pick(write, GEMV_KERNEL)
+    gf, gw = _pick(fetch, kernel), _pick(write, kernel)
     f_kib, w_kib = sum(gf) / len(gf), sum(gw) / len(gw)
     hbm = (f_kib * rs + w_kib * ws) * 1024.0
     rec = {}
@@ -214,20 +288,21 @@ def derive_traffic(fetch_csv: str, write_csv: str) -> int:
             rec = json.load(f)
     except (OSError, ValueError):
         pass
-    rec["k_gemv_m1"] = {
+    rec[key] = {
         "kernel_source_sha256": kernel_source_hash(),
-        "hbm_bytes_per_launch": round(hbm),
+        "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": algo,
+        "traffic_over_algorithmic": hbm / algo,
         "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
         "copy_bytes": COPY_BYTES, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
         "read_scale": rs, "write_scale": ws, "launches": len(gf),
-        "how": "rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE of `bench.py --only gemv1 --copy-probe`; "
-               "each counter scaled by known bytes / its reading for a %d-byte device copy" % COPY_BYTES,
+        "how": "rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE of `bench.py --only %s --copy-probe`; each counter "
+               "scaled by known bytes / its reading for a %d-byte device copy" % (row, COPY_BYTES),
     }
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
-    print(json.dumps(rec["k_gemv_m1"]))
+    print(json.dumps({key: rec[key]}))
     return 0
 
 
@@ -237,7 +312,10 @@ class Bench:
     def __init__(self, torch, q2k, synth, np):
         self.torch, self.q2k, self.synth, self.np = torch, q2k, synth, np
         self.dev = torch.device("cuda:0")
+        # Every call runs on this stream (made current by main): HIP graphs cannot capture the null stream.
         self.stream = torch.cuda.current_stream().cuda_stream
+        if self.stream == 0:
+            raise RuntimeError("run the benchmark on a side stream")
 
     def gemv1_setup(self):
         inp = self.synth.make_inputs(1)
@@ -285,7 +363,7 @@ class Bench:
         t = timed(0, 4)
         out = {"bytes": b, "us": t * 1e6, "GB/s": b / t / 1e9,
                "shape": {"grid": int(probe.q2k_probe_default_grid(b, 4)), "loads_per_thread": 4}}
-        if not sweep:
+        if not sweep or EAGER_ONLY[0]:
             return out
         shapes = []
         for grid in PROBE_GRIDS:
@@ -322,7 +400,8 @@ class Bench:
         log("dequantize: %.2f us, %.1f GB/s" % (t * 1e6, gbs))
         return {"workload": "%d blocks (the decode GEMV weights), cold replicas" % (w_bytes // 84),
                 "us": t * 1e6, "algorithmic_bytes": b, "GB/s": gbs, "bound": "hbm",
-                "frac_hbm": gbs / HBM_PEAK_GBS, "write_ceiling": self.write_ceiling([out])}
+                "frac_hbm": gbs / HBM_PEAK_GBS, "write_ceiling": self.write_ceiling([out]),
+                "traffic": traffic_row("k_dequantize")}
 
     def gather(self, n=200):
         np, torch = self.np, self.torch
@@ -337,7 +416,7 @@ class Bench:
         b = c.n_tokens * (c.embed_dim // 256) * 84 + c.n_tokens * c.embed_dim * 4 + c.n_tokens * 4
         t = time_launches(torch, lambda i: self.q2k.q2k_embedding_gather(table, id_sets[i % 64], outs[i % 8],
                                                                          c.vocab, c.embed_dim, c.n_tokens,
-                                                                         stream=self.stream), n, 20)
+                                                                         stream=self.stream), n, 20, spin=False)
         gbs = b / t / 1e9
         log("gather: %.2f us/call (synchronous), %.1f GB/s" % (t * 1e6, gbs))
         # The asynchronous entry point on the same calls: back-to-back launches, one status word checked
@@ -352,7 +431,27 @@ class Bench:
                             "its id check", "us_per_call_incl_sync": t * 1e6, "algorithmic_bytes": b,
                 "GB/s": gbs, "bound": "hbm", "frac_hbm": gbs / HBM_PEAK_GBS,
                 "async": {"us_per_call": ta * 1e6, "GB/s": b / ta / 1e9, "frac_hbm": b / ta / 1e9 / HBM_PEAK_GBS},
-                "write_ceiling": self.write_ceiling(outs)}
+                "write_ceiling": self.write_ceiling(outs), "traffic": traffic_row("k_gather")}
+
+    def gemv1_wide(self, n=100):
+        """M=1 GEMV at N=65536, K=4096 (352 MB of weights per call, two cold replicas): the large-N decode shape
+        (an LM-head-sized or expert-sized matrix), where the GEMV is limited by instruction issue, not HBM."""
+        torch, np = self.torch, self.np
+        N, K = 65536, 4096
+        rng = np.random.Generator(np.random.PCG64(5000 + N))
+        blocks = self.synth.random_blocks(rng, N * K // 256)
+        reps = max(2, math.ceil(COLD_BYTES / blocks.size))
+        wh = torch.from_numpy(blocks)
+        wr = [wh.to(self.dev) for _ in range(reps)]
+        x = torch.from_numpy(rng.standard_normal((1, K), dtype=np.float32)).to(self.dev)
+        y = torch.empty((1, N), dtype=torch.float32, device=self.dev)
+        t = time_launches(torch, lambda i: self.q2k.q2k_matmul(x, wr[i % reps], y, 1, N, K, stream=self.stream), n,
+                          10)
+        b = blocks.size + 4 * K + 4 * N
+        log("GEMV M=1 N=65536: %.2f us, %.1f GB/s" % (t * 1e6, b / t / 1e9))
+        return {"workload": "M=1 N=65536 K=4096 (%d cold weight replicas)" % reps, "us": t * 1e6,
+                "algorithmic_bytes": b, "GB/s": b / t / 1e9, "bound": "hbm", "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
+                "read_ceiling": self.read_ceiling(wr, 50, sweep=True)}
 
     def gemv8(self, n=300):
         torch = self.torch
@@ -372,7 +471,8 @@ class Bench:
         return {"workload": "M=8 N=14336 K=4096 (%d cold weight replicas)" % reps, "us": t * 1e6,
                 "algorithmic_bytes": b, "flop": f, "GB/s": b / t / 1e9, "TFLOP/s": f / t / 1e12,
                 "bound": "hbm", "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
-                "frac_fp32": f / t / 1e12 / FP32_PEAK_TFLOPS, "read_ceiling": self.read_ceiling(wr, 100, sweep=True)}
+                "frac_fp32": f / t / 1e12 / FP32_PEAK_TFLOPS, "read_ceiling": self.read_ceiling(wr, 100, sweep=True),
+                "traffic": traffic_row("k_gemv_m8")}
 
     def mfma(self, n=400):
         torch = self.torch
@@ -383,21 +483,17 @@ class Bench:
         x = torch.from_numpy(inp.x).to(self.dev)
         y = torch.empty((c.M, c.N), dtype=torch.float32, device=self.dev)
         # Enough calls (about 30 ms) that the clock has settled; a short run reads 10 % slow.
-        t = time_launches(torch, lambda i: self.q2k.q2k_matmul(x, w, y, c.M, c.N, c.K, stream=self.stream), n,
-                          n // 10)
-        f = 2.0 * c.M * c.N * c.K
-        log("MFMA M=512: %.2f us, %.1f TFLOP/s" % (t * 1e6, f / t / 1e12))
-        # The same calls replayed from a HIP graph (no host launch work between the two kernels of a call),
-        # checked against the eager result first.
+        call = lambda i: self.q2k.q2k_matmul(x, w, y, c.M, c.N, c.K, stream=self.stream)
+        t = time_launches(torch, call, n, n // 10)
         torch.cuda.synchronize()
         want = y.clone()
         y.fill_(float("nan"))
-        tg = time_graph(torch, lambda st: (lambda i: self.q2k.q2k_matmul(x, w, y, c.M, c.N, c.K, stream=st)),
-                        min(n, 200))
+        tg = time_launches(torch, call, n, n // 10, graph=True)
         torch.cuda.synchronize()
         if not torch.equal(y.view(torch.int32), want.view(torch.int32)):
             raise RuntimeError("M=512: graph replay differs from the eager result")
-        log("MFMA M=512 graph replay: %.2f us, %.1f TFLOP/s" % (tg * 1e6, f / tg / 1e12))
+        f = 2.0 * c.M * c.N * c.K
+        log("MFMA M=512: %.2f us, %.1f TFLOP/s (graph replay: %.2f us)" % (t * 1e6, f / t / 1e12, tg * 1e6))
         return {"workload": "M=512 N=14336 K=4096 (one call: bf16(x) pre-pass + GEMM)", "us": t * 1e6,
                 "flop": f, "TFLOP/s": f / t / 1e12, "bound": "mfma",
                 "frac_bf16_mfma": f / t / 1e12 / BF16_PEAK_TFLOPS,
@@ -527,7 +623,8 @@ def main() -> int:
                     help="skip the M=512 context timings (zero activations, torch bf16 linear)")
     ap.add_argument("--only", choices=ROWS, help="run only this row's timed loop")
     ap.add_argument("--copy-probe", action="store_true", help="also run the calibration copy")
-    ap.add_argument("--derive-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--derive-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KEY"),
+                    help="record HBM bytes per launch of one row's kernel (KEY: %s)" % ", ".join(TRAFFIC_ROWS))
     ap.add_argument("--sweep", action="store_true",
                     help="M=1, K=4096 GEMV and read ceiling over N = 4096 .. 131072 (cold), one JSON line per N")
     args = ap.parse_args()
@@ -547,6 +644,12 @@ def main() -> int:
     import synth
 
     q2k.load_library()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        return run(args, torch, q2k, synth, np)
+
+
+def run(args, torch, q2k, synth, np) -> int:
     b = Bench(torch, q2k, synth, np)
 
     if args.sweep:
@@ -566,15 +669,17 @@ def main() -> int:
                 rc = lib.q2k_matmul(x.data_ptr(), wr[i % reps].data_ptr(), y.data_ptr(), 1, N, K, st)
                 if rc:
                     raise RuntimeError(lib.q2k_last_error_message().decode())
-            d = time_blocks(torch, step, 30, 20)
+            t = time_launches(torch, step, 200, 20)
             byt = blocks.size + 4 * K + 4 * N
+            rc = b.read_ceiling(wr, 100, sweep=True)
             print(json.dumps({"sweep": "gemv_m1", "N": N, "K": K, "weight_replicas": reps, "bytes": byt,
-                              "us": dist_us(d), "GB/s": byt / d["mean"] / 1e9,
-                              "read_ceiling": b.read_ceiling(wr, 300)}), flush=True)
+                              "us": t * 1e6, "GB/s": byt / t / 1e9, "of_best_read": rc["best"]["us"] / (t * 1e6),
+                              "read_ceiling": rc}), flush=True)
             del wr
         return 0
 
     if args.only:
+        EAGER_ONLY[0] = True
         out = {"only": args.only}
         if args.copy_probe:
             b.copy_probe()
@@ -599,23 +704,24 @@ def main() -> int:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record()
-    for i in range(args.steps):
-        step(i)
-    t_end.record()
-    torch.cuda.synchronize()
-    sec_per_step = t_start.elapsed_time(t_end) * 1e-3 / args.steps
+    want = g["y"].clone()
+    g["y"].fill_(float("nan"))
+    # The K timed steps: after a read of other memory that leaves every replica cold, issued back to back behind a
+    # GPU spin that lets the host queue them all before the first starts; events on the launch stream.
+    sec_per_step = time_launches(torch, step, args.steps, 0)
+    if not torch.equal(g["y"].view(torch.int32), want.view(torch.int32)):
+        raise RuntimeError("decode GEMV: the timed steps' result differs from the warm-up result")
     gbs = g["bytes"] / sec_per_step / 1e9
     log("GEMV M=1: %.3f us/step, %.1f GB/s" % (sec_per_step * 1e6, gbs))
-    # Per-call spread (runs of 20 calls) and graph replay of the same launches, after the timed region.
+    # Context after the timed region: the same steps from a HIP graph replay, the steps issued by the host one by
+    # one with nothing queued ahead (runs of 20: the host's launch rate shows in these), and the plain-read
+    # ceiling for the same cold bytes.
+    graph_s = time_launches(torch, step, max(args.steps, 200), 0, graph=True)
     dist = time_blocks(torch, step, 50, 20)
-    graph_s = time_graph(torch, g["make_step"], min(args.steps, 500))
     ceiling = b.read_ceiling(g["replicas"], sweep=True)
-    log("GEMV M=1 per call p10/p50/p90 %.2f/%.2f/%.2f us, graph %.2f us; read ceiling %.2f us (%.0f GB/s), best "
-        "read shape %s: %.2f us; d2d copy %.2f us" % (
-            dist["p10"] * 1e6, dist["p50"] * 1e6, dist["p90"] * 1e6, graph_s * 1e6, ceiling["us"], ceiling["GB/s"],
+    log("GEMV M=1 graph replay %.2f us/call; host-paced runs of 20: p10/p50/p90 %.2f/%.2f/%.2f us; read ceiling "
+        "%.2f us (%.0f GB/s), best read shape %s: %.2f us; d2d copy %.2f us" % (
+            graph_s * 1e6, dist["p10"] * 1e6, dist["p50"] * 1e6, dist["p90"] * 1e6, ceiling["us"], ceiling["GB/s"],
             (ceiling["best"]["grid"], ceiling["best"]["loads_per_thread"]), ceiling["best"]["us"],
             ceiling["d2d_copy"]["us"]))
 
@@ -623,6 +729,7 @@ def main() -> int:
     if not args.no_rows:
         rows["dequantize"] = b.dequant()
         rows["gather"] = b.gather()
+        rows["gemv_m1_n65536"] = b.gemv1_wide()
         rows["gemv_m8"] = b.gemv8()
         rows["mfma_m512"] = b.mfma()
         if not args.no_context:
@@ -655,7 +762,9 @@ def main() -> int:
                    "algorithmic_bytes_per_step": g["bytes"], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("k_gemv_m1")},
-        "step_us": dict(dist_us(dist), graph_replay=round(graph_s * 1e6, 3)),
+        "timing": "the %d steps issued back to back behind a GPU spin (queued before the first starts), cold "
+                  "weights, events on the launch stream" % args.steps,
+        "step_us": {"graph_replay": round(graph_s * 1e6, 3), "host_paced_runs_of_20": dist_us(dist)},
         "read_ceiling": ceiling,
         "cpu_baseline": {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
                          "sample": "the whole decode GEMV workload (M=1, N=K=4096), %d calls of the f64 "
