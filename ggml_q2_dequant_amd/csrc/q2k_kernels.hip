@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "q2k_launch.h"
 
 namespace q2k {
@@ -178,38 +180,66 @@ struct GemvRoute {
 // before any arithmetic, so the workgroup's whole share of the matrix is in
 // flight at once.
 //
-// Codes leave the bytes as e4m3 values four at a time: a byte masked with
-// 0x03 is q * 2^-9 (a subnormal) and a byte masked with 0x0C is 4q * 2^-9 =
-// q * 2^-7, both exact, so positions 0 and 1 need only a mask and positions 2
-// and 3 the same masks after one 4-bit shift. Per sub-block the lane forms
-// T = sum q*x; the row gains d * sc * T - dmin * mn * sum(x). Partial sums are
-// reduced over the 16 lanes of a row with DPP and over the four wavefronts
-// through LDS, in a fixed order.
+// The lane's arithmetic per row is segment_value (below): T = sum q*x per
+// sub-block, then d * (sum sc * T) - dmin * (sum mn * S), S = sum x over the
+// sub-block. The four lanes of a (block, segment) hold the same activations,
+// so each computes one of their four sums S (pairwise) and they meet in LDS.
+// Partial sums are reduced over the 16 lanes of a row with DPP and over the
+// four wavefronts through LDS, in a fixed order.
+//
+// Error bound (first order, u = 2^-24): every term of the result passes
+// through at most 16 roundings in T (the first FMA adds to +0), 4 in the sc
+// sum, 1 each in the FMAs with d and dmin, 2 per further K chunk of 4096 in
+// the running sum, 4 in the DPP row sum and 3 in the wavefront sum; the min
+// terms through fewer. So
+//   |y - exact| <= (27 + 2 * ceil(K / 4096)) u * B,
+//   B = sum_k |x[k]| * (|d * sc * q| + |dmin * mn|),
+// as long as the scaled sums T (q x times 4^p 2^-24) stay in f32's normal range
+// (activations above about 2^-100 where they meet non-zero codes). B equals
+// sum_k |x * w| unless a block's code and min terms cancel; the 1e-5 * sum|x w|
+// rule holds whenever B is within 5.5x of sum |x w| (K <= 4096).
 // Row quadruples per workgroup. Four (16 rows) keep a decode-sized matrix
 // (N = 4096: 256 workgroups) spread over every CU; once a launch has at least
-// two 24-row workgroups per CU, six (24 rows) amortize each workgroup's
-// activation loads and reduction over more rows (expert-routed decode over
-// 6 x 14336 rows: 33 us against 39 us). A row's arithmetic does not depend on
-// the choice, so both give bit-identical rows.
-constexpr int kSegItersSmall = 4, kSegItersLarge = 6;
+// two large workgroups per CU, more rows per workgroup amortize its activation
+// loads, sub-block sums and reduction: eight (32 rows) for M = 1, six (24
+// rows) for M = 2, whose registers would not hold eight. A row's arithmetic
+// does not depend on the choice, so all give bit-identical rows.
+constexpr int kSegItersSmall = 4;
+template <int M>
+constexpr int kSegItersLarge = M == 1 ? 8 : 6;
 constexpr uint64_t kSegLargeMinWorkgroups = 512;
-static_assert(4ull * kSegItersLarge * (kMaxK / 256) * 84 < (1ull << 31), "a workgroup's rows fit a 31-bit offset");
+static_assert(4ull * kSegItersLarge<1> * (kMaxK / 256) * 84 < (1ull << 31), "a workgroup's rows fit a 31-bit offset");
 
+template <int M>
 inline bool seg_iters_large(uint32_t N, uint64_t problems) {
-    return static_cast<uint64_t>((N + 4 * kSegItersLarge - 1) / (4 * kSegItersLarge)) * problems >=
+    return static_cast<uint64_t>((N + 4 * kSegItersLarge<M> - 1) / (4 * kSegItersLarge<M>)) * problems >=
            kSegLargeMinWorkgroups;
 }
 
-__device__ __forceinline__ void e4m3x4(uint32_t c, float *q) {
-    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c), false);
-    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c), true);
-    q[0] = lo[0];
-    q[1] = lo[1];
-    q[2] = hi[0];
-    q[3] = hi[1];
+// Bytes 0, 1 (W = false) or 2, 3 (W = true) of v, each below 16, as exact integers.
+template <bool W>
+__device__ __forceinline__ void nibbles2(uint32_t v, float *a, float *b) {
+    const auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(static_cast<int>(v), 512.0f, W);
+    *a = r[0];
+    *b = r[1];
 }
 
-// Sum over each 16-lane DPP row; every lane of the row receives the total.
+// acc + f16(half H of codes) * x in one v_fma_mix_f32 (the f16 widening is
+// exact, so this is fma(f32(code), x, acc)); written out so that every code
+// meets every activation row through this one instruction.
+template <int H>
+__device__ __forceinline__ float fma_code(uint32_t codes, float x, float acc) {
+    float r;
+    if constexpr (H == 1)
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(codes), "v"(x), "v"(acc));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(codes), "v"(x), "v"(acc));
+    return r;
+}
+
+// Sum over each 16-lane DPP row; every lane of the row receives the total,
+// though not every lane the same association of it (lane i adds the quads in
+// the order its row_ror steps meet them).
 __device__ __forceinline__ float row16_sum(float v) {
     v += dpp<kDppQuadXor1>(v);
     v += dpp<kDppQuadXor2>(v);
@@ -236,6 +266,64 @@ __device__ __forceinline__ SegLoads load_seg(__amdgpu_buffer_rsrc_t rs, uint32_t
     return t;
 }
 
+// One lane's share of one weight row: the 64 weights of its code segment
+// (sub-blocks 8h + 2p + s, p = 0..3, of one block) against its activations
+// xv[m][p][i] (element i of sub-block p) and their sums xs[m][p], added to
+// acc[m] as acc + d * (sum_p sc_p T_p) - dmin * (sum_p mn_p S_p), T_p = sum_i q x.
+// Both M <= 2 kernels use exactly this arithmetic, so a row comes out
+// bit-identical from either. scsel picks the lane's four scale bytes.
+//
+// Codes never pass through a conversion instruction: masked in place within a
+// 16-bit half (0x0003 << 2p), a code is the f16 subnormal q * 4^p * 2^-24,
+// which v_fma_mix_f32 multiplies by an f32 activation exactly (the odd code
+// bytes reach the low byte of a half by one 8-bit shift). T_p is thus carried
+// scaled by 4^p 2^-24, and the scale nibbles, converted with the power-of-two
+// scales 2^33 and 2^29 (times 4^-1 for positions 1 and 3), carry it back
+// exactly.
+template <int M>
+__device__ __forceinline__ void segment_value(const SegLoads &L, const float (&xv)[M][4][16],
+                                              const float (&xs)[M][4], uint32_t scsel, float (&acc)[M]) {
+    float t[M][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t v = L.q[j], u = v >> 8;  // u: the odd bytes in the low byte of each half
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t mask = 0x00030003u << (2 * p);
+            const uint32_t me = v & mask, mo = u & mask;  // bytes 4j, 4j+2 and 4j+1, 4j+3 of the segment
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float a = fma_code<0>(me, xv[m][p][4 * j], j == 0 ? 0.0f : t[m][p]);
+                a = fma_code<0>(mo, xv[m][p][4 * j + 1], a);
+                a = fma_code<1>(me, xv[m][p][4 * j + 2], a);
+                t[m][p] = fma_code<1>(mo, xv[m][p][4 * j + 3], a);
+            }
+        }
+    }
+    // Scale bytes 8h + 2p + s (p = 0..3): bytes s, 2 + s of the half's two scale dwords, gathered into one
+    // dword; low nibbles sc, high nibbles mn.
+    const uint32_t sb = __builtin_amdgcn_perm(L.sc[1], L.sc[0], scsel);
+    const uint32_t lo = sb & 0x0F0F0F0Fu, hi = (sb >> 4) & 0x0F0F0F0Fu;
+    const auto s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(static_cast<int>(lo), 8589934592.0f, false);  // sc 2^24
+    const auto s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(static_cast<int>(lo), 536870912.0f, true);   // sc 2^20
+    const float sc[4] = {s01[0], s01[1] * 0.25f, s23[0], s23[1] * 0.25f};  // sc_p 2^(24 - 2p)
+    float mn[4];
+    nibbles2<false>(hi, &mn[0], &mn[1]);
+    nibbles2<true>(hi, &mn[2], &mn[3]);
+    const float d = f16_low(L.dd), dmin = f16_high(L.dd);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        float codes = sc[0] * t[m][0];
+#pragma unroll
+        for (int p = 1; p < 4; ++p) codes = __builtin_fmaf(sc[p], t[m][p], codes);
+        float mins = mn[0] * xs[m][0];
+#pragma unroll
+        for (int p = 1; p < 4; ++p) mins = __builtin_fmaf(mn[p], xs[m][p], mins);
+        const float a = __builtin_fmaf(d, codes, acc[m]);
+        acc[m] = __builtin_fmaf(-dmin, mins, a);
+    }
+}
+
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 // Wait until at most N vector-memory operations of this wavefront are still in
@@ -252,7 +340,11 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
                                                   float *__restrict__ y, uint32_t N, uint32_t K, GemvBatch bt,
                                                   GemvRoute rt) {
     __shared__ float red[4][NI * 4 * M];
-    __shared__ __attribute__((aligned(16))) float xl[4][M][1024];  // per wavefront: x of its four blocks
+    // Per wavefront: x of its four blocks, block j at float 260 j so that the lanes' 16-byte reads of
+    // different blocks fall in different bank groups.
+    constexpr uint32_t kXB = 260;
+    __shared__ __attribute__((aligned(16))) float xl[4][M][4 * kXB];
+    __shared__ __attribute__((aligned(16))) float xsum[4][M][64];  // per wavefront: S of its 64 sub-blocks
     const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1);
     const uint32_t row0 = blockIdx.x * (4 * NI);
     if constexpr (kRouted) {
@@ -274,6 +366,7 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
     }
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const uint32_t rr = lane >> 4, bq = (lane >> 2) & 3u, g = lane & 3u, h = g >> 1, s = g & 1u;
+    const uint32_t scsel = 0x06040200u + 0x01010101u * s;  // scale bytes s, 2 + s of each scale dword
     const uint32_t nb = K >> 8;
     const uint32_t row_bytes = nb * kBlockBytes;
 
@@ -316,7 +409,7 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
                 // kernel stub when the LDS load takes an element of xr.)
                 const __amdgpu_buffer_rsrc_t xm = xr[m];
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    xm, (__attribute__((address_space(3))) void *)(xl[wave][m] + 256u * j), 16,
+                    xm, (__attribute__((address_space(3))) void *)(xl[wave][m] + kXB * j), 16,
                     static_cast<int>(u + 16u * lane), 0, 0, 0);
             }
         __builtin_amdgcn_sched_barrier(0);
@@ -329,84 +422,245 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
         vm_wait<3u * NI>();
         __builtin_amdgcn_sched_barrier(0);
         float xv[M][4][16], xs[M][4];
+        // S of sub-block 8h + 2p + s for p = rr: the lane's own quarter of the four sums its (block,
+        // segment) needs, summed pairwise in element order, then exchanged through LDS ([bq][g][p]).
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4v t4 = *reinterpret_cast<const f32x4v *>(xl[wave][m] + bq * kXB + 128u * h + 16u * s +
+                                                                   32u * rr + 4u * i);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[4 * i + c] = t4[c];
+            }
+            float s2[8], s4[4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s2[i] = v[2 * i] + v[2 * i + 1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s4[i] = s2[2 * i] + s2[2 * i + 1];
+            xsum[wave][m][16u * bq + 4u * g + rr] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        }
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int p = 0; p < 4; ++p)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const f32x4v v = *reinterpret_cast<const f32x4v *>(xl[wave][m] + bq * 256u + 128u * h + 16u * s +
+                    const f32x4v v = *reinterpret_cast<const f32x4v *>(xl[wave][m] + bq * kXB + 128u * h + 16u * s +
                                                                       32u * p + 4u * i);
 #pragma unroll
                     for (int c = 0; c < 4; ++c) xv[m][p][4 * i + c] = v[c];
                 }
+        // The sums were written by other lanes of this wavefront; its LDS operations complete in order.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const f32x4v t4 = *reinterpret_cast<const f32x4v *>(&xsum[wave][m][16u * bq + 4u * g]);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) xs[m][p] = t4[p];
+        }
         // Keep the scheduler from sinking these loads towards their uses.
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                float t = xv[m][p][0];
-#pragma unroll
-                for (int i = 1; i < 16; ++i) t += xv[m][p][i];
-                xs[m][p] = t;
-            }
 
 #pragma unroll
-        for (int it = 0; it < NI; ++it) {
-            const SegLoads &cur = wl[it];
-            // q[p][i]: code of byte i at position p, as q * 2^-9 (p even) or q * 2^-7 (p odd).
-            float q[4][16];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t v = cur.q[j], u = v >> 4;
-                e4m3x4(v & 0x03030303u, &q[0][4 * j]);
-                e4m3x4(v & 0x0C0C0C0Cu, &q[1][4 * j]);
-                e4m3x4(u & 0x03030303u, &q[2][4 * j]);
-                e4m3x4(u & 0x0C0C0C0Cu, &q[3][4 * j]);
-            }
-            // Scale bytes 8h + 2p + s: bytes s and 2 + s of each scale dword.
-            const uint32_t u0 = cur.sc[0] >> (8 * s), u1 = cur.sc[1] >> (8 * s);
-            const uint32_t lo0 = u0 & 0x000F000Fu, hi0 = (u0 >> 4) & 0x000F000Fu;
-            const uint32_t lo1 = u1 & 0x000F000Fu, hi1 = (u1 >> 4) & 0x000F000Fu;
-            const float sc[4] = {static_cast<float>(lo0 & 0xffu), static_cast<float>(lo0 >> 16),
-                                 static_cast<float>(lo1 & 0xffu), static_cast<float>(lo1 >> 16)};
-            const float mn[4] = {static_cast<float>(hi0 & 0xffu), static_cast<float>(hi0 >> 16),
-                                 static_cast<float>(hi1 & 0xffu), static_cast<float>(hi1 >> 16)};
-            const float d = f16_low(cur.dd), dmin = f16_high(cur.dd);
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float t[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    float a = q[p][0] * xv[m][p][0];
-#pragma unroll
-                    for (int i = 1; i < 16; ++i) a = __builtin_fmaf(q[p][i], xv[m][p][i], a);
-                    t[p] = a;
-                }
-                const float even = __builtin_fmaf(sc[2], t[2], sc[0] * t[0]);  // scaled by 2^-9
-                const float odd = __builtin_fmaf(sc[3], t[3], sc[1] * t[1]);   // scaled by 2^-7
-                const float codes = __builtin_fmaf(even, 512.0f, odd * 128.0f);
-                float mins = mn[0] * xs[m][0];
-#pragma unroll
-                for (int p = 1; p < 4; ++p) mins = __builtin_fmaf(mn[p], xs[m][p], mins);
-                const float a = __builtin_fmaf(d, codes, acc[it][m]);
-                acc[it][m] = __builtin_fmaf(-dmin, mins, a);
-            }
-        }
+        for (int it = 0; it < NI; ++it) segment_value<M>(wl[it], xv, xs, scsel, acc[it]);
     }
 
 #pragma unroll
     for (int it = 0; it < NI; ++it)
 #pragma unroll
         for (int m = 0; m < M; ++m) {
+            // The lanes of a DPP row end with differently associated sums: lane 15's is the one
+            // k_gemv_rows combines, so it is the one published here too.
             const float v = row16_sum(acc[it][m]);
-            if ((lane & 15u) == 0) red[wave][(it * 4 + rr) * M + m] = v;
+            if ((lane & 15u) == 15u) red[wave][(it * 4 + rr) * M + m] = v;
         }
     __syncthreads();
     if (tid < NI * 4 * M) {
         const uint32_t r = tid / M, m = tid % M, n = row0 + r;
         if (n < N) y[static_cast<uint64_t>(m) * N + n] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 GEMV for M <= 2 and K <= 4096: persistent wavefronts that stream rows.
+//
+// Lane l of a wavefront owns block l / 4 of a row (K <= 4096 is at most 16
+// blocks) and code segment g = l % 4 of it: the 16 code bytes qs[32h + 16s ..]
+// with h = g / 2, s = g % 2, at all four 2-bit positions p, that is sub-blocks
+// 8h + 2p + s (64 weights). A wavefront therefore covers whole rows and sums
+// each one within itself (DPP), with no barrier between wavefronts. The
+// lane's 64 activations and its four sub-block sums S are the same for every
+// row: they come once from x staged in LDS by the workgroup and stay in
+// registers while the wavefront walks its row groups (kRowsPerGroup rows;
+// group i, i + W, i + 2W, ... for the W wavefronts of the problem), loading
+// the next group's weights while it computes the current one. The host sizes
+// the grid to the workgroups the chip holds at once.
+//
+// Per row the lane adds segment_value, the same arithmetic as k_gemv_seg, and
+// the 64-lane sum follows k_gemv_seg's order (16 lanes by DPP, then the four
+// 16-lane rows in order), so the two kernels give bit-identical rows and the
+// same error bound, |y - exact| <= 29 u * B (K <= 4096).
+constexpr uint32_t kRowsPerGroup = 4;
+
+template <int M, bool kRouted>
+__global__ __launch_bounds__(256) void k_gemv_rows(const float *__restrict__ x, const uint8_t *__restrict__ w,
+                                                   float *__restrict__ y, uint32_t N, uint32_t K, GemvBatch bt,
+                                                   GemvRoute rt) {
+    constexpr uint32_t R = kRowsPerGroup;
+    // Block b's 256 activations at float 260 b: a 16-byte read by the lanes of all 16 blocks then spreads
+    // over the 16 groups of four banks (256 apart they would all share one group per segment parity).
+    constexpr uint32_t kXB = 260;
+    __shared__ __attribute__((aligned(16))) float xl[M][16 * kXB];
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if constexpr (kRouted) {
+        static_assert(M == 1, "routes are single activation rows");
+        const uint32_t r = rt.route0 + blockIdx.y;
+        const uint32_t e = rt.ids[r];
+        y += static_cast<uint64_t>(r) * N;
+        if (e >= rt.n_experts) {
+            for (uint32_t n = blockIdx.x * 256u + tid; n < N; n += gridDim.x * 256u) y[n] = __builtin_nanf("");
+            if (blockIdx.x == 0 && tid == 0 && rt.status)
+                __hip_atomic_store(rt.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            return;
+        }
+        x += static_cast<uint64_t>(r / rt.x_div) * K;
+        w += e * rt.expert_stride;
+    } else {
+        x += blockIdx.y * bt.x_elems;
+        w += blockIdx.y * bt.w_bytes;
+        y += blockIdx.y * bt.y_elems;
+    }
+    const uint32_t nb = K >> 8, row_bytes = nb * kBlockBytes;
+    const uint32_t groups = (N + R - 1) / R;
+    const uint32_t b = lane >> 2, g = lane & 3u, h = g >> 1, s = g & 1u;
+    // Lanes past the row's last block aim their loads beyond every descriptor (they read zeros).
+    const uint32_t loff = b < nb ? b * kBlockBytes : 0x80000000u;
+
+    // x of the whole row (16 blocks of 256 floats per activation row, zeros past K) into LDS: each wavefront
+    // copies blocks wave, wave + 4, wave + 8, wave + 12 (one 1 KiB load each), issued before any weight load.
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x + static_cast<uint64_t>(m) * K, K * 4u);
+#pragma unroll
+        for (uint32_t j = 0; j < 4; ++j) {
+            const uint32_t blk = 4u * j + wave;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void *)(xl[m] + kXB * blk),
+                                                     16, static_cast<int>(1024u * blk + 16u * lane), 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Group i holds rows R i .. R i + R - 1; one descriptor spans them (rows past N read zeros).
+    auto load_group = [&](SegLoads (&L)[R], uint32_t grp) __attribute__((always_inline)) {
+        const uint32_t n0 = grp * R;
+        const uint32_t nrows = N - n0 < R ? N - n0 : R;
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w + static_cast<uint64_t>(n0) * row_bytes, nrows * row_bytes);
+#pragma unroll
+        for (uint32_t r = 0; r < R; ++r) L[r] = load_seg(rs, r * row_bytes + loff, g, h);
+    };
+
+    const uint32_t W = gridDim.x * 4u;
+    uint32_t grp = blockIdx.x * 4u + wave;
+    SegLoads A[R], B[R];
+    if (grp < groups) load_group(A, grp);
+    __builtin_amdgcn_sched_barrier(0);
+    // Loads complete in issue order: the x copies are in once the group's weight loads alone are in flight.
+    if (grp < groups) vm_wait<3 * R>();
+    else vm_wait<0>();
+    __syncthreads();
+
+    // The lane's activations: element i of sub-block p is x[256 b + 128 h + 32 p + 16 s + i].
+    float xv[M][4][16], xs[M][4];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4v v = *reinterpret_cast<const f32x4v *>(xl[m] + kXB * b + 128u * h + 32u * p + 16u * s +
+                                                                  4u * i);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) xv[m][p][4 * i + c] = v[c];
+            }
+            float s2[8], s4[4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s2[i] = xv[m][p][2 * i] + xv[m][p][2 * i + 1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s4[i] = s2[2 * i] + s2[2 * i + 1];
+            xs[m][p] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        }
+    const uint32_t scsel = 0x06040200u + 0x01010101u * s;
+
+    // Sum over the 64 lanes: each DPP row (blocks 4r .. 4r + 3) as the chunked kernel sums a wavefront, then
+    // ((r0 + r1) + r2) + r3 as it adds its wavefronts: row 1 takes row 0's lane 15, row 2 row 1's lane 31,
+    // row 3 row 2's lane 47 (the other rows add +0, and no lane value is -0). Lane 63 holds the total.
+    auto wave_sum = [&](float v) __attribute__((always_inline)) {
+        v = row16_sum(v);
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0x2, 0xF, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0x4, 0xF, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0x8, 0xF, false));
+        return v;
+    };
+
+    // Row r of a group is computed once its three loads are in. Loads and stores
+    // complete in issue order; the group's own later rows and, when a next
+    // group was requested after it, that group's 3R loads may still be in
+    // flight (stores of the previous group, issued in between, are waited for
+    // too: the count leaves them out, which only waits longer).
+    auto compute_group = [&](const SegLoads (&L)[R], uint32_t gi, auto next_in_flight)
+        __attribute__((always_inline)) {
+        constexpr uint32_t kNext = decltype(next_in_flight)::value ? 3 * R : 0;
+        float tot[R][M];
+#pragma unroll
+        for (uint32_t r = 0; r < R; ++r) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (r == 0) vm_wait<3 * (R - 1) + kNext>();
+            else if (r == 1) vm_wait<3 * (R - 2) + kNext>();
+            else if (r == 2) vm_wait<3 * (R - 3) + kNext>();
+            else vm_wait<kNext>();
+            __builtin_amdgcn_sched_barrier(0);
+            float v[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) v[m] = 0.0f;
+            segment_value<M>(L[r], xv, xs, scsel, v);
+#pragma unroll
+            for (int m = 0; m < M; ++m) tot[r][m] = wave_sum(v[m]);
+        }
+#pragma unroll
+        for (uint32_t r = 0; r < R; ++r) {
+            const uint32_t n = gi * R + r;
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                if (lane == 63u && n < N) y[static_cast<uint64_t>(m) * N + n] = tot[r][m];
+        }
+    };
+    static_assert(R == 4, "compute_group spells out the waits of four rows");
+
+    typedef std::integral_constant<bool, true> InFlight;
+    typedef std::integral_constant<bool, false> Drained;
+    while (grp < groups) {
+        const uint32_t g1 = grp + W;
+        if (g1 < groups) {
+            load_group(B, g1);
+            compute_group(A, grp, InFlight{});
+        } else {
+            compute_group(A, grp, Drained{});
+            break;
+        }
+        const uint32_t g2 = g1 + W;
+        if (g2 < groups) {
+            load_group(A, g2);
+            compute_group(B, g1, InFlight{});
+        } else {
+            compute_group(B, g1, Drained{});
+            break;
+        }
+        grp = g2;
     }
 }
 
@@ -1163,11 +1417,48 @@ hipError_t launch_gemv_seg_ni(const float *x, const uint8_t *w, float *y, uint32
     return hipGetLastError();
 }
 
+// Workgroups of k_gemv_rows per problem: enough for every wavefront to take at
+// least one row group, at most what the chip holds at once (occupancy times
+// compute units) shared among the problems of the launch. Returns 0 when the
+// launch is too small for every wavefront to stream two or more groups: then
+// the per-wavefront setup (activations, sub-block sums, the workgroup barrier)
+// is not amortized and k_gemv_seg, which splits K over the wavefronts of a
+// workgroup instead, is faster (decode M = 1, N = K = 4096: 4.1 us against
+// 4.7 us; M = 1, N = 65536: 24.4 us against 22.9 us the other way).
+template <int M, bool kRouted>
+uint32_t rows_grid(uint32_t N, uint32_t problems) {
+    static const int per_cu = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(k_gemv_rows<M, kRouted>),
+                                                         256, 0) != hipSuccess || n < 1)
+            n = 1;
+        return n;
+    }();
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus < 1)
+        cus = 256;
+    const uint64_t groups = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const uint64_t want = (groups + 3) / 4;
+    const uint64_t cap = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
+    if (groups * problems < 2 * 4 * cap) return 0;
+    const uint64_t per = cap / problems;
+    const uint64_t g = want < per ? want : per;
+    return static_cast<uint32_t>(g > 0 ? g : 1);
+}
+
 template <int M>
 hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, uint32_t batches,
                            GemvBatch bt, hipStream_t stream) {
-    return seg_iters_large(N, batches) ? launch_gemv_seg_ni<M, kSegItersLarge>(x, w, y, N, K, batches, bt, stream)
-                                       : launch_gemv_seg_ni<M, kSegItersSmall>(x, w, y, N, K, batches, bt, stream);
+    const uint32_t rg = K <= 4096u ? rows_grid<M, false>(N, batches) : 0;
+    if (rg > 0) {
+        hipLaunchKernelGGL((k_gemv_rows<M, false>), dim3(rg, batches), dim3(256), 0, stream, x, w, y, N, K, bt,
+                           GemvRoute{});
+        return hipGetLastError();
+    }
+    return seg_iters_large<M>(N, batches)
+               ? launch_gemv_seg_ni<M, kSegItersLarge<M>>(x, w, y, N, K, batches, bt, stream)
+               : launch_gemv_seg_ni<M, kSegItersSmall>(x, w, y, N, K, batches, bt, stream);
 }
 
 }  // namespace
@@ -1233,13 +1524,30 @@ hipError_t launch_gemm_mfma(const float *x, const uint8_t *w, float *y, uint32_t
 hipError_t launch_moe_gemv(const float *x, const uint8_t *w, const uint32_t *ids, float *y, uint32_t routes,
                            uint32_t x_div, uint32_t N, uint32_t K, uint32_t n_experts, uint64_t expert_stride,
                            int *status, hipStream_t stream) {
-    const bool large = seg_iters_large(N, routes);
-    const uint32_t rows = 4 * (large ? kSegItersLarge : kSegItersSmall), blocks = (N + rows - 1) / rows;
+    if (K <= 4096u && rows_grid<1, true>(N, routes < kMaxGridY ? routes : kMaxGridY) > 0) {
+        for (uint32_t r0 = 0; r0 < routes; r0 += kMaxGridY) {
+            const uint32_t nr = routes - r0 < kMaxGridY ? routes - r0 : kMaxGridY;
+            const uint32_t rg = rows_grid<1, true>(N, nr);
+            const GemvRoute rt{ids, status, expert_stride, r0, x_div, n_experts};
+            if (rg > 0)
+                hipLaunchKernelGGL((k_gemv_rows<1, true>), dim3(rg, nr), dim3(256), 0, stream, x, w, y, N, K,
+                                   GemvBatch{}, rt);
+            else
+                hipLaunchKernelGGL((k_gemv_seg<1, kSegItersSmall, true>), dim3((N + 4 * kSegItersSmall - 1) /
+                                                                               (4 * kSegItersSmall), nr),
+                                   dim3(256), 0, stream, x, w, y, N, K, GemvBatch{}, rt);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    const bool large = seg_iters_large<1>(N, routes);
+    const uint32_t rows = 4 * (large ? kSegItersLarge<1> : kSegItersSmall), blocks = (N + rows - 1) / rows;
     for (uint32_t r0 = 0; r0 < routes; r0 += kMaxGridY) {
         const uint32_t nr = routes - r0 < kMaxGridY ? routes - r0 : kMaxGridY;
         const GemvRoute rt{ids, status, expert_stride, r0, x_div, n_experts};
         if (large)
-            hipLaunchKernelGGL((k_gemv_seg<1, kSegItersLarge, true>), dim3(blocks, nr), dim3(256), 0, stream, x, w, y,
+            hipLaunchKernelGGL((k_gemv_seg<1, kSegItersLarge<1>, true>), dim3(blocks, nr), dim3(256), 0, stream, x, w, y,
                                N, K, GemvBatch{}, rt);
         else
             hipLaunchKernelGGL((k_gemv_seg<1, kSegItersSmall, true>), dim3(blocks, nr), dim3(256), 0, stream, x, w, y,

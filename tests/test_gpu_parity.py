@@ -280,6 +280,38 @@ def test_gemv_ragged_shapes(M, N, K):
     check_gemv(y, x, blocks, M, N, K)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 40001, 1024), (2, 33333, 768), (1, 70003, 4096), (2, 9999, 3840),
+                                   (1, 5, 256), (2, 4, 512)])
+def test_gemv_streaming_rows_many_groups_per_wavefront(M, N, K):
+    # M <= 2 with K <= 4096 runs wavefronts that each stream several 4-row groups
+    # (the grid is capped at what the chip holds): large ragged N walks that loop
+    # and its last partial group; K below 4096 leaves lanes without a block.
+    rng = np.random.Generator(np.random.PCG64(M * 7 + N + K))
+    blocks = synth.random_blocks(rng, N * K // QK_K)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    y = gpu_matmul(x, blocks, M, N, K)
+    check_gemv(y, x, blocks, M, N, K)
+    if M == 2:
+        for m in range(2):
+            assert bits_equal(gpu_matmul(x[m:m + 1], blocks, 1, N, K), y[m:m + 1])
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_streaming_and_chunked_kernels_agree_bitwise(M):
+    # A large launch streams rows through persistent wavefronts; a 4096-row call
+    # splits K over the wavefronts of a workgroup. Both run the same per-lane
+    # arithmetic and summation order, so the shared rows must match bit for bit
+    # (that is what keeps routed and batched rows equal to single calls).
+    N, K, n_small = 40000, 4096, 4096
+    rng = np.random.Generator(np.random.PCG64(4200 + M))
+    blocks = synth.random_blocks(rng, N * K // QK_K)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    y_big = gpu_matmul(x, blocks, M, N, K)
+    y_small = gpu_matmul(x, blocks[:n_small * (K // QK_K) * BB], M, n_small, K)
+    assert bits_equal(y_big[:, :n_small], y_small)
+    check_gemv(y_small, x, blocks[:n_small * (K // QK_K) * BB], M, n_small, K)
+
+
 @pytest.mark.parametrize("M", [3, 8])
 def test_gemv_wide_dynamic_range_activations(M):
     # 3 <= M <= 8 splits each row of each 256-column block into two f16 pieces
