@@ -100,10 +100,26 @@ q2k_status q2k_dequantize(const void *blocks, size_t blocks_bytes, float *out, s
  *   w  device Q2_K bytes, N * K/256 * 84 long (layout above); 4-byte aligned.
  *   y  device f32 [M, N] row-major; 16-byte aligned.
  *   M, N >= 1; K a multiple of 256 with 256 <= K <= 2^21.
- * M <= 8 runs the fp32-accurate GEMV: |y - exact| <= 1e-5 * sum_k |x*w| per
- * output. M <= 2 uses fp32 FMAs; 3 <= M <= 8 uses the matrix cores on exact
- * f16 encodings of the weights' integer parts and a two-piece f16 split of x,
- * built inside the kernel (no workspace).
+ * M <= 8 runs an fp32 GEMV (no workspace). Both forms compute each block as
+ * d * sum(x * sc*q) - dmin * sum_s(mn_s * sum_{k in s} x), so their error is
+ * stated against B = sum_k |x[k]| * (|d*sc*q| + |dmin*mn|), which equals
+ * A = sum_k |x*w| unless a block's code and min terms cancel:
+ *  - M <= 2 (fp32 FMAs on exact encodings of the codes):
+ *      |y - exact| <= (27 + 2*ceil(K/4096)) * 2^-24 * B  (first order),
+ *    for activations above about 2^-100 wherever they meet a non-zero code.
+ *    This is within 1e-5 * A whenever B <= 5.5 * A (K <= 4096). A block whose
+ *    weights are all exactly zero still contributes up to that bound times its B.
+ *  - 3 <= M <= 8 (matrix cores on exact f16 encodings of sc*q and of mn, x
+ *    scaled per block row and split into two f16 pieces): the matrix cores
+ *    sum the 32 products of each step within a window of about 2^16 below
+ *    its largest product, and the split keeps about 22 bits of each
+ *    activation above 2^-34 of its block row's largest. So
+ *      |y - exact| <= 2^-18 * B + 2^-6 * sum_b max_{k in b}|x[k]| *
+ *                     (max_{k in b} |d*sc*q| + 16 * max_{s in b} |dmin*mn_s|),
+ *    which is within 1e-5 * A as for M <= 2 whenever the activations of each
+ *    256-weight block span less than 2^10 in magnitude (every product then
+ *    lies inside the window); beyond that small activations lose precision
+ *    relative to their block's largest.
  * A row of y depends only on its own row of x: calls with the same M give it
  * bit-identical values whatever the other rows hold (M <= 2 and 3 <= M <= 8
  * run different kernels and may differ in the last bits).
@@ -200,7 +216,7 @@ q2k_status q2k_matmul_batched(const float *x, const void *w, float *y, uint32_t 
  * 1 <= n_experts <= 512; n_tokens * top_k <= 2^24; expert_stride a multiple
  * of 4 and >= n * k/256 * 84. Outputs may not overlap inputs (or each other).
  * Two schedules compute it:
- *   - fp32 mat-vec per route (Q2K_PATH_GEMV): |y - exact| <= 1e-5 * sum|x*w|;
+ *   - fp32 mat-vec per route (Q2K_PATH_GEMV): the M <= 2 bound of q2k_matmul;
  *     route r's row is bit-identical to q2k_matmul(x row, W_e, M = 1).
  *   - matrix-core (Q2K_PATH_MFMA): routes grouped by expert in increasing
  *     route order, bf16(x) * bf16(w) with fp32 accumulation in tiles of up to

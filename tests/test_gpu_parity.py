@@ -593,3 +593,130 @@ def test_read_probe_reads_every_word():
     assert probe.q2k_probe_read(d.data_ptr(), 20, sink.data_ptr(), sink.numel(), 0, 4, None) == 1
     assert probe.q2k_probe_read(d.data_ptr(), 64, sink.data_ptr(), 8, 16, 4, None) == 1
     assert probe.q2k_probe_read(d.data_ptr(), 64, sink.data_ptr(), sink.numel(), 0, 3, None) == 1
+
+
+# ----------------------------------------------------------------- the fp32 GEMV's error bound at its edges
+
+def _code_min_magnitudes(blocks, N, K):
+    """Per weight: |d*sc*q| and |dmin*mn| (f64), from the Q2_K record layout (scales @0, codes @16, d @80, dmin @82)."""
+    b = np.asarray(blocks, np.uint8).reshape(N, K // QK_K, BB)
+    d = b[:, :, 80:82].copy().view(np.float16)[:, :, 0].astype(np.float64)
+    dmin = b[:, :, 82:84].copy().view(np.float16)[:, :, 0].astype(np.float64)
+    e = np.arange(QK_K)
+    sbyte = b[:, :, e // 16].astype(np.int64)
+    code = (b[:, :, 16 + 32 * (e // 128) + e % 32].astype(np.int64) >> (2 * ((e // 32) % 4))) & 3
+    codes = np.abs(d[:, :, None] * (sbyte & 15) * code).reshape(N, K)
+    mins = np.abs(dmin[:, :, None] * (sbyte >> 4)).reshape(N, K)
+    return codes, mins
+
+
+def _b_bound(x, blocks, M, N, K):
+    """B[m, n] = sum_k |x[m, k]| * (|d*sc*q| + |dmin*mn|): what the M <= 2 kernels' error is relative to."""
+    codes, mins = _code_min_magnitudes(blocks, N, K)
+    return np.abs(np.asarray(x, np.float64)).reshape(M, K) @ (codes + mins).T
+
+
+def _m2_bound(K):
+    return (27 + 2 * ((K + 4095) // 4096)) * 2.0 ** -24
+
+
+def _m8_bound(x, blocks, M, N, K):
+    """The 3 <= M <= 8 bound: 2^-18 B + 2^-6 sum_b max_k|x| (max_k |d*sc*q| + 16 max_s |dmin*mn|)."""
+    codes, mins = _code_min_magnitudes(blocks, N, K)
+    nb = K // QK_K
+    xmax = np.abs(np.asarray(x, np.float64)).reshape(M, nb, QK_K).max(axis=2)              # [M, blocks]
+    wmax = codes.reshape(N, nb, QK_K).max(axis=2) + 16 * mins.reshape(N, nb, QK_K).max(axis=2)  # [N, blocks]
+    return 2.0 ** -18 * _b_bound(x, blocks, M, N, K) + 2.0 ** -6 * xmax @ wmax.T
+
+
+def _block(d, dmin, scale_byte, code_byte):
+    blk = np.zeros(BB, np.uint8)
+    blk[0:16] = scale_byte
+    blk[16:80] = code_byte
+    blk[80:82] = np.frombuffer(np.float16(d).tobytes(), np.uint8)
+    blk[82:84] = np.frombuffer(np.float16(dmin).tobytes(), np.uint8)
+    return blk
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_blocks_whose_weights_cancel_to_zero(M):
+    # d*sc*q == dmin*mn for every element (d = dmin = 1, sc = mn = 2, every code 1, or sc = 1, mn = 3, every code 3):
+    # each weight is exactly 0, so sum |x*w| = 0, but the factored form d*sum(sc*q*x) - dmin*sum(mn*x) rounds its
+    # two sums separately. The result must stay within the stated bound against B, which is not zero.
+    rng = np.random.Generator(np.random.PCG64(4400 + M))
+    N, K = 24, 1024
+    zero_a = _block(1.0, 1.0, 0x22, 0x55)   # sc 2, mn 2, codes 1
+    zero_b = _block(0.5, 0.5, 0x31, 0xFF)   # sc 1, mn 3, codes 3: d*1*3 = dmin*3
+    blocks = np.concatenate([zero_a if (i + j) % 2 else zero_b for i in range(N) for j in range(K // QK_K)])
+    assert np.all(oracle.dequantize(blocks) == 0.0)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    y = gpu_matmul(x, blocks, M, N, K)
+    b = _b_bound(x, blocks, M, N, K)
+    assert np.all(b > 0)
+    assert np.all(np.abs(y.astype(np.float64)) <= _m2_bound(K) * b), "max |y| / B = %g" % np.max(np.abs(y) / b)
+    print("weights all zero, M=%d: max |y| / B = %.3g (bound %.3g)" % (M, np.max(np.abs(y) / b), _m2_bound(K)))
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_near_cancelling_blocks_within_the_stated_bound(M):
+    # Random blocks whose min term nearly cancels the code term (dmin*mn within a few percent of d*sc*q for the
+    # codes present): sum |x*w| is far smaller than B. The M <= 2 bound is stated against B and must hold.
+    rng = np.random.Generator(np.random.PCG64(4500 + M))
+    N, K = 64, 2048
+    blocks = synth.random_blocks(rng, N * K // QK_K).reshape(N * K // QK_K, BB).copy()
+    blocks[:, 16:80] = 0xAA                                             # every code 2
+    sc = rng.integers(1, 16, (blocks.shape[0], 16))
+    blocks[:, 0:16] = (sc | (sc << 4)).astype(np.uint8)                 # mn = sc
+    d = rng.uniform(0.05, 0.2, blocks.shape[0]).astype(np.float16)
+    dmin = (d.astype(np.float64) * 2 * (1 + rng.uniform(-0.03, 0.03, blocks.shape[0]))).astype(np.float16)
+    blocks[:, 80:82] = d.view(np.uint8).reshape(-1, 2)
+    blocks[:, 82:84] = dmin.view(np.uint8).reshape(-1, 2)
+    blocks = blocks.reshape(-1)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    y = gpu_matmul(x, blocks, M, N, K)
+    ref, a = oracle.matmul(x, blocks, M, N, K)
+    b = _b_bound(x, blocks, M, N, K)
+    err = np.abs(y.astype(np.float64) - ref)
+    assert np.all(err <= _m2_bound(K) * b)
+    print("near cancellation, M=%d: B/A up to %.3g, max err/B = %.3g, max err/A = %.3g" % (
+        M, np.max(b / a), np.max(err / b), np.max(err / a)))
+
+
+@pytest.mark.parametrize("M", [3, 8])
+def test_gemv_matrix_cores_meet_the_fp32_rule_within_a_2_pow_10_spread(M):
+    # 3 <= M <= 8: the matrix cores sum the 32 exact products of a step within a window of about 2^16 below its
+    # largest; codes span up to 45 (2^5.5), so activations spanning up to 2^10 inside a 256-weight block keep
+    # every product in the window and the 1e-5 rule holds. Here every block row spans the full 2^10.
+    rng = np.random.Generator(np.random.PCG64(4600 + M))
+    N, K = 300, 4096
+    blocks = synth.random_blocks(rng, N * K // QK_K)
+    mag = 2.0 ** rng.uniform(-10, 0, (M, K))
+    mag[:, ::256] = 1.0                                                 # each block row reaches its top
+    x = (mag * rng.choice([-1.0, 1.0], (M, K))).astype(np.float32)
+    y = gpu_matmul(x, blocks, M, N, K)
+    worst = check_gemv(y, x, blocks, M, N, K)
+    print("matrix-core GEMV, activations spanning 2^10 per block, M=%d: max err/A = %.3g" % (M, worst))
+
+
+@pytest.mark.parametrize("M", [3, 8])
+def test_gemv_matrix_cores_beyond_the_window_lose_only_small_products(M):
+    # The case the fp32 rule does not cover for 3 <= M <= 8: each block row's largest activation sits on a zero
+    # weight and the others are 1e-7 of it, so the activations that count are split into f16 pieces far below
+    # the block's scale. The stated bound is relative to the block maxima:
+    #   |y - exact| <= 2^-18 B + 2^-6 sum_b max_k|x| (max_k |d*sc*q| + 16 max_s |dmin*mn|).
+    rng = np.random.Generator(np.random.PCG64(4700 + M))
+    N, K = 64, 1024
+    blocks = synth.random_blocks(rng, N * K // QK_K).reshape(N, K // QK_K, BB).copy()
+    blocks[:, :, 16] &= 0xFC                                            # element 0 of each block: code 0
+    blocks[:, :, 0] &= 0x0F                                             # and min nibble 0: weight exactly 0
+    blocks = blocks.reshape(-1)
+    assert np.all(oracle.dequantize(blocks).reshape(N, K)[:, ::256] == 0.0)
+    x = (rng.standard_normal((M, K)) * 1e-7).astype(np.float32)
+    x[:, ::256] = 1.0
+    y = gpu_matmul(x, blocks, M, N, K)
+    ref, a = oracle.matmul(x, blocks, M, N, K)
+    bound = _m8_bound(x, blocks, M, N, K)
+    err = np.abs(y.astype(np.float64) - ref)
+    assert np.all(err <= bound)
+    print("matrix-core GEMV, block maxima on zero weights, M=%d: max err/A = %.3g, max err/bound = %.3g" % (
+        M, np.max(err / a), np.max(err / bound)))
