@@ -69,30 +69,27 @@ static float block_dmin(const uint8_t *blk) {
     return oracle_f16_to_f32((uint16_t)(blk[82] | (blk[83] << 8)));
 }
 
-/* fn reference_dequant: two halves of 128 weights; within a half the four
- * 2-bit positions of each code byte (shift 0, 2, 4, 6); within a position two
- * 16-byte segments; each (half, shift, segment) consumes the next scale byte,
- * whose low nibble scales the codes and whose high nibble scales dmin.
- * Outputs are appended in that order, 16 per segment. */
+/* fn reference_dequant (decode rule and output order), walked by sub-block.
+ * The 256 weights of a block form 16 sub-blocks of 16 consecutive weights.
+ * Sub-block j takes scale byte j (low nibble: the multiplier of d; high
+ * nibble: the multiplier of dmin) and its 2-bit codes from the 16 consecutive
+ * code bytes that start at qs offset 32*(j/8) + 16*(j%2), all at bit offset
+ * 2*((j/2)%4). Taking j = 0, 1, ..., 15 visits the page's order exactly:
+ * first half (j < 8) before second, within a half the bit offsets 0, 2, 4, 6,
+ * within an offset the lower 16 code bytes before the upper 16. Each weight
+ * is (d * sc) * code - dmin * mn in f32, written to out[16 j + i]. */
 void oracle_dequant_block(const uint8_t *blk, float *out) {
-    const uint8_t *scales = blk;
-    const uint8_t *qs = blk + 16;
     const float d = block_d(blk);
     const float dmin = block_dmin(blk);
-    int scale_index = 0;
-    int o = 0;
-    for (int half = 0; half < 2; ++half) {
-        for (int shift = 0; shift <= 6; shift += 2) {
-            for (int segment = 0; segment < 2; ++segment) {
-                const uint8_t s = scales[scale_index++];
-                const float dl = d * (float)(s & 0x0f);
-                const float ml = dmin * (float)(s >> 4);
-                const uint8_t *q = qs + half * 32 + segment * 16;
-                for (int lane = 0; lane < 16; ++lane) {
-                    const int code = (q[lane] >> shift) & 3;
-                    out[o++] = dl * (float)code - ml;
-                }
-            }
+    for (int j = 0; j < 16; ++j) {
+        const uint8_t sub_scale = blk[j];
+        const float step = d * (float)(sub_scale & 0x0f);
+        const float floor_value = dmin * (float)(sub_scale >> 4);
+        const uint8_t *code_bytes = blk + 16 + 32 * (j / 8) + 16 * (j % 2);
+        const int bit = 2 * ((j / 2) % 4);
+        for (int i = 0; i < 16; ++i) {
+            const int code = (code_bytes[i] >> bit) & 3;
+            out[16 * j + i] = step * (float)code - floor_value;
         }
     }
 }

@@ -70,9 +70,20 @@ def test_page_block5_bytes_match_hand_derivation(golden):
 def test_page_block5_hand_decoded_values(golden):
     out = oracle.dequant_block(synth.page_block(5))
     for idx, val, *_ in golden("block5_hand_decode.txt"):
+        if idx == "SUM":
+            continue
         assert out[int(idx)] == np.float32(float(val)), idx
     # The page also asserts the decoded fixture has both signs.
     assert (out < 0).any() and (out > 0).any()
+
+
+def test_page_block5_sum_of_decoded_values(golden):
+    # The hand-derived total (per sub-block d*sc*sum(q) - 16*dmin*mn, golden file) against the oracle's
+    # 256 decoded values summed exactly: a dropped element, sub-block or min term would move it.
+    want = [float(v) for tag, v, *_ in golden("block5_hand_decode.txt") if tag == "SUM"]
+    out = oracle.dequant_block(synth.page_block(5))
+    assert want == [256.875]
+    assert sum(Fraction(float(v)) for v in out) == Fraction(2055, 8)
 
 
 def test_page_block5_decode_is_exact_sixteenths():
