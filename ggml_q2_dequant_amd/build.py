@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libq2k.so")
 SOURCES = [os.path.join(CSRC, n) for n in ("q2k_kernels.hip", "q2k_sample.hip", "q2k_moe.hip", "q2k_noalloc.hip",
-                                           "q2k_api.cpp", "q2k_gguf.cpp")]
+                                           "q2k_api.cpp", "q2k_gguf.cpp", "q2k_sizes.cpp")]
 PROBE_LIB = os.path.join(PKG, "libq2k_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "q2k_probe.hip")]
 ARCH = os.environ.get("Q2K_OFFLOAD_ARCH", "gfx950")

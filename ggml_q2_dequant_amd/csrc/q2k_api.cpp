@@ -89,7 +89,9 @@ struct StatusWord {
 };
 
 std::mutex g_status_mu;
-std::vector<StatusWord *> g_status;  // indexed by device ordinal; never freed
+// Indexed by device ordinal. Neither the vector nor its words are ever freed,
+// so a call made while the process exits still finds them.
+std::vector<StatusWord *> &g_status = *new std::vector<StatusWord *>;
 
 // Argument rules shared by both gather entry points (sizes, alignment, overlap).
 q2k_status check_gather(const char *fn, const void *table, const uint32_t *ids, float *out, uint32_t vocab,
@@ -160,7 +162,10 @@ struct Workspace {
 };
 
 std::mutex g_ws_mu;  // guards the map, not the workspaces
-std::map<std::pair<int, hipStream_t>, std::unique_ptr<Workspace>> g_ws;
+// Never destroyed (like the buffers it holds), so a call made while the
+// process exits still finds it.
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<Workspace>> &g_ws =
+    *new std::map<std::pair<int, hipStream_t>, std::unique_ptr<Workspace>>;
 
 // Calls launch(buffer) with the stream's workspace grown to at least `bytes`,
 // holding the workspace's lock until launch returns. launch returns a status.

@@ -240,33 +240,7 @@ __global__ __launch_bounds__(256) void k_moe_gather(const float *__restrict__ x,
     }
 }
 
-constexpr uint64_t align256(uint64_t v) { return (v + 255u) & ~uint64_t{255u}; }
-
 }  // namespace
-
-uint32_t moe_tiles_max(uint32_t routes, uint32_t n_experts) {
-    // sum over non-empty experts of ceil(count / 128) <= (routes + 127 * non-empty experts) / 128
-    const uint64_t used = routes < n_experts ? routes : n_experts;
-    return static_cast<uint32_t>((routes + used * (kMoeTileRows - 1)) / kMoeTileRows);
-}
-
-uint64_t moe_scratch_bytes(uint32_t routes, uint32_t n_experts, uint32_t K) {
-    return align256(16) + align256(4ull * routes) + align256(sizeof(MoeTile) * moe_tiles_max(routes, n_experts)) +
-           2ull * routes * K;
-}
-
-MoeScratch moe_scratch_carve(void *base, uint32_t routes, uint32_t n_experts) {
-    auto *b = static_cast<uint8_t *>(base);
-    MoeScratch s;
-    s.hdr = reinterpret_cast<uint32_t *>(b);
-    b += align256(16);
-    s.perm = reinterpret_cast<uint32_t *>(b);
-    b += align256(4ull * routes);
-    s.tiles = reinterpret_cast<MoeTile *>(b);
-    b += align256(sizeof(MoeTile) * moe_tiles_max(routes, n_experts));
-    s.x_bf16 = b;
-    return s;
-}
 
 hipError_t launch_moe_route(const uint32_t *ids, uint32_t routes, uint32_t n_experts, MoeScratch s, int *status,
                             hipStream_t stream) {

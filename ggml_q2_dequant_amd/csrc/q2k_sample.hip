@@ -41,6 +41,7 @@ struct ArgMax {
     float val;
     uint32_t idx;  // kNone: no non-NaN value seen
 };
+static_assert(sizeof(ArgMax) == kSampleArgMaxBytes, "workspace sizing assumes 8-byte partials");
 
 // The earlier-index-wins combination of two partial first maxima.
 __device__ __forceinline__ ArgMax pick(ArgMax a, ArgMax b) {
@@ -219,16 +220,6 @@ __global__ __launch_bounds__(256) void k_cand_collect(const float *__restrict__ 
 
 }  // namespace
 
-uint32_t sample_chunk(uint32_t vocab) {
-    // 256 threads x at least 32 columns each, and at most kSampleMaxChunks
-    // chunks per slot; a multiple of 256 so each wavefront's quarter is whole
-    // 64-column steps.
-    uint64_t chunk = (static_cast<uint64_t>(vocab) + kSampleMaxChunks - 1) / kSampleMaxChunks;
-    if (chunk < 8192) chunk = 8192;
-    chunk = (chunk + 255) / 256 * 256;
-    return static_cast<uint32_t>(chunk);
-}
-
 hipError_t launch_argmax_candidates(const float *logits, uint32_t n_slots, uint32_t vocab, uint32_t cap,
                                     uint32_t *top1_idx, float *top1_val, uint32_t *cand_count, uint32_t *overflow,
                                     uint32_t *cand_ids, void *workspace, hipStream_t stream) {
@@ -243,12 +234,6 @@ hipError_t launch_argmax_candidates(const float *logits, uint32_t n_slots, uint3
     hipLaunchKernelGGL(k_cand_collect, grid, block, 0, stream, logits, vocab, chunk, part, counts, cap, cand_count,
                        overflow, cand_ids);
     return hipGetLastError();
-}
-
-uint64_t sample_workspace_bytes(uint32_t n_slots, uint32_t vocab) {
-    const uint32_t chunk = sample_chunk(vocab);
-    const uint64_t chunks = (vocab + chunk - 1) / chunk;
-    return static_cast<uint64_t>(n_slots) * chunks * (sizeof(ArgMax) + 4 * sizeof(uint32_t));
 }
 
 }  // namespace q2k

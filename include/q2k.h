@@ -71,8 +71,15 @@ typedef enum q2k_status {
 /* Matmul kernel choice. Q2K_PATH_AUTO picks the fp32 GEMV for M <= 8 and the
  * bf16 matrix-core path for M > 8, the switch the page's dense test makes at
  * more than 8 rows (fn run_dense: its tolerance changes there). The forced
- * values mirror the page's forced-mm test hooks (dispatch_mm_for_test). */
+ * values mirror the page's forced-mm test hooks (dispatch_mm_for_test).
+ * Passed as an int: any other value is rejected with Q2K_ERR_INVALID_ARGUMENT
+ * (in C++ the type is given int as its underlying type, so such a value is
+ * still a valid q2k_path to receive and test). */
+#ifdef __cplusplus
+typedef enum q2k_path : int {
+#else
 typedef enum q2k_path {
+#endif
     Q2K_PATH_AUTO = 0,
     Q2K_PATH_GEMV = 1, /* fp32 GEMV; only valid for 1 <= M <= 8 */
     Q2K_PATH_MFMA = 2  /* bf16 operands (round to nearest even), fp32 accumulation; any M */

@@ -51,8 +51,12 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        # Q2K_ORACLE_LIB names another build of q2k_oracle.c to load instead
+        # (the sanitizer build of tests/test_sanitizers.py).
+        path = os.environ.get("Q2K_ORACLE_LIB")
+        if not path:
+            path = build(force=False)
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         L = ctypes.c_long
         lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]

@@ -30,11 +30,16 @@ def _header_functions():
     return sorted(set(re.findall(r"\b(q2k_[a-z_]+)\s*\(", text)))
 
 
+# Q2K_ABI_TEST_LIB names another build of the same C ABI layer to test instead
+# of libq2k.so (the sanitizer build of tests/test_sanitizers.py).
+LIB_UNDER_TEST = os.environ.get("Q2K_ABI_TEST_LIB") or q2k.LIB_PATH
+
+
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(q2k.LIB_PATH):
-        pytest.skip("libq2k.so not built")
-    return q2k.load_library()
+    if not os.path.exists(LIB_UNDER_TEST):
+        pytest.skip("%s not built" % LIB_UNDER_TEST)
+    return q2k.load_library(LIB_UNDER_TEST)
 
 
 def test_header_declares_the_expected_entry_points():
