@@ -287,17 +287,26 @@ __device__ __forceinline__ void segment_value(const SegLoads &L, const float (&x
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t v = L.q[j], u = v >> 8;  // u: the odd bytes in the low byte of each half
+        uint32_t me[4], mo[4];                  // bytes 4j, 4j+2 and 4j+1, 4j+3 of the segment
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const uint32_t mask = 0x00030003u << (2 * p);
-            const uint32_t me = v & mask, mo = u & mask;  // bytes 4j, 4j+2 and 4j+1, 4j+3 of the segment
+            me[p] = v & mask;
+            mo[p] = u & mask;
+        }
+        // The four chains (one per position) advance in turn: a chain's next
+        // FMA never directly follows its last, so no wait state sits between.
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float a = fma_code<0>(me, xv[m][p][4 * j], j == 0 ? 0.0f : t[m][p]);
-                a = fma_code<0>(mo, xv[m][p][4 * j + 1], a);
-                a = fma_code<1>(me, xv[m][p][4 * j + 2], a);
-                t[m][p] = fma_code<1>(mo, xv[m][p][4 * j + 3], a);
-            }
+        for (int m = 0; m < M; ++m) {
+            float a[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) a[p] = fma_code<0>(me[p], xv[m][p][4 * j], j == 0 ? 0.0f : t[m][p]);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) a[p] = fma_code<0>(mo[p], xv[m][p][4 * j + 1], a[p]);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) a[p] = fma_code<1>(me[p], xv[m][p][4 * j + 2], a[p]);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) t[m][p] = fma_code<1>(mo[p], xv[m][p][4 * j + 3], a[p]);
         }
     }
     // Scale bytes 8h + 2p + s (p = 0..3): bytes s, 2 + s of the half's two scale dwords, gathered into one
@@ -333,6 +342,18 @@ template <uint32_t N>
 __device__ __forceinline__ void vm_wait() {
     static_assert(N < 64, "vmcnt has six bits");
     __builtin_amdgcn_s_waitcnt(static_cast<int>((N & 15u) | ((N >> 4) << 14) | 0x0F70u));
+}
+
+// vm_wait<n> for a count known only after unrolling (n <= Hi): the chain of
+// comparisons folds to the one wait.
+template <uint32_t Hi>
+__device__ __forceinline__ void vm_wait_n(uint32_t n) {
+    if constexpr (Hi == 0) {
+        vm_wait<0>();
+    } else {
+        if (n >= Hi) vm_wait<Hi>();
+        else vm_wait_n<Hi - 1>(n);
+    }
 }
 
 template <int M, int NI, bool kRouted>
@@ -465,8 +486,13 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
         // Keep the scheduler from sinking these loads towards their uses.
         __builtin_amdgcn_sched_barrier(0);
 
+        // One row quadruple at a time, in load order: a quadruple's arithmetic
+        // waits only for its own loads.
 #pragma unroll
-        for (int it = 0; it < NI; ++it) segment_value<M>(wl[it], xv, xs, scsel, acc[it]);
+        for (int it = 0; it < NI; ++it) {
+            __builtin_amdgcn_sched_barrier(0);
+            segment_value<M>(wl[it], xv, xs, scsel, acc[it]);
+        }
     }
 
 #pragma unroll
@@ -599,12 +625,21 @@ __global__ __launch_bounds__(256) void k_gemv_rows(const float *__restrict__ x, 
     // Sum over the 64 lanes: each DPP row (blocks 4r .. 4r + 3) as the chunked kernel sums a wavefront, then
     // ((r0 + r1) + r2) + r3 as it adds its wavefronts: row 1 takes row 0's lane 15, row 2 row 1's lane 31,
     // row 3 row 2's lane 47 (the other rows add +0, and no lane value is -0). Lane 63 holds the total.
-    auto wave_sum = [&](float v) __attribute__((always_inline)) {
-        v = row16_sum(v);
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0x2, 0xF, false));
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0x4, 0xF, false));
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0x8, 0xF, false));
-        return v;
+    // The group's rows take each step in turn, so a DPP read never waits on the step just before it.
+    auto wave_sums = [&](float (&v)[R][M]) __attribute__((always_inline)) {
+        auto each = [&](auto step) __attribute__((always_inline)) {
+#pragma unroll
+            for (uint32_t r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m) v[r][m] = step(v[r][m]);
+        };
+        each([](float t) { return t + dpp<kDppQuadXor1>(t); });
+        each([](float t) { return t + dpp<kDppQuadXor2>(t); });
+        each([](float t) { return t + dpp<kDppRowRor4>(t); });
+        each([](float t) { return t + dpp<kDppRowRor8>(t); });
+        each([](float t) { return t + dpp<0x142, 0x2>(t); });
+        each([](float t) { return t + dpp<0x143, 0x4>(t); });
+        each([](float t) { return t + dpp<0x142, 0x8>(t); });
     };
 
     // Row r of a group is computed once its three loads are in. Loads and stores
@@ -619,18 +654,13 @@ __global__ __launch_bounds__(256) void k_gemv_rows(const float *__restrict__ x, 
 #pragma unroll
         for (uint32_t r = 0; r < R; ++r) {
             __builtin_amdgcn_sched_barrier(0);
-            if (r == 0) vm_wait<3 * (R - 1) + kNext>();
-            else if (r == 1) vm_wait<3 * (R - 2) + kNext>();
-            else if (r == 2) vm_wait<3 * (R - 3) + kNext>();
-            else vm_wait<kNext>();
+            vm_wait_n<3 * R + kNext>(3 * (R - 1 - r) + kNext);
             __builtin_amdgcn_sched_barrier(0);
-            float v[M];
 #pragma unroll
-            for (int m = 0; m < M; ++m) v[m] = 0.0f;
-            segment_value<M>(L[r], xv, xs, scsel, v);
-#pragma unroll
-            for (int m = 0; m < M; ++m) tot[r][m] = wave_sum(v[m]);
+            for (int m = 0; m < M; ++m) tot[r][m] = 0.0f;
+            segment_value<M>(L[r], xv, xs, scsel, tot[r]);
         }
+        wave_sums(tot);
 #pragma unroll
         for (uint32_t r = 0; r < R; ++r) {
             const uint32_t n = gi * R + r;
@@ -639,7 +669,6 @@ __global__ __launch_bounds__(256) void k_gemv_rows(const float *__restrict__ x, 
                 if (lane == 63u && n < N) y[static_cast<uint64_t>(m) * N + n] = tot[r][m];
         }
     };
-    static_assert(R == 4, "compute_group spells out the waits of four rows");
 
     typedef std::integral_constant<bool, true> InFlight;
     typedef std::integral_constant<bool, false> Drained;
