@@ -286,6 +286,9 @@ __device__ __forceinline__ void segment_value(const SegLoads &L, const float (&x
     float t[M][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+        // One code dword at a time: left free, the scheduler may mask all 16 dwords' codes up front and
+        // hold them in 32 registers.
+        __builtin_amdgcn_sched_barrier(0);
         const uint32_t v = L.q[j], u = v >> 8;  // u: the odd bytes in the low byte of each half
         uint32_t me[4], mo[4];                  // bytes 4j, 4j+2 and 4j+1, 4j+3 of the segment
 #pragma unroll
@@ -541,6 +544,9 @@ __global__ __launch_bounds__(256) void k_gemv_rows(const float *__restrict__ x, 
     // over the 16 groups of four banks (256 apart they would all share one group per segment parity).
     constexpr uint32_t kXB = 260;
     __shared__ __attribute__((aligned(16))) float xl[M][16 * kXB];
+    // Per wavefront: each lane's partial sums of a group's R rows, lane-major (the row reduction's transpose).
+    static_assert(R == 4, "a lane's group partials are one 16-byte LDS store");
+    __shared__ __attribute__((aligned(16))) float gsum[4][M][64 * R];
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if constexpr (kRouted) {
@@ -622,24 +628,32 @@ __global__ __launch_bounds__(256) void k_gemv_rows(const float *__restrict__ x, 
         }
     const uint32_t scsel = 0x06040200u + 0x01010101u * s;
 
-    // Sum over the 64 lanes: each DPP row (blocks 4r .. 4r + 3) as the chunked kernel sums a wavefront, then
-    // ((r0 + r1) + r2) + r3 as it adds its wavefronts: row 1 takes row 0's lane 15, row 2 row 1's lane 31,
-    // row 3 row 2's lane 47 (the other rows add +0, and no lane value is -0). Lane 63 holds the total.
-    // The group's rows take each step in turn, so a DPP read never waits on the step just before it.
-    auto wave_sums = [&](float (&v)[R][M]) __attribute__((always_inline)) {
-        auto each = [&](auto step) __attribute__((always_inline)) {
+    // Sum of a group's rows over the 64 lanes, in k_gemv_seg's association: per block the four segments
+    // (g0 + g1) + (g2 + g3); per four blocks (one chunked-kernel wavefront) (b0 + b1) + (b2 + b3); then the
+    // four of those in order, ((G0 + G1) + G2) + G3. The R rows are reduced together: each lane stores its
+    // R partials, then lane l reads the four segments of block l % 16 of row l / 16, so a 16-lane DPP row
+    // holds one row's 16 blocks: two quad steps form the G's, and three row_shr:4 steps limited to one
+    // bank (four lanes) each chain them in order (the disabled lanes add +0; no lane value is -0).
+    // Lanes 15, 31, 47 and 63 end with the totals of rows 0..3.
+    const uint32_t srow = lane >> 4, sblk = lane & 15u;
+    auto group_sums = [&](float (&v)[R][M], float (&out)[M]) __attribute__((always_inline)) {
 #pragma unroll
-            for (uint32_t r = 0; r < R; ++r)
+        for (int m = 0; m < M; ++m)
+            *reinterpret_cast<f32x4v *>(&gsum[wave][m][R * lane]) = f32x4v{v[0][m], v[1][m], v[2][m], v[3][m]};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-                for (int m = 0; m < M; ++m) v[r][m] = step(v[r][m]);
-        };
-        each([](float t) { return t + dpp<kDppQuadXor1>(t); });
-        each([](float t) { return t + dpp<kDppQuadXor2>(t); });
-        each([](float t) { return t + dpp<kDppRowRor4>(t); });
-        each([](float t) { return t + dpp<kDppRowRor8>(t); });
-        each([](float t) { return t + dpp<0x142, 0x2>(t); });
-        each([](float t) { return t + dpp<0x143, 0x4>(t); });
-        each([](float t) { return t + dpp<0x142, 0x8>(t); });
+        for (int m = 0; m < M; ++m) {
+            const float *src = &gsum[wave][m][R * 4u * sblk + srow];
+            float t = (src[0] + src[R]) + (src[2 * R] + src[3 * R]);
+            t += dpp<kDppQuadXor1>(t);
+            t += dpp<kDppQuadXor2>(t);
+            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x114, 0xF, 0x2, false));
+            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x114, 0xF, 0x4, false));
+            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x114, 0xF, 0x8, false));
+            out[m] = t;
+        }
     };
 
     // Row r of a group is computed once its three loads are in. Loads and stores
@@ -658,16 +672,19 @@ __global__ __launch_bounds__(256) void k_gemv_rows(const float *__restrict__ x, 
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int m = 0; m < M; ++m) tot[r][m] = 0.0f;
-            segment_value<M>(L[r], xv, xs, scsel, tot[r]);
-        }
-        wave_sums(tot);
+            // The row's words enter the arithmetic only here, after its wait: the compiler otherwise hoists
+            // the code masks of both loop branches above the wait and holds them in registers.
+            SegLoads Lr = L[r];
 #pragma unroll
-        for (uint32_t r = 0; r < R; ++r) {
-            const uint32_t n = gi * R + r;
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-                if (lane == 63u && n < N) y[static_cast<uint64_t>(m) * N + n] = tot[r][m];
+            for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(Lr.q[j]));
+            segment_value<M>(Lr, xv, xs, scsel, tot[r]);
         }
+        float sum[M];
+        group_sums(tot, sum);
+        const uint32_t n = gi * R + srow;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            if (sblk == 15u && n < N) y[static_cast<uint64_t>(m) * N + n] = sum[m];
     };
 
     typedef std::integral_constant<bool, true> InFlight;
