@@ -6,6 +6,9 @@ per-stream workspace), and q2k_matmul's result is in turn held to the oracle's
 rule for its path. Two calls in a row, the second smaller, show that a call
 does not depend on what the previous one left in the shared array. Sizes whose
 bf16 activations exceed the array are rejected before anything is enqueued.
+The call is meant for code under HIP graph capture: a captured call replays
+correctly with new activations, with eager calls of its own (which overwrite the
+shared array) between the replays.
 """
 import ctypes
 
@@ -86,3 +89,40 @@ def test_noalloc_rejects_activations_larger_than_its_array(lib):
     torch.cuda.synchronize()
     assert torch.all(yy == 0)
     assert ctypes.sizeof(ctypes.c_void_p) == 8
+
+
+def test_noalloc_call_captured_in_a_graph_replays_with_new_activations(lib):
+    # Capture one M=200 matrix-core call (its bf16 staging in the library's array), then replay it three
+    # times; before each replay the activations change and an eager call of another shape overwrites the
+    # array. Every replay must equal q2k_matmul on the same activations, bit for bit.
+    M, N, K = 200, 384, 1024
+    rng = np.random.Generator(np.random.PCG64(8103))
+    w_h = synth.random_blocks(rng, N * K // QK_K)
+    xs_h = [rng.standard_normal((M, K), dtype=np.float32) for _ in range(4)]
+    w = torch.from_numpy(w_h).to("cuda:0")
+    x = torch.from_numpy(xs_h[0]).to("cuda:0")
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    x_o, w_o = torch.from_numpy(rng.standard_normal((64, 512), dtype=np.float32)).to("cuda:0"), \
+        torch.from_numpy(synth.random_blocks(rng, 96 * 512 // QK_K)).to("cuda:0")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        _run(lib, "q2k_matmul_noalloc", x, w, M, N, K)       # the array's address is looked up eagerly
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            rc = lib.q2k_matmul_noalloc(x.data_ptr(), w.data_ptr(), y.data_ptr(), M, N, K,
+                                        torch.cuda.current_stream().cuda_stream)
+        assert rc == q2k.Q2K_OK, lib.q2k_last_error_message().decode()
+        torch.cuda.synchronize()
+        for r in range(1, 4):
+            print("noalloc graph replay %d" % r, flush=True)
+            x.copy_(torch.from_numpy(xs_h[r]).to("cuda:0"))
+            _run(lib, "q2k_matmul_noalloc", x_o, w_o, 64, 96, 512)   # eager work on the shared array
+            torch.cuda.synchronize()
+            y.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            want = _run(lib, "q2k_matmul", x, w, M, N, K)
+            torch.cuda.synchronize()
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), want.cpu().numpy().view(np.uint32)), r
+    del g
