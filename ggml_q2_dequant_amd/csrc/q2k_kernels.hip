@@ -167,30 +167,33 @@ struct GemvRoute {
 // ---------------------------------------------------------------------------
 // fp32 GEMV for M <= 2 (decode).
 //
-// A 256-thread workgroup owns 4 * NI consecutive weight rows, taken four at a
-// time (NI iterations), and walks K in chunks of 16 blocks (4096 weights).
-// Wavefront w covers blocks 4w .. 4w+3 of a chunk; lane l of it works on row
-// l / 16 of the current four, block (l / 4) % 4 of the wavefront's four and
-// code segment g = l % 4: the 16 code bytes qs[32h + 16s ..] with h = g / 2,
-// s = g % 2, at all four 2-bit positions p -- that is, all of sub-blocks
-// 8h + 2p + s (64 weights). The lane's 64 activations depend only on
-// (block, segment): each wavefront copies its four blocks' activations into
-// LDS once per chunk, and each lane reads its 64 from there into registers,
-// where they stay for all 4 * NI rows. All of a chunk's loads are issued
-// before any arithmetic, so the workgroup's whole share of the matrix is in
-// flight at once.
+// A workgroup of 16 / BW wavefronts owns (16 / BW) * NI consecutive weight
+// rows, taken 16 / BW at a time (a row group; NI of them), and walks K in
+// chunks of 16 blocks (4096 weights). Wavefront w covers blocks BW w ..
+// BW w + BW - 1 of a chunk; lane l of it works on row l / (4 BW) of the
+// current group, block (l / 4) % BW of the wavefront's BW and code segment
+// g = l % 4: the 16 code bytes qs[32h + 16s ..] with h = g / 2, s = g % 2, at
+// all four 2-bit positions p -- that is, all of sub-blocks 8h + 2p + s (64
+// weights). The lane's 64 activations depend only on (block, segment): each
+// wavefront copies its blocks' activations into LDS once per chunk, and each
+// lane reads its 64 from there into registers, where they stay for all the
+// workgroup's rows. All of a chunk's loads are issued before any arithmetic,
+// so the workgroup's whole share of the matrix is in flight at once.
 //
 // The lane's arithmetic per row is segment_value (below): T = sum q*x per
 // sub-block, then d * (sum sc * T) - dmin * (sum mn * S), S = sum x over the
 // sub-block. The four lanes of a (block, segment) hold the same activations,
 // so each computes one of their four sums S (pairwise) and they meet in LDS.
-// Partial sums are reduced over the 16 lanes of a row with DPP and over the
-// four wavefronts through LDS, in a fixed order.
+// Partial sums are reduced over the 4 BW lanes of a row with DPP and over the
+// wavefronts through LDS, in a fixed order: the four segments of a block
+// pairwise, then blocks pairwise up to four, then the four quarters of the
+// chunk left to right. That is the order k_gemv_rows uses, so the two kernels
+// (and both shapes below) give bit-identical rows.
 //
 // Error bound (first order, u = 2^-24): every term of the result passes
 // through at most 16 roundings in T (the first FMA adds to +0), 4 in the sc
 // sum, 1 each in the FMAs with d and dmin, 2 per further K chunk of 4096 in
-// the running sum, 4 in the DPP row sum and 3 in the wavefront sum; the min
+// the running sum and 7 in the reduction over blocks and wavefronts; the min
 // terms through fewer. So
 //   |y - exact| <= (27 + 2 * ceil(K / 4096)) u * B,
 //   B = sum_k |x[k]| * (|d * sc * q| + |dmin * mn|),
@@ -198,22 +201,33 @@ struct GemvRoute {
 // (activations above about 2^-100 where they meet non-zero codes). B equals
 // sum_k |x * w| unless a block's code and min terms cancel; the 1e-5 * sum|x w|
 // rule holds whenever B is within 5.5x of sum |x w| (K <= 4096).
-// Row quadruples per workgroup. Four (16 rows) keep a decode-sized matrix
-// (N = 4096: 256 workgroups) spread over every CU; once a launch has at least
-// two large workgroups per CU, more rows per workgroup amortize its activation
-// loads, sub-block sums and reduction: eight (32 rows) for M = 1, six (24
-// rows) for M = 2, whose registers would not hold eight. A row's arithmetic
-// does not depend on the choice, so all give bit-identical rows.
-constexpr int kSegItersSmall = 4;
+//
+// Two shapes. A decode-sized matrix (N = 4096) runs 8 wavefronts of two
+// blocks per workgroup and two row groups of 8 (16 rows: 256 workgroups, one
+// per CU): twice the wavefronts of the four-block form issue a chunk's loads
+// sooner, with the same activation traffic (M = 1: 3.74 us against 3.87 us).
+// Once a launch has at least two workgroups of the large shape per CU, the
+// memory system is busy anyway and per-lane setup (activations, sub-block
+// sums, reduction) is what to amortize: 4 wavefronts of four blocks and row
+// groups of 4, eight of them (32 rows) for M = 1 and six (24 rows) for M = 2,
+// whose registers would not hold eight (M = 1, N = 16384: 7.6 us against
+// 8.4 us in the small shape's layout). A row's arithmetic does not depend on
+// the shape.
+constexpr uint32_t kSegSmallBW = 2;
+constexpr int kSegSmallNI = 2;
+constexpr uint32_t kSegLargeBW = 4;
 template <int M>
-constexpr int kSegItersLarge = M == 1 ? 8 : 6;
+constexpr int kSegLargeNI = M == 1 ? 8 : 6;
+constexpr uint32_t seg_rows(uint32_t bw, int ni) { return 16 / bw * static_cast<uint32_t>(ni); }
 constexpr uint64_t kSegLargeMinWorkgroups = 512;
-static_assert(4ull * kSegItersLarge<1> * (kMaxK / 256) * 84 < (1ull << 31), "a workgroup's rows fit a 31-bit offset");
+static_assert(seg_rows(kSegLargeBW, kSegLargeNI<1>) * (kMaxK / 256) * 84 < (1ull << 31) &&
+                  seg_rows(kSegSmallBW, kSegSmallNI) * (kMaxK / 256) * 84 < (1ull << 31),
+              "a workgroup's rows fit a 31-bit offset");
 
 template <int M>
 inline bool seg_iters_large(uint32_t N, uint64_t problems) {
-    return static_cast<uint64_t>((N + 4 * kSegItersLarge<M> - 1) / (4 * kSegItersLarge<M>)) * problems >=
-           kSegLargeMinWorkgroups;
+    constexpr uint32_t rows = seg_rows(kSegLargeBW, kSegLargeNI<M>);
+    return static_cast<uint64_t>((N + rows - 1) / rows) * problems >= kSegLargeMinWorkgroups;
 }
 
 // Bytes 0, 1 (W = false) or 2, 3 (W = true) of v, each below 16, as exact integers.
@@ -235,17 +249,6 @@ __device__ __forceinline__ float fma_code(uint32_t codes, float x, float acc) {
     else
         asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(codes), "v"(x), "v"(acc));
     return r;
-}
-
-// Sum over each 16-lane DPP row; every lane of the row receives the total,
-// though not every lane the same association of it (lane i adds the quads in
-// the order its row_ror steps meet them).
-__device__ __forceinline__ float row16_sum(float v) {
-    v += dpp<kDppQuadXor1>(v);
-    v += dpp<kDppQuadXor2>(v);
-    v += dpp<kDppRowRor4>(v);
-    v += dpp<kDppRowRor8>(v);
-    return v;
 }
 
 struct SegLoads {
@@ -359,25 +362,28 @@ __device__ __forceinline__ void vm_wait_n(uint32_t n) {
     }
 }
 
-template <int M, int NI, bool kRouted>
-__global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, const uint8_t *__restrict__ w,
-                                                  float *__restrict__ y, uint32_t N, uint32_t K, GemvBatch bt,
-                                                  GemvRoute rt) {
-    __shared__ float red[4][NI * 4 * M];
-    // Per wavefront: x of its four blocks, block j at float 260 j so that the lanes' 16-byte reads of
+template <int M, uint32_t BW, int NI, bool kRouted>
+__global__ __launch_bounds__(64 * 16 / BW) void k_gemv_seg(const float *__restrict__ x, const uint8_t *__restrict__ w,
+                                                float *__restrict__ y, uint32_t N, uint32_t K, GemvBatch bt,
+                                                GemvRoute rt) {
+    static_assert(BW == 2 || BW == 4, "two or four blocks per wavefront");
+    constexpr uint32_t kWaves = 16 / BW, kGroupRows = 16 / BW;
+    constexpr uint32_t kRows = kGroupRows * NI;  // rows of the workgroup
+    __shared__ float red[kWaves][kRows * M];     // per wavefront: its blocks' sum of each row
+    // Per wavefront: x of its BW blocks, block j at float 260 j so that the lanes' 16-byte reads of
     // different blocks fall in different bank groups.
     constexpr uint32_t kXB = 260;
-    __shared__ __attribute__((aligned(16))) float xl[4][M][4 * kXB];
-    __shared__ __attribute__((aligned(16))) float xsum[4][M][64];  // per wavefront: S of its 64 sub-blocks
+    __shared__ __attribute__((aligned(16))) float xl[kWaves][M][BW * kXB];
+    __shared__ __attribute__((aligned(16))) float xsum[kWaves][M][16 * BW];  // per wavefront: S of its sub-blocks
     const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1);
-    const uint32_t row0 = blockIdx.x * (4 * NI);
+    const uint32_t row0 = blockIdx.x * kRows;
     if constexpr (kRouted) {
         static_assert(M == 1, "routes are single activation rows");
         const uint32_t r = rt.route0 + blockIdx.y;
         const uint32_t e = rt.ids[r];
         y += static_cast<uint64_t>(r) * N;
         if (e >= rt.n_experts) {
-            if (tid < 4 * NI && row0 + tid < N) y[row0 + tid] = __builtin_nanf("");
+            if (tid < kRows && row0 + tid < N) y[row0 + tid] = __builtin_nanf("");
             if (tid == 0 && rt.status) __hip_atomic_store(rt.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             return;
         }
@@ -389,19 +395,19 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
         y += blockIdx.y * bt.y_elems;
     }
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const uint32_t rr = lane >> 4, bq = (lane >> 2) & 3u, g = lane & 3u, h = g >> 1, s = g & 1u;
+    const uint32_t rr = lane / (4 * BW), bq = (lane >> 2) & (BW - 1), g = lane & 3u, h = g >> 1, s = g & 1u;
     const uint32_t scsel = 0x06040200u + 0x01010101u * s;  // scale bytes s, 2 + s of each scale dword
     const uint32_t nb = K >> 8;
     const uint32_t row_bytes = nb * kBlockBytes;
 
     // One descriptor spans the workgroup's rows; a lane addresses its row with
     // a 32-bit offset (rows past N reread row N-1 and are never stored). The
-    // host guarantees 4 * NI * row_bytes < 2^31.
-    const uint32_t nrows = min(4u * NI, N - row0);
+    // host guarantees kRows * row_bytes < 2^31.
+    const uint32_t nrows = min(kRows, N - row0);
     const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(w + static_cast<uint64_t>(row0) * row_bytes, nrows * row_bytes);
     uint32_t wrow[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) wrow[i] = min(4u * i + rr, nrows - 1) * row_bytes;
+    for (int i = 0; i < NI; ++i) wrow[i] = min(kGroupRows * i + rr, nrows - 1) * row_bytes;
     __amdgpu_buffer_rsrc_t xr[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) xr[m] = buffer_rsrc(x + static_cast<uint64_t>(m) * K, K * 4u);
@@ -413,22 +419,23 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
         for (int m = 0; m < M; ++m) acc[i][m] = 0.0f;
 
     for (uint32_t kb0 = 0; kb0 < nb; kb0 += 16) {
-        const uint32_t kb = kb0 + 4 * wave + bq;
+        const uint32_t kb = kb0 + BW * wave + bq;
         // Lanes past the end of K aim every weight load beyond the descriptor
         // (they read zeros) and their activation loads beyond K (zeros too).
         const uint32_t boff = kb < nb ? kb * kBlockBytes : 0x80000000u;
 
-        // The wavefront's activations (its four blocks: 4 KiB per row of x) go
-        // to its own LDS region by direct buffer-to-LDS loads, then each row
-        // quadruple's weights are requested in the order they are used. The
-        // four lanes of a (block, segment) read the same activations, so loading
-        // them once into LDS instead of once per lane keeps three quarters of
-        // the activation bytes off the vector-memory path, ahead of the weights.
+        // The wavefront's activations (its BW blocks: 1 KiB each per row of x)
+        // go to its own LDS region by direct buffer-to-LDS loads, then each row
+        // group's weights are requested in the order they are used. The lanes
+        // of a (block, segment), one per row of the group, read the same
+        // activations, so loading them once into LDS instead of once per lane
+        // keeps most of the activation bytes off the vector-memory path, ahead
+        // of the weights.
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (uint32_t j = 0; j < 4; ++j) {
-                const uint32_t u = __builtin_amdgcn_readfirstlane(4u * (kb0 + 4u * wave) * 256u + 1024u * j);
+            for (uint32_t j = 0; j < BW; ++j) {
+                const uint32_t u = __builtin_amdgcn_readfirstlane(4u * (kb0 + BW * wave) * 256u + 1024u * j);
                 // (A descriptor held in a local: this compiler drops the host-side
                 // kernel stub when the LDS load takes an element of xr.)
                 const __amdgpu_buffer_rsrc_t xm = xr[m];
@@ -446,15 +453,17 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
         vm_wait<3u * NI>();
         __builtin_amdgcn_sched_barrier(0);
         float xv[M][4][16], xs[M][4];
-        // S of sub-block 8h + 2p + s for p = rr: the lane's own quarter of the four sums its (block,
-        // segment) needs, summed pairwise in element order, then exchanged through LDS ([bq][g][p]).
+        // S of sub-block 8h + 2p + s for p = rr % 4: one of the four sums the lane's (block, segment)
+        // needs, summed pairwise in element order, then exchanged through LDS ([bq][g][p]; with two
+        // blocks per wavefront rows rr and rr + 4 compute, and store, the same sum).
+        const uint32_t pq = rr & 3u;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             float v[16];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f32x4v t4 = *reinterpret_cast<const f32x4v *>(xl[wave][m] + bq * kXB + 128u * h + 16u * s +
-                                                                   32u * rr + 4u * i);
+                                                                   32u * pq + 4u * i);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) v[4 * i + c] = t4[c];
             }
@@ -463,7 +472,7 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
             for (int i = 0; i < 8; ++i) s2[i] = v[2 * i] + v[2 * i + 1];
 #pragma unroll
             for (int i = 0; i < 4; ++i) s4[i] = s2[2 * i] + s2[2 * i + 1];
-            xsum[wave][m][16u * bq + 4u * g + rr] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+            xsum[wave][m][16u * bq + 4u * g + pq] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         }
 #pragma unroll
         for (int m = 0; m < M; ++m)
@@ -489,8 +498,8 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
         // Keep the scheduler from sinking these loads towards their uses.
         __builtin_amdgcn_sched_barrier(0);
 
-        // One row quadruple at a time, in load order: a quadruple's arithmetic
-        // waits only for its own loads.
+        // One row group at a time, in load order: a group's arithmetic waits
+        // only for its own loads.
 #pragma unroll
         for (int it = 0; it < NI; ++it) {
             __builtin_amdgcn_sched_barrier(0);
@@ -498,19 +507,31 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
         }
     }
 
+    // Reduction in the association both M <= 2 kernels share: per block the four segments
+    // (g0 + g1) + (g2 + g3) (two quad steps), then blocks pairwise: (b0 + b1) by a row_ror:4 step,
+    // (b0 + b1) + (b2 + b3) by a row_ror:8 step with four blocks per wavefront (the last lane of the
+    // row's 4 BW holds it), else from two wavefronts' partials; then the four quarters of the chunk
+    // in order, ((Q0 + Q1) + Q2) + Q3.
 #pragma unroll
     for (int it = 0; it < NI; ++it)
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            // The lanes of a DPP row end with differently associated sums: lane 15's is the one
-            // k_gemv_rows combines, so it is the one published here too.
-            const float v = row16_sum(acc[it][m]);
-            if ((lane & 15u) == 15u) red[wave][(it * 4 + rr) * M + m] = v;
+            float t = acc[it][m];
+            t += dpp<kDppQuadXor1>(t);
+            t += dpp<kDppQuadXor2>(t);
+            t += dpp<kDppRowRor4>(t);
+            if constexpr (BW == 4) t += dpp<kDppRowRor8>(t);
+            if ((lane & (4 * BW - 1)) == 4 * BW - 1) red[wave][(it * kGroupRows + rr) * M + m] = t;
         }
     __syncthreads();
-    if (tid < NI * 4 * M) {
+    if (tid < kRows * M) {
         const uint32_t r = tid / M, m = tid % M, n = row0 + r;
-        if (n < N) y[static_cast<uint64_t>(m) * N + n] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+        auto quarter = [&](uint32_t q) {  // blocks 4q .. 4q + 3 of the chunk
+            if constexpr (BW == 4) return red[q][tid];
+            else return red[2 * q][tid] + red[2 * q + 1][tid];
+        };
+        const float v = ((quarter(0) + quarter(1)) + quarter(2)) + quarter(3);
+        if (n < N) y[static_cast<uint64_t>(m) * N + n] = v;
     }
 }
 
@@ -530,9 +551,10 @@ __global__ __launch_bounds__(256) void k_gemv_seg(const float *__restrict__ x, c
 // the grid to the workgroups the chip holds at once.
 //
 // Per row the lane adds segment_value, the same arithmetic as k_gemv_seg, and
-// the 64-lane sum follows k_gemv_seg's order (16 lanes by DPP, then the four
-// 16-lane rows in order), so the two kernels give bit-identical rows and the
-// same error bound, |y - exact| <= 29 u * B (K <= 4096).
+// the 64-lane sum follows k_gemv_seg's association (segments pairwise, block
+// pairs, four-block quarters, then the quarters in order), so the two kernels
+// give bit-identical rows and the same error bound, |y - exact| <= 29 u * B
+// (K <= 4096).
 constexpr uint32_t kRowsPerGroup = 4;
 
 template <int M, bool kRouted>
@@ -629,7 +651,7 @@ __global__ __launch_bounds__(256) void k_gemv_rows(const float *__restrict__ x, 
     const uint32_t scsel = 0x06040200u + 0x01010101u * s;
 
     // Sum of a group's rows over the 64 lanes, in k_gemv_seg's association: per block the four segments
-    // (g0 + g1) + (g2 + g3); per four blocks (one chunked-kernel wavefront) (b0 + b1) + (b2 + b3); then the
+    // (g0 + g1) + (g2 + g3); per four blocks (two chunked-kernel wavefronts) (b0 + b1) + (b2 + b3); then the
     // four of those in order, ((G0 + G1) + G2) + G3. The R rows are reduced together: each lane stores its
     // R partials, then lane l reads the four segments of block l % 16 of row l / 16, so a 16-lane DPP row
     // holds one row's 16 blocks: two quad steps form the G's, and three row_shr:4 steps limited to one
@@ -1454,13 +1476,14 @@ __global__ __launch_bounds__(512) void k_gemm_q2k(const __bf16 *__restrict__ xb,
     else finish(2, false);
 }
 
-template <int M, int NI>
-hipError_t launch_gemv_seg_ni(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, uint32_t batches,
-                              GemvBatch bt, hipStream_t stream) {
-    const uint32_t blocks = (N + 4 * NI - 1) / (4 * NI);
-    hipLaunchKernelGGL((k_gemv_seg<M, NI, false>), dim3(blocks, batches), dim3(256), 0, stream, x, w, y, N, K, bt,
-                       GemvRoute{});
-    return hipGetLastError();
+// k_gemv_seg in one shape over problems (grid y) problems: batch matrices, or routes from route0 when
+// kRouted.
+template <int M, uint32_t BW, int NI, bool kRouted>
+void launch_seg(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, uint32_t problems,
+                GemvBatch bt, GemvRoute rt, hipStream_t stream) {
+    constexpr uint32_t rows = seg_rows(BW, NI);
+    hipLaunchKernelGGL((k_gemv_seg<M, BW, NI, kRouted>), dim3((N + rows - 1) / rows, problems), dim3(64 * 16 / BW), 0,
+                       stream, x, w, y, N, K, bt, rt);
 }
 
 // Workgroups of k_gemv_rows per problem: enough for every wavefront to take at
@@ -1502,9 +1525,11 @@ hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t 
                            GemvRoute{});
         return hipGetLastError();
     }
-    return seg_iters_large<M>(N, batches)
-               ? launch_gemv_seg_ni<M, kSegItersLarge<M>>(x, w, y, N, K, batches, bt, stream)
-               : launch_gemv_seg_ni<M, kSegItersSmall>(x, w, y, N, K, batches, bt, stream);
+    if (seg_iters_large<M>(N, batches))
+        launch_seg<M, kSegLargeBW, kSegLargeNI<M>, false>(x, w, y, N, K, batches, bt, GemvRoute{}, stream);
+    else
+        launch_seg<M, kSegSmallBW, kSegSmallNI, false>(x, w, y, N, K, batches, bt, GemvRoute{}, stream);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -1579,25 +1604,20 @@ hipError_t launch_moe_gemv(const float *x, const uint8_t *w, const uint32_t *ids
                 hipLaunchKernelGGL((k_gemv_rows<1, true>), dim3(rg, nr), dim3(256), 0, stream, x, w, y, N, K,
                                    GemvBatch{}, rt);
             else
-                hipLaunchKernelGGL((k_gemv_seg<1, kSegItersSmall, true>), dim3((N + 4 * kSegItersSmall - 1) /
-                                                                               (4 * kSegItersSmall), nr),
-                                   dim3(256), 0, stream, x, w, y, N, K, GemvBatch{}, rt);
+                launch_seg<1, kSegSmallBW, kSegSmallNI, true>(x, w, y, N, K, nr, GemvBatch{}, rt, stream);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
     }
     const bool large = seg_iters_large<1>(N, routes);
-    const uint32_t rows = 4 * (large ? kSegItersLarge<1> : kSegItersSmall), blocks = (N + rows - 1) / rows;
     for (uint32_t r0 = 0; r0 < routes; r0 += kMaxGridY) {
         const uint32_t nr = routes - r0 < kMaxGridY ? routes - r0 : kMaxGridY;
         const GemvRoute rt{ids, status, expert_stride, r0, x_div, n_experts};
         if (large)
-            hipLaunchKernelGGL((k_gemv_seg<1, kSegItersLarge<1>, true>), dim3(blocks, nr), dim3(256), 0, stream, x, w, y,
-                               N, K, GemvBatch{}, rt);
+            launch_seg<1, kSegLargeBW, kSegLargeNI<1>, true>(x, w, y, N, K, nr, GemvBatch{}, rt, stream);
         else
-            hipLaunchKernelGGL((k_gemv_seg<1, kSegItersSmall, true>), dim3(blocks, nr), dim3(256), 0, stream, x, w, y,
-                               N, K, GemvBatch{}, rt);
+            launch_seg<1, kSegSmallBW, kSegSmallNI, true>(x, w, y, N, K, nr, GemvBatch{}, rt, stream);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
