@@ -744,10 +744,10 @@ __global__ __launch_bounds__(256) void k_gemv_rows(const float *__restrict__ x, 
 //  - A holds x in two f16 pieces (x' = h1 + h2 to 2^-22 of |x'|), after scaling
 //    each row of each block by a power of two 2^s so its largest |x| lies in
 //    [2^13, 2^14). Products h * v * 2^-24 are exact in fp32.
-// k_gemv_mfma builds each block's A fragments inside the wavefront that uses
-// them and streams the weights. Codes at 2-bit position p are masked in place (value 4^p q for
-// p < 3, 4q for p = 3 after a 4-bit shift), so the A pieces of position p
-// carry the inverse factor 1, 1/4, 1/16 or 1/4 (exact powers of two).
+// Codes at 2-bit position p are masked in place (value 4^p q for p < 3, 4q for
+// p = 3 after a 4-bit shift), so the A pieces of position p carry the inverse
+// factor 1, 1/4, 1/16 or 1/4 (exact powers of two). Each wavefront builds the A
+// fragments of its own block and keeps them in registers for all its tiles.
 //
 // MFMA v_mfma_f32_16x16x32_f16: lane l holds A row l % 16 (m = row % 8, piece =
 // row / 8) and k = 8 (l / 16) .. +7, B column l % 16 and the same k, and D
@@ -772,30 +772,192 @@ __device__ __forceinline__ void f16_pieces(float v, _Float16 *h1, _Float16 *h2) 
     *h2 = static_cast<_Float16>(v - static_cast<float>(a));
 }
 
-// Which blocks and tiles a wavefront of k_gemv_mfma takes (set by the host):
-// with nb = K / 256 >= 16 every wavefront takes blocks wave, wave + 16, ...
-// of all tiles (kAll); otherwise wavefront w < nb * (16 / nb) takes block
-// w % nb of the tiles t with t % (16 / nb) == w / nb.
-struct MvPlan {
-    uint32_t wpb, active;
-};
-
 // Activation rows of one block in LDS: 8 rows of 256 floats per wavefront,
 // rows 260 floats apart so that lanes reading different rows at the same
 // column start in different banks.
 constexpr uint32_t kMvXRow = 260;
 constexpr uint32_t kMvXWave = 8 * kMvXRow;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A operands of one block, for lane l = 16 G + col (row m = col % 8, piece 1
+// if col < 8 else 2): the eight 16x16x32 fragments, the min-term fragment and
+// the inverse scales of the lane's four D rows.
+struct MvA {
+    f16x8 af[8];
+    f16x4 am;
+    f32x4 isc;
+};
+
+// Builds MvA from the lane's 32 activations xq[p][jj] = elements 8 jj + 4 half
+// .. +3 of sub-block 8 (G / 2) + 2 p + G % 2 of row m (half = col / 8; lanes
+// col and col ^ 8 hold the two halves of the same sixteen elements).
+//  - Row maximum of |x| over the block (the eight lanes of row m), giving the
+//    scale 2^s that puts it in [2^13, 2^14). A subnormal maximum counts as
+//    2^-127; zero, inf or NaN maxima leave the row unscaled.
+//  - Sub-block sums S, pairwise in element order: ((e0 + e1) + (e2 + e3)) for
+//    each quad, then (q0 + q1) + (q2 + q3); quads 0 and 2 are lane half 0's,
+//    1 and 3 half 1's, and both lanes form the same sum.
+//  - Fragments: MFMA j takes elements 8 (j % 2) .. +7 of sub-block p = j / 2,
+//    scaled by 2^s times the position factor (one exact power of two). Each
+//    lane splits its four elements into h1 = f16(v) and h2 = f16(v - h1) (the
+//    difference is exact before its one rounding), keeps the piece of its row
+//    and takes the other four elements' piece from its partner by DPP.
+__device__ __forceinline__ MvA mv_build_a(const f32x4 (&xq)[4][2], uint32_t G, uint32_t m, bool second) {
+    MvA a;
+    float mx = 0.0f, S[4];
+#pragma unroll
+    for (uint32_t p = 0; p < 4; ++p) {
+        float q[2];
+#pragma unroll
+        for (uint32_t jj = 0; jj < 2; ++jj) {
+            const f32x4 v = xq[p][jj];
+#pragma unroll
+            for (uint32_t i = 0; i < 4; ++i)
+                mx = p == 0 && jj == 0 && i == 0 ? __builtin_fabsf(v[0]) : __builtin_fmaxf(mx, __builtin_fabsf(v[i]));
+            q[jj] = (v[0] + v[1]) + (v[2] + v[3]);
+        }
+        S[p] = (q[0] + dpp<kDppRowRor8>(q[0])) + (q[1] + dpp<kDppRowRor8>(q[1]));
+    }
+    mx = __builtin_fmaxf(mx, dpp<kDppRowRor8>(mx));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
+    int sx = 0;
+    if (mx > 0.0f && mx <= 3.4e38f) {
+        const int e = static_cast<int>(__builtin_bit_cast(uint32_t, mx) >> 23) - 127;
+        sx = 13 - e;
+        sx = sx < -100 ? -100 : (sx > 100 ? 100 : sx);
+    }
+    const float fwd = __builtin_bit_cast(float, static_cast<uint32_t>(127 + sx) << 23);
+    const float inv = __builtin_bit_cast(float, static_cast<uint32_t>(127 - sx) << 23);
+#pragma unroll
+    for (uint32_t j = 0; j < 8; ++j) {
+        const uint32_t p = j >> 1;
+        // The product differs from scaling twice only below f32's normal range, where both pieces are
+        // zero in f16 anyway.
+        const float c = fwd * (p == 0 ? 1.0f : (p == 2 ? 0.0625f : 0.25f));
+        const f32x4 v = xq[p][j & 1u];
+        u32x4 frag;
+#pragma unroll
+        for (uint32_t i = 0; i < 2; ++i) {
+            const float a0 = v[2 * i] * c, a1 = v[2 * i + 1] * c;
+            const uint32_t b1 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a0, a1}), f16x2));
+            float r0, r1;  // a - f32(h1) in one rounding: the fused product with -1 is exact
+            asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r0) : "v"(b1), "v"(a0));
+            asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r1) : "v"(b1), "v"(a1));
+            const uint32_t b2 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r0, r1}), f16x2));
+            // Elements 2i, 2i + 1 of the eight are lane half 0's: piece 1 lanes (DPP banks 0, 1) keep h1,
+            // piece 2 lanes (banks 2, 3) take the partner's h2. Elements 4 + 2i, 5 + 2i the other way round.
+            frag[i] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(b1), static_cast<int>(b2),
+                                                                        kDppRowRor8, 0xF, 0xC, false));
+            frag[2 + i] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(b2), static_cast<int>(b1),
+                                                                            kDppRowRor8, 0xF, 0x3, false));
+        }
+        a.af[j] = __builtin_bit_cast(f16x8, frag);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Min-term fragment: sub-blocks 4 G .. 4 G + 3 of row m. Sub-block 4 G + i is S[2 (G % 2) + i / 2] of
+    // the lanes of segment 2 (G / 2) + i % 2, and a lane of half h offers S[2 h + q] as its q-th sum.
+    const float s01[2] = {second ? S[2] : S[0], second ? S[3] : S[1]};
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) {
+        const int src = static_cast<int>(16u * (2u * (G >> 1) + (i & 1u)) + m + 8u * (G & 1u));
+        const float sub = __shfl(s01[i >> 1], src, 64);
+        _Float16 h1, h2;
+        f16_pieces(sub * fwd * 0.03125f, &h1, &h2);  // |sum| < 2^18: scaled by 2^-5 into f16 range
+        a.am[i] = second ? h2 : h1;
+    }
+    // Inverse scales of D rows 4 (G % 2) .. +3 (activation rows of lanes 0..7).
+#pragma unroll
+    for (uint32_t v = 0; v < 4; ++v) a.isc[v] = __shfl(inv, static_cast<int>(4u * (G & 1u) + v), 64);
+    return a;
+}
+
+// One block of one 16-column tile: the lane's 16 code bytes qv (segment G of
+// column col), its half's scale bytes scv (8 (G / 2) ..), the min nibbles of
+// sub-blocks 4 G .. +3 (mnv) and d, dmin (ddv); adds the block's products,
+// scaled back, to acc (D rows 4 G .. +3 of column col).
+__device__ __forceinline__ void mv_tile(const MvA &a, u32x4 qv, u32x2 scv, uint32_t mnv, uint32_t ddv, uint32_t G,
+                                        f32x4 &acc) {
+    uint32_t u[8];
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) {
+        u[2 * i] = __builtin_amdgcn_perm(0u, qv[i], 0x0c010c00u);      // bytes 0, 1 -> 16-bit slots
+        u[2 * i + 1] = __builtin_amdgcn_perm(0u, qv[i], 0x0c030c02u);  // bytes 2, 3
+    }
+    const uint32_t sh = 8u * (G & 1u);
+    const uint32_t sc[4] = {(scv[0] >> sh) & 15u, (scv[0] >> (sh + 16u)) & 15u, (scv[1] >> sh) & 15u,
+                            (scv[1] >> (sh + 16u)) & 15u};
+    f32x4 d1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (uint32_t j = 0; j < 8; ++j) {
+        const uint32_t p = j >> 1, jj = j & 1u;
+        const uint32_t mask = p == 0 ? 0x00030003u : (p == 2 ? 0x00300030u : 0x000C000Cu);
+        u32x4 bv;
+#pragma unroll
+        for (uint32_t i = 0; i < 4; ++i) {
+            const uint32_t vv = p == 3 ? u[4 * jj + i] >> 4 : u[4 * jj + i];
+            bv[i] = __umul24(vv & mask, sc[p]);
+        }
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.af[j], __builtin_bit_cast(f16x8, bv), d1, 0, 0, 0);
+    }
+    u32x2 bm;
+    bm[0] = (__builtin_amdgcn_perm(0u, mnv, 0x0c010c00u) >> 4) & 0x000F000Fu;
+    bm[1] = (__builtin_amdgcn_perm(0u, mnv, 0x0c030c02u) >> 4) & 0x000F000Fu;
+    const f32x4 d2 = __builtin_amdgcn_mfma_f32_16x16x16f16(a.am, __builtin_bit_cast(f16x4, bm),
+                                                          f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    const float dl = f16_low(ddv) * 16777216.0f;    // d * 2^24
+    const float ml = f16_high(ddv) * 536870912.0f;  // dmin * 2^24 * 2^5
+#pragma unroll
+    for (uint32_t v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(a.isc[v], __builtin_fmaf(-ml, d2[v], dl * d1[v]), acc[v]);
+}
+
+// The workgroup's partial sums: lane l of wavefront w holds D rows 4 G + v
+// (piece G / 2 of activation row m = 4 (G % 2) + v) of column l % 16 of each
+// tile; they meet in LDS (part, at w * stride) and are added in wavefront
+// order, piece 1 before piece 2. The caller has made part free.
+__device__ __forceinline__ void mv_store(const f32x4 (&acc)[kMvTiles], float *part, uint32_t stride, uint32_t tid,
+                                         uint32_t wave, uint32_t G, uint32_t col, float *y, uint32_t M, uint32_t N,
+                                         uint32_t row0) {
+#pragma unroll
+    for (uint32_t t = 0; t < kMvTiles; ++t)
+#pragma unroll
+        for (uint32_t v = 0; v < 4; ++v) part[wave * stride + t * 256u + (4u * G + v) * 16u + col] = acc[t][v];
+    __syncthreads();
+    if (tid < kMvTiles * 128u) {
+        const uint32_t t = tid >> 7, q = tid & 127u, mm = q >> 4, c = q & 15u, n = row0 + 16u * t + c;
+        const float *rs = part + t * 256u;
+        float s = rs[q] + rs[q + 128u];
+#pragma unroll
+        for (uint32_t wv = 1; wv < kMvWaves; ++wv) s += rs[wv * stride + q] + rs[wv * stride + q + 128u];
+        if (mm < M && n < N) y[static_cast<uint64_t>(mm) * N + n] = s;
+    }
+}
+
+// The lane's 32 activations (see mv_build_a) from a wavefront's LDS copy of
+// the block's 8 rows.
+__device__ __forceinline__ void mv_read_x(const float *xw, uint32_t G, uint32_t m, uint32_t half, f32x4 (&xq)[4][2]) {
+#pragma unroll
+    for (uint32_t p = 0; p < 4; ++p)
+#pragma unroll
+        for (uint32_t jj = 0; jj < 2; ++jj)
+            xq[p][jj] = *reinterpret_cast<const f32x4 *>(xw + m * kMvXRow + 128u * (G >> 1) + 16u * (G & 1u) + 32u * p +
+                                                         8u * jj + 4u * half);
+}
+
+// K < 4096 (nb = K / 256 < 16 blocks): wavefront w < nb * (16 / nb) takes
+// block w % nb of the tiles t with t % (16 / nb) == w / nb (set by the host as
+// wpb = 16 / nb, active = nb * wpb).
+struct MvPlan {
+    uint32_t wpb, active;
+};
+
 // grid (ceil(N / (16 kMvTiles)), problems); 1024 threads = 16 wavefronts.
-// Each wavefront builds its block's A fragments itself: it copies the block's
-// 8 activation rows into its own LDS region (direct buffer-to-LDS loads,
-// issued before the weight loads so they land first), finds each row's
-// power-of-two scale and the sub-block sums there, and splits the scaled
-// activations into f16 pieces, all while its weight bytes are in flight. The
-// fragments stay in registers for all its tiles; per tile the wavefronts'
-// partial sums (both pieces) meet in LDS and are added in wavefront order,
-// piece 1 before piece 2.
-template <bool kAll>
+// Each active wavefront copies its block's 8 activation rows into its own LDS
+// region (direct buffer-to-LDS loads, issued before its weight loads so they
+// land first), loads its tiles' weight bytes straight into registers and
+// builds the block's A fragments from the LDS copy.
 __global__ __launch_bounds__(1024) void k_gemv_mfma(const float *__restrict__ x, const uint8_t *__restrict__ w,
                                                    float *__restrict__ y, uint32_t M, uint32_t N, uint32_t K,
                                                    GemvBatch bt, MvPlan plan) {
@@ -813,24 +975,16 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const float *__restrict__ x,
     // Rows past N (weights) or M (activations) lie beyond these descriptors and read as zeros.
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(w + static_cast<uint64_t>(row0) * row_bytes, nrows * row_bytes);
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, M * K * 4u);
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     float *const xw = lds + wave * kMvXWave;
-    // A row r = col of this lane: activation row m = r % 8, piece r / 8. Its
-    // elements of MFMA j lie in sub-block 8 (G / 2) + 2 (j / 2) + G % 2.
     const uint32_t m = col & 7u;
     const bool second = col >= 8u;
-    const uint32_t xbase = m * kMvXRow + 128u * (G >> 1) + 16u * (G & 1u);
 
     f32x4 acc[kMvTiles];
 #pragma unroll
     for (uint32_t t = 0; t < kMvTiles; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const bool active = kAll || wave < plan.active;
-    const uint32_t tl = kAll ? 0u : wave / nb;
-    const uint32_t b_first = kAll ? wave : wave % nb, b_step = kAll ? kMvWaves : nb;
-    for (uint32_t b = b_first; active && b < nb; b += b_step) {
-        // Activation rows 0..7 of block b: one 1 KiB load per row, 16 bytes a lane.
+    const uint32_t tl = wave / nb, b = wave % nb;
+    if (wave < plan.active) {
 #pragma unroll
         for (uint32_t r = 0; r < 8; ++r) {
             const uint32_t u = __builtin_amdgcn_readfirstlane((r * K + 256u * b) * 4u);
@@ -838,14 +992,12 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const float *__restrict__ x,
                                                      16, static_cast<int>(u + 16u * lane), 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // Every tile's bytes of this block (with a partial plan, the
-        // wavefront's own tiles') are requested before any arithmetic.
         u32x4 qv[kMvTiles];
         u32x2 scv[kMvTiles];
         uint32_t mnv[kMvTiles], ddv[kMvTiles];
 #pragma unroll
         for (uint32_t t = 0; t < kMvTiles; ++t) {
-            if (!kAll && t % plan.wpb != tl) continue;
+            if (t % plan.wpb != tl) continue;
             const uint32_t off = (16u * t + col) * row_bytes + b * kBlockBytes;
             qv[t] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16u + 16u * G, 0, 0);
             scv[t] = __builtin_amdgcn_raw_buffer_load_b64(wr, off + 8u * (G >> 1), 0, 0);
@@ -853,160 +1005,138 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma(const float *__restrict__ x,
             ddv[t] = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 80u, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kAll) {
-            // Loads complete in issue order: the activation rows are in once at
-            // most the 4 kMvTiles weight loads issued after them are in flight,
-            // so the scaling below overlaps the weights' memory latency.
-            vm_wait<4 * kMvTiles>();
-        } else {
-            // The weight loads depend on the plan here, so wait for all of them.
-            vm_wait<0>();
-        }
+        // The weight loads depend on the plan, so wait for all of them.
+        vm_wait<0>();
         __builtin_amdgcn_sched_barrier(0);
-
-        // Lanes col and col ^ 8 hold the same activation row m (pieces 1 and 2)
-        // and share the work: each takes half and the halves are exchanged by a
-        // DPP rotation of its 16-lane row by 8.
-        const uint32_t half = second ? 1u : 0u;
-        // Row maximum of |x| over the block, and the sums (pairwise, in element
-        // order) of sub-blocks p = 2 half and 2 half + 1 of this lane's four.
-        float mx = 0.0f, s01[2];
-#pragma unroll
-        for (uint32_t q = 0; q < 2; ++q) {
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(xw + xbase + 32u * (2u * half + q));
-            float v[16];
-#pragma unroll
-            for (uint32_t r4 = 0; r4 < 4; ++r4) {
-                const f32x4 t4 = src[r4];
-                v[4 * r4] = t4[0];
-                v[4 * r4 + 1] = t4[1];
-                v[4 * r4 + 2] = t4[2];
-                v[4 * r4 + 3] = t4[3];
-            }
-#pragma unroll
-            for (uint32_t i = 0; i < 16; ++i) mx = q == 0 && i == 0 ? __builtin_fabsf(v[0]) : __builtin_fmaxf(mx, __builtin_fabsf(v[i]));
-            float s2[8], s4[4];
-#pragma unroll
-            for (uint32_t i = 0; i < 8; ++i) s2[i] = v[2 * i] + v[2 * i + 1];
-#pragma unroll
-            for (uint32_t i = 0; i < 4; ++i) s4[i] = s2[2 * i] + s2[2 * i + 1];
-            s01[q] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-            // Pin the sums here: left to the compiler they sink to their use after
-            // the fragments, keeping all 32 activations live.
-            asm volatile("" : "+v"(s01[q]), "+v"(mx));
-        }
-        mx = __builtin_fmaxf(mx, dpp<kDppRowRor8>(mx));
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // s = 13 - floor(log2 max): the scaled row lies in [2^13, 2^14). A subnormal
-        // maximum counts as 2^-127; zero, inf or NaN maxima leave the row unscaled.
-        int sx = 0;
-        if (mx > 0.0f && mx <= 3.4e38f) {
-            const int e = static_cast<int>(__builtin_bit_cast(uint32_t, mx) >> 23) - 127;
-            sx = 13 - e;
-            sx = sx < -100 ? -100 : (sx > 100 ? 100 : sx);
-        }
-        const float fwd = __builtin_bit_cast(float, static_cast<uint32_t>(127 + sx) << 23);
-        const float inv = __builtin_bit_cast(float, static_cast<uint32_t>(127 - sx) << 23);
-
-        // A fragments: MFMA j takes elements 8 (j % 2) .. +7 of sub-block p = j / 2,
-        // scaled by 2^s and by the position factor 1, 1/4, 1/16, 1/4. This lane
-        // splits elements 4 half .. +3 into h1 = f16(v) and h2 = f16(v - h1) (two at
-        // a time, rounded to nearest even), keeps its own piece and hands the
-        // other to its partner, which split the other four elements.
-        f16x8 af[8];
-#pragma unroll
-        for (uint32_t j = 0; j < 8; ++j) {
-            const uint32_t p = j >> 1;
-            // 2^s times the position factor, one exact power of two: the product
-            // differs from scaling twice only below f32's normal range, where both
-            // pieces are zero in f16 anyway.
-            const float c = fwd * (p == 0 ? 1.0f : (p == 2 ? 0.0625f : 0.25f));
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(xw + xbase + 32u * p + 8u * (j & 1u) + 4u * half);
-            uint32_t own[2], got[2];
-#pragma unroll
-            for (uint32_t i = 0; i < 2; ++i) {
-                const f32x2 a = {v[2 * i] * c, v[2 * i + 1] * c};
-                const f16x2 h1 = __builtin_convertvector(a, f16x2);
-                const f16x2 h2 = __builtin_convertvector(a - __builtin_convertvector(h1, f32x2), f16x2);
-                const uint32_t b1 = __builtin_bit_cast(uint32_t, h1), b2 = __builtin_bit_cast(uint32_t, h2);
-                own[i] = second ? b2 : b1;
-                got[i] = __builtin_bit_cast(uint32_t, dpp<kDppRowRor8>(__builtin_bit_cast(float, second ? b1 : b2)));
-            }
-            af[j] = __builtin_bit_cast(f16x8, second ? u32x4{got[0], got[1], own[0], own[1]}
-                                                     : u32x4{own[0], own[1], got[0], got[1]});
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // Min-term fragment: sub-blocks 4 G .. 4 G + 3 of row m. Sub-block 4 G + i
-        // is sum number i / 2 of lane 16 (2 (G / 2) + i % 2) + m + 8 (G % 2).
-        f16x4 am;
-#pragma unroll
-        for (uint32_t i = 0; i < 4; ++i) {
-            const int src = static_cast<int>(16u * (2u * (G >> 1) + (i & 1u)) + m + 8u * (G & 1u));
-            const float sub = __shfl(s01[i >> 1], src, 64);
-            _Float16 h1, h2;
-            f16_pieces(sub * fwd * 0.03125f, &h1, &h2);  // |sum| < 2^18: scaled by 2^-5 into f16 range
-            am[i] = second ? h2 : h1;
-        }
-        // Inverse scales of D rows 4 (G % 2) .. +3 (activation rows of lanes 0..7).
-        f32x4 isc;
-#pragma unroll
-        for (uint32_t v = 0; v < 4; ++v) isc[v] = __shfl(inv, static_cast<int>(4u * (G & 1u) + v), 64);
-
+        f32x4 xq[4][2];
+        mv_read_x(xw, G, m, second ? 1u : 0u, xq);
+        const MvA a = mv_build_a(xq, G, m, second);
 #pragma unroll
         for (uint32_t t = 0; t < kMvTiles; ++t) {
-            if (!kAll && t % plan.wpb != tl) continue;
-            uint32_t u[8];
-#pragma unroll
-            for (uint32_t i = 0; i < 4; ++i) {
-                u[2 * i] = __builtin_amdgcn_perm(0u, qv[t][i], 0x0c010c00u);      // bytes 0, 1 -> 16-bit slots
-                u[2 * i + 1] = __builtin_amdgcn_perm(0u, qv[t][i], 0x0c030c02u);  // bytes 2, 3
-            }
-            const uint32_t sh = 8u * (G & 1u);
-            const uint32_t sc[4] = {(scv[t][0] >> sh) & 15u, (scv[t][0] >> (sh + 16u)) & 15u,
-                                    (scv[t][1] >> sh) & 15u, (scv[t][1] >> (sh + 16u)) & 15u};
-            f32x4 d1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (uint32_t j = 0; j < 8; ++j) {
-                const uint32_t p = j >> 1, jj = j & 1u;
-                const uint32_t mask = p == 0 ? 0x00030003u : (p == 2 ? 0x00300030u : 0x000C000Cu);
-                u32x4 bv;
-#pragma unroll
-                for (uint32_t i = 0; i < 4; ++i) {
-                    const uint32_t vv = p == 3 ? u[4 * jj + i] >> 4 : u[4 * jj + i];
-                    bv[i] = __umul24(vv & mask, sc[p]);
-                }
-                d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[j], __builtin_bit_cast(f16x8, bv), d1, 0, 0, 0);
-            }
-            u32x2 bm;
-            bm[0] = (__builtin_amdgcn_perm(0u, mnv[t], 0x0c010c00u) >> 4) & 0x000F000Fu;
-            bm[1] = (__builtin_amdgcn_perm(0u, mnv[t], 0x0c030c02u) >> 4) & 0x000F000Fu;
-            const f32x4 d2 = __builtin_amdgcn_mfma_f32_16x16x16f16(am, __builtin_bit_cast(f16x4, bm),
-                                                                  f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-            const float dl = f16_low(ddv[t]) * 16777216.0f;     // d * 2^24
-            const float ml = f16_high(ddv[t]) * 536870912.0f;   // dmin * 2^24 * 2^5
-#pragma unroll
-            for (uint32_t v = 0; v < 4; ++v)
-                acc[t][v] = __builtin_fmaf(isc[v], __builtin_fmaf(-ml, d2[v], dl * d1[v]), acc[t][v]);
+            if (t % plan.wpb != tl) continue;
+            mv_tile(a, qv[t], scv[t], mnv[t], ddv[t], G, acc[t]);
         }
     }
-
-    // Lane l holds rows 4 G + v (piece G / 2 of m = 4 (G % 2) + v) of column l % 16.
     // The partial sums reuse the activation rows once every wavefront is done with them.
     __syncthreads();
+    mv_store(acc, lds, kMvXWave, tid, wave, G, col, y, M, N, row0);
+}
+
+// K >= 4096: the weights go through LDS. Per 16-block chunk of K each
+// wavefront takes one block (wavefronts past the chunk's last block only copy
+// and wait) and the workgroup copies its 64 rows' chunk bytes into LDS with
+// dword buffer-to-LDS loads, each reading 256 contiguous bytes of one row: far
+// fewer cache lines than per-lane loads of codes, scales, mins and d, which
+// touch every row's lines four times. The LDS holds each wavefront's 8
+// activation rows (as k_gemv_mfma) and tile 0's rows; once a wavefront has its
+// activations in registers, its region takes its rows of tiles 1..3, whose
+// bytes arrive while the A fragments are built. A wavefront copies row
+// 16 t + w of every tile t; a barrier per tile makes its rows visible.
+//
+// LDS row stride of a staged chunk in dwords: 336 (16 blocks of 21 dwords)
+// plus 3, odd, so a wavefront's operand reads (16 rows x 4 segments) fall at
+// most two to a bank. Rows of tiles 1..3 sit in wavefront w's activation
+// region at 339 (t - 1) + 35 w: with the region stride 2080 = 32 (mod 64) the
+// rows of consecutive columns land 3 banks apart.
+constexpr uint32_t kMvStageRow = 339;
+constexpr uint32_t kMvStageSkew = 35;
+static_assert(2u * kMvStageRow + 336u + kMvStageSkew * 15u <= kMvXWave, "three staged rows fit an activation region");
+
+// kTail: K is not a multiple of 4096, so the last chunk has fewer than 16 blocks.
+template <bool kTail>
+__global__ __launch_bounds__(1024) void k_gemv_mfma_staged(const float *__restrict__ x, const uint8_t *__restrict__ w,
+                                                          float *__restrict__ y, uint32_t M, uint32_t N, uint32_t K,
+                                                          GemvBatch bt) {
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kMvWaves * kMvXWave + 16u * kMvStageRow];
+    static_assert(kMvXWave >= kMvTiles * 256, "the partial sums reuse the activation rows");
+    x += blockIdx.y * bt.x_elems;
+    w += blockIdx.y * bt.w_bytes;
+    y += blockIdx.y * bt.y_elems;
+    const uint32_t nb = K >> 8, row_bytes = nb * kBlockBytes;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t col = lane & 15u, G = lane >> 4;
+    const uint32_t row0 = blockIdx.x * (16u * kMvTiles);
+    const uint32_t nrows = min(16u * kMvTiles, N - row0);
+    // Rows past N (weights) or M (activations) lie beyond these descriptors and read as zeros.
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(w + static_cast<uint64_t>(row0) * row_bytes, nrows * row_bytes);
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, M * K * 4u);
+    float *const xw = reinterpret_cast<float *>(stage) + wave * kMvXWave;
+    uint32_t *const tile0 = stage + kMvWaves * kMvXWave;
+    const uint32_t m = col & 7u;
+    const bool second = col >= 8u;
+
+    f32x4 acc[kMvTiles];
 #pragma unroll
-    for (uint32_t t = 0; t < kMvTiles; ++t)
+    for (uint32_t t = 0; t < kMvTiles; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (uint32_t c = 0; c < nb; c += kMvWaves) {
+        // A wavefront past the chunk's last block builds fragments of that block and adds nothing.
+        const bool mine = !kTail || c + wave < nb;
+        const uint32_t b = mine ? c + wave : nb - 1u;
+        // Dwords of the chunk per row (336 but in a last, partial chunk). Every copy instruction keeps
+        // lane 0 on, so that each tile is six vector-memory instructions for the waits below; a lane 0 past
+        // the chunk copies unused bytes into unused slot space.
+        const uint32_t chunk_dw = kTail ? (nb - c < kMvWaves ? nb - c : kMvWaves) * (kBlockBytes / 4u) : 336u;
+        // Activation rows 0..7 of block b (1 KiB each, 16 bytes a lane), then row `wave` of tile 0.
 #pragma unroll
-        for (uint32_t v = 0; v < 4; ++v) xw[t * 256u + (4u * G + v) * 16u + col] = acc[t][v];
-    __syncthreads();
-    if (tid < kMvTiles * 128u) {
-        const uint32_t t = tid >> 7, q = tid & 127u, mm = q >> 4, c = q & 15u, n = row0 + 16u * t + c;
-        const float *rs = lds + t * 256u;
-        float s = rs[q] + rs[q + 128u];
+        for (uint32_t r = 0; r < 8; ++r) {
+            const uint32_t u = __builtin_amdgcn_readfirstlane((r * K + 256u * b) * 4u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void *)(xw + r * kMvXRow), 16,
+                                                     static_cast<int>(u + 16u * lane), 0, 0, 0);
+        }
 #pragma unroll
-        for (uint32_t wv = 1; wv < kMvWaves; ++wv) s += rs[wv * kMvXWave + q] + rs[wv * kMvXWave + q + 128u];
-        if (mm < M && n < N) y[static_cast<uint64_t>(mm) * N + n] = s;
+        for (uint32_t k = 0; k < 6; ++k)
+            if (kTail ? 64u * k + lane < chunk_dw || lane == 0u : k < 5u || lane < 16u)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wr, (__attribute__((address_space(3))) void *)(tile0 + wave * kMvStageRow + 64u * k), 4,
+                    static_cast<int>(wave * row_bytes + c * kBlockBytes + 4u * (64u * k + lane)), 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // Loads complete in issue order: the activations are in once at most tile 0's six copies are in flight.
+        vm_wait<6>();
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 xq[4][2];
+        mv_read_x(xw, G, m, second ? 1u : 0u, xq);
+        // The region is free once these reads are done: row `wave` of tiles 1..3 goes there.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (uint32_t t = 1; t < kMvTiles; ++t) {
+            const uint32_t r = 16u * t + wave;
+#pragma unroll
+            for (uint32_t k = 0; k < 6; ++k)
+                if (kTail ? 64u * k + lane < chunk_dw || lane == 0u : k < 5u || lane < 16u)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        wr,
+                        (__attribute__((address_space(3))) void *)(reinterpret_cast<uint32_t *>(xw) + (t - 1u) * kMvStageRow +
+                                                                   kMvStageSkew * wave + 64u * k),
+                        4, static_cast<int>(r * row_bytes + c * kBlockBytes + 4u * (64u * k + lane)), 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const MvA a = mv_build_a(xq, G, m, second);
+#pragma unroll
+        for (uint32_t t = 0; t < kMvTiles; ++t) {
+            // Tile t's rows are in LDS once this wavefront's copies of them are done (they complete in
+            // issue order: six per tile) and every wavefront has passed the barrier.
+            __builtin_amdgcn_sched_barrier(0);
+            vm_wait_n<6 * (kMvTiles - 1)>(6u * (kMvTiles - 1u - t));
+            asm volatile("s_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if (mine) {
+                const uint32_t *blk =
+                    (t == 0 ? tile0 + col * kMvStageRow
+                            : stage + col * kMvXWave + (t - 1u) * kMvStageRow + kMvStageSkew * col) +
+                    wave * (kBlockBytes / 4u);
+                const u32x4 qv = {blk[4u + 4u * G], blk[5u + 4u * G], blk[6u + 4u * G], blk[7u + 4u * G]};
+                const u32x2 scv = {blk[2u * (G >> 1)], blk[2u * (G >> 1) + 1u]};
+                mv_tile(a, qv, scv, blk[G], blk[20], G, acc[t]);
+            }
+        }
+        // Every wavefront is done with this chunk's LDS before the next chunk (or the partial sums)
+        // overwrites it.
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
+    mv_store(acc, reinterpret_cast<float *>(stage), kMvTiles * 256u, tid, wave, G, col, y, M, N, row0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1565,12 +1695,16 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, uint32_t M, u
             const uint32_t nb = K / kQK;
             const uint32_t wgs = (N + 16 * kMvTiles - 1) / (16 * kMvTiles);
             if (nb >= kMvWaves) {
-                hipLaunchKernelGGL(k_gemv_mfma<true>, dim3(wgs, batches), dim3(1024), 0, stream, x, w, y, M, N, K, bt,
-                                   MvPlan{1, kMvWaves});
+                if (nb % kMvWaves == 0)
+                    hipLaunchKernelGGL(k_gemv_mfma_staged<false>, dim3(wgs, batches), dim3(1024), 0, stream, x, w, y, M, N,
+                                       K, bt);
+                else
+                    hipLaunchKernelGGL(k_gemv_mfma_staged<true>, dim3(wgs, batches), dim3(1024), 0, stream, x, w, y, M, N,
+                                       K, bt);
             } else {
                 const uint32_t wpb = kMvWaves / nb;
-                hipLaunchKernelGGL(k_gemv_mfma<false>, dim3(wgs, batches), dim3(1024), 0, stream, x, w, y, M, N, K,
-                                   bt, MvPlan{wpb, nb * wpb});
+                hipLaunchKernelGGL(k_gemv_mfma, dim3(wgs, batches), dim3(1024), 0, stream, x, w, y, M, N, K, bt,
+                                   MvPlan{wpb, nb * wpb});
             }
             return hipGetLastError();
         }
