@@ -624,9 +624,10 @@ __global__ __launch_bounds__(256) void k_gemv_rows(const float *__restrict__ x, 
     if (grp < groups) load_group(A, grp);
     __builtin_amdgcn_sched_barrier(0);
     // Loads complete in issue order: the x copies are in once the group's weight loads alone are in flight.
+    // A plain barrier then (__syncthreads would also wait for those weight loads).
     if (grp < groups) vm_wait<3 * R>();
     else vm_wait<0>();
-    __syncthreads();
+    asm volatile("s_barrier" ::: "memory");
 
     // The lane's activations: element i of sub-block p is x[256 b + 128 h + 32 p + 16 s + i].
     float xv[M][4][16], xs[M][4];
