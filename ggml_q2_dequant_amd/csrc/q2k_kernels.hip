@@ -767,10 +767,27 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kMvTiles = 4;             // 16-column tiles per workgroup
 constexpr uint32_t kMvWaves = 16;
 
-__device__ __forceinline__ void f16_pieces(float v, _Float16 *h1, _Float16 *h2) {
-    const _Float16 a = static_cast<_Float16>(v);
-    *h1 = a;
-    *h2 = static_cast<_Float16>(v - static_cast<float>(a));
+// The two f16 pieces of v0 c and v1 c (c a power of two), packed low, high:
+// h1 = f16(v c) and h2 = f16(v c - h1), each one rounding of a value that is
+// exact in f32 (v c scales by a power of two; v c - h1 keeps the bits h1 left),
+// so they equal rounding v c to f32 and then to f16. One v_fma_mix per piece.
+__device__ __forceinline__ void split_f16_pair(float v0, float v1, float c, uint32_t *b1, uint32_t *b2) {
+    uint32_t h, r;
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(h) : "v"(v0), "v"(c));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0" : "+v"(h) : "v"(v1), "v"(c));
+    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(v0), "v"(c), "v"(h));
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(r) : "v"(v1), "v"(c), "v"(h));
+    *b1 = h;
+    *b2 = r;
+}
+
+// The same for one value: h1 in the low half of *b1, h2 in the low half of *b2.
+__device__ __forceinline__ void split_f16_one(float v, float c, uint32_t *b1, uint32_t *b2) {
+    uint32_t h, r;
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(h) : "v"(v), "v"(c));
+    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(v), "v"(c), "v"(h));
+    *b1 = h;
+    *b2 = r;
 }
 
 // Activation rows of one block in LDS: 8 rows of 256 floats per wavefront,
@@ -842,12 +859,8 @@ __device__ __forceinline__ MvA mv_build_a(const f32x4 (&xq)[4][2], uint32_t G, u
         u32x4 frag;
 #pragma unroll
         for (uint32_t i = 0; i < 2; ++i) {
-            const float a0 = v[2 * i] * c, a1 = v[2 * i + 1] * c;
-            const uint32_t b1 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a0, a1}), f16x2));
-            float r0, r1;  // a - f32(h1) in one rounding: the fused product with -1 is exact
-            asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r0) : "v"(b1), "v"(a0));
-            asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r1) : "v"(b1), "v"(a1));
-            const uint32_t b2 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r0, r1}), f16x2));
+            uint32_t b1, b2;
+            split_f16_pair(v[2 * i], v[2 * i + 1], c, &b1, &b2);
             // Elements 2i, 2i + 1 of the eight are lane half 0's: piece 1 lanes (DPP banks 0, 1) keep h1,
             // piece 2 lanes (banks 2, 3) take the partner's h2. Elements 4 + 2i, 5 + 2i the other way round.
             frag[i] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(b1), static_cast<int>(b2),
@@ -865,9 +878,9 @@ __device__ __forceinline__ MvA mv_build_a(const f32x4 (&xq)[4][2], uint32_t G, u
     for (uint32_t i = 0; i < 4; ++i) {
         const int src = static_cast<int>(16u * (2u * (G >> 1) + (i & 1u)) + m + 8u * (G & 1u));
         const float sub = __shfl(s01[i >> 1], src, 64);
-        _Float16 h1, h2;
-        f16_pieces(sub * fwd * 0.03125f, &h1, &h2);  // |sum| < 2^18: scaled by 2^-5 into f16 range
-        a.am[i] = second ? h2 : h1;
+        uint32_t h1, h2;  // |sum| < 2^18: scaled by 2^-5 into f16 range
+        split_f16_one(sub, fwd * 0.03125f, &h1, &h2);
+        a.am[i] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(second ? h2 : h1));
     }
     // Inverse scales of D rows 4 (G % 2) .. +3 (activation rows of lanes 0..7).
 #pragma unroll
