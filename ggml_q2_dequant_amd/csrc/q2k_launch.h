@@ -41,11 +41,16 @@ hipError_t noalloc_scratch(void **out);
 
 // First-max argmax + threshold candidates over [n_slots, vocab] logits
 // (q2k_sample.hip). workspace holds sample_workspace_bytes(n_slots, vocab)
-// bytes, 8-byte aligned; 1 <= n_slots <= kMaxGridY, vocab, cap >= 1.
+// bytes, 8-byte aligned; 1 <= n_slots <= kMaxGridY, vocab, cap >= 1. Its
+// layout, per (slot, chunk) in slot-major order: all the chunk partials
+// (value, index), then all the kept local candidates (kSampleLocalCap of
+// (index, value) each), then all the local candidate counts (u32).
 // sample_chunk and the scratch sizes below are host code (q2k_sizes.cpp).
 constexpr uint32_t kSampleMaxChunks = 64;      // chunks (workgroups) per slot
 constexpr uint32_t kSampleMaxVocab = 1u << 29;  // keeps every row's byte offsets below 2^31
 constexpr uint32_t kSampleArgMaxBytes = 8;     // one chunk's partial: value and index
+constexpr uint32_t kSampleLocalCap = 64;       // local candidates kept per chunk
+constexpr uint32_t kSampleCandBytes = 8;       // one kept candidate: index and value
 uint32_t sample_chunk(uint32_t vocab);
 uint64_t sample_workspace_bytes(uint32_t n_slots, uint32_t vocab);
 hipError_t launch_argmax_candidates(const float *logits, uint32_t n_slots, uint32_t vocab, uint32_t cap,

@@ -16,16 +16,21 @@
 // that a NaN in column 0 is the scan's starting value and stays the answer
 // (and then no logit is >= NaN - 0.5, so there are no candidates).
 //
-// Three launches, each over grid (chunks, slots) with 256 threads:
-//   1. per chunk, the first maximum of its non-NaN logits -> partials;
-//   2. per chunk, the slot's top1 from all partials (and column 0), then the
-//      number of candidates in each quarter of the chunk -> counts; chunk 0
-//      writes top1;
-//   3. per chunk, each quarter's offset among the slot's candidates (sum of
-//      the counts before it), then its candidate ids in index order; chunk 0
-//      writes the total and the overflow flag.
-// Within a chunk each wavefront walks its quarter 64 columns at a time
-// (coalesced); ballots and lane masks rank candidates inside a wavefront.
+// Two launches. The first reads the logits once, grid (chunks, slots) with
+// 256 threads: per chunk, the first maximum of its non-NaN logits (a partial),
+// and its local candidates, the logits >= (chunk maximum) - 0.5, counted and
+// the first kSampleLocalCap of them kept (index and value, in index order).
+// The slot's maximum is at least the chunk's, and f32 rounding of x - 0.5 is
+// monotonic, so every candidate of the slot is a local candidate of its chunk.
+// The second, one workgroup per slot, takes top1 from the partials (and
+// column 0), counts each chunk's candidates among its kept ones (rescanning
+// the chunk's logits only when it had more local candidates than it kept),
+// and writes the first cap candidate ids in index order, the total and the
+// overflow flag. Within a chunk each wavefront walks its quarter 64 columns
+// at a time (coalesced); ballots and lane masks rank candidates inside a
+// wavefront. For 8 x 262144 Gaussian logits the two take 12.7 us per call,
+// against 14.7 us for three passes (maximum, count, collect) that each read
+// the logits.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -84,8 +89,10 @@ __device__ __forceinline__ Span wave_span(uint32_t c, uint32_t chunk, uint32_t v
 // loads of a round are issued before any is used (buffer loads past the row
 // return 0 and are flagged out of range), then f(column, value, in_range) runs
 // in increasing column order. A quarter of an 8192-column chunk is one round,
-// so each pass over the logits waits out one memory latency per wavefront
-// (rounds of 8: 18.8 us for 8 x 262144 logits; of 32: 16.2 us).
+// so each pass over the logits waits out one memory latency per wavefront (in
+// an earlier three-pass form of this call, rounds of 8 took 18.8 us for
+// 8 x 262144 logits and rounds of 32 16.2 us). With one round the scan keeps
+// the values in registers for all its walks (round_first_max and below).
 constexpr uint32_t kRound = 32;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float *row, uint32_t vocab) {
@@ -110,25 +117,134 @@ __device__ __forceinline__ void scan_span(__amdgpu_buffer_rsrc_t rs, Span s, uin
     }
 }
 
-// Step 1: partial first maximum of each chunk.
-__global__ __launch_bounds__(256) void k_argmax_partial(const float *__restrict__ logits, uint32_t vocab,
-                                                        uint32_t chunk, ArgMax *__restrict__ part) {
-    __shared__ ArgMax red[4];
-    const uint32_t slot = blockIdx.y, c = blockIdx.x, lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const float *row = logits + static_cast<uint64_t>(slot) * vocab;
-    const Span s = wave_span(c, chunk, vocab, wave);
-    ArgMax best{0.0f, kNone};
-    scan_span(row_rsrc(row, vocab), s, lane, [&](uint32_t i, float v, bool in) {
-        if (in && v == v && (best.idx == kNone || v > best.val)) best = ArgMax{v, i};
-    });
-    best = wave_pick(best);
-    if (lane == 0) red[wave] = best;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        part[static_cast<uint64_t>(slot) * gridDim.x + c] = pick(pick(red[0], red[1]), pick(red[2], red[3]));
+// Local candidates of one chunk, kept by the scan: index and value.
+struct Cand {
+    uint32_t idx;
+    float val;
+};
+static_assert(sizeof(Cand) == kSampleCandBytes, "workspace sizing assumes 8-byte candidates");
+
+// Where the scan leaves a slot's chunks in the workspace: partials, local
+// candidate counts, kept candidates.
+struct SampleWs {
+    ArgMax *part;    // [slots * chunks]
+    uint32_t *nloc;  // [slots * chunks]
+    Cand *cand;      // [slots * chunks * kSampleLocalCap]
+};
+
+inline SampleWs sample_ws(void *ws, uint32_t n_slots, uint32_t chunks) {
+    const uint64_t pc = static_cast<uint64_t>(n_slots) * chunks;
+    SampleWs w;
+    w.part = static_cast<ArgMax *>(ws);
+    w.cand = reinterpret_cast<Cand *>(w.part + pc);
+    w.nloc = reinterpret_cast<uint32_t *>(w.cand + pc * kSampleLocalCap);
+    return w;
 }
 
-// The slot's top1 from its chunk partials (read by the first wavefront).
+// The wavefront's first maximum over its quarter when the quarter is one
+// round held in registers (v[u] is column begin + 64 u + lane, NaN past the
+// row): the largest non-NaN value M (max ignores NaN), then the lowest
+// column holding a value equal to M, and that column's own value (so +0 and
+// -0 keep their bits).
+__device__ __forceinline__ ArgMax round_first_max(const float (&v)[kRound], uint32_t begin, uint32_t lane) {
+    float m = v[0];
+#pragma unroll
+    for (uint32_t u = 1; u < kRound; ++u) m = __builtin_fmaxf(m, v[u]);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, d, 64));
+    if (m != m) return ArgMax{0.0f, kNone};  // no non-NaN value in the quarter
+    // Steps in column order; the first whose ballot finds M holds the answer in its lowest such lane.
+#pragma unroll
+    for (uint32_t u = 0; u < kRound; ++u) {
+        const uint64_t b = __ballot(v[u] == m);
+        if (b != 0) {
+            const uint32_t l = static_cast<uint32_t>(__builtin_ctzll(b));
+            const float val = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[u]), l));
+            return ArgMax{val, begin + 64u * u + l};
+        }
+    }
+    return ArgMax{0.0f, kNone};  // unreachable: M is one of the values
+}
+
+// Pass 1: per chunk, the partial first maximum and the local candidates. The
+// wavefront's quarter is walked up to three times (maximum, count, collect);
+// kOneRound: the quarter is a single round, whose values stay in registers.
+template <bool kOneRound>
+__global__ __launch_bounds__(256) void k_sample_scan(const float *__restrict__ logits, uint32_t vocab, uint32_t chunk,
+                                                     SampleWs ws) {
+    __shared__ ArgMax red[4];
+    __shared__ uint32_t cnt[4];
+    const uint32_t slot = blockIdx.y, c = blockIdx.x, chunks = gridDim.x;
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const float *row = logits + static_cast<uint64_t>(slot) * vocab;
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, vocab);
+    const Span s = wave_span(c, chunk, vocab, wave);
+    const uint64_t below = (1ull << lane) - 1ull;
+    const uint64_t pc = static_cast<uint64_t>(slot) * chunks + c;
+    Cand *out = ws.cand + pc * kSampleLocalCap;
+    float v1[kRound];  // kOneRound: the wavefront's whole quarter, NaN past the row
+    ArgMax best{0.0f, kNone};
+    if constexpr (kOneRound) {
+        // Column begin + 64 u + lane at byte offset 4 (begin + lane) + 256 u (the step in the scalar offset);
+        // past the quarter it is another wavefront's logit or, past the row, zero: NaN either way here.
+        const uint32_t len = s.end - s.begin;
+#pragma unroll
+        for (uint32_t u = 0; u < kRound; ++u) {
+            const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(rs, 4u * (s.begin + lane), 256u * u, 0);
+            v1[u] = 64u * u + lane < len ? __builtin_bit_cast(float, e) : __builtin_nanf("");
+        }
+        best = round_first_max(v1, s.begin, lane);
+    } else {
+        scan_span(rs, s, lane, [&](uint32_t i, float v, bool in) {
+            if (in && v == v && (best.idx == kNone || v > best.val)) best = ArgMax{v, i};
+        });
+        best = wave_pick(best);
+    }
+    if (lane == 0) red[wave] = best;
+    __syncthreads();
+    const ArgMax cm = pick(pick(red[0], red[1]), pick(red[2], red[3]));
+    if (threadIdx.x == 0) ws.part[pc] = cm;
+    if (cm.idx == kNone) {  // no non-NaN logit in the chunk: no candidates
+        if (threadIdx.x == 0) ws.nloc[pc] = 0;
+        return;
+    }
+    const float thr = cm.val - 0.5f;
+    uint32_t n = 0;
+    if constexpr (kOneRound) {
+#pragma unroll
+        for (uint32_t u = 0; u < kRound; ++u) n += static_cast<uint32_t>(__popcll(__ballot(v1[u] >= thr)));
+    } else {
+        scan_span(rs, s, lane, [&](uint32_t, float v, bool in) { n += static_cast<uint32_t>(__popcll(__ballot(in && v >= thr))); });
+    }
+    if (lane == 0) cnt[wave] = n;
+    __syncthreads();
+    uint32_t pos = 0;
+    for (uint32_t w = 0; w < wave; ++w) pos += cnt[w];
+    if (threadIdx.x == 0) ws.nloc[pc] = (cnt[0] + cnt[1]) + (cnt[2] + cnt[3]);
+    if (pos >= kSampleLocalCap || n == 0) return;
+    if constexpr (kOneRound) {
+#pragma unroll
+        for (uint32_t u = 0; u < kRound; ++u) {
+            const uint64_t mk = __ballot(v1[u] >= thr);
+            if (mk != 0) {  // uniform: most steps of a quarter hold no candidate
+                const bool hit = (mk >> lane) & 1ull;
+                const uint32_t r = pos + static_cast<uint32_t>(__popcll(mk & below));
+                if (hit && r < kSampleLocalCap) out[r] = Cand{s.begin + 64 * u + lane, v1[u]};
+                pos += static_cast<uint32_t>(__popcll(mk));
+            }
+        }
+    } else {
+        scan_span(rs, s, lane, [&](uint32_t i, float v, bool in) {
+            const bool hit = in && v >= thr;
+            const uint64_t m = __ballot(hit);
+            const uint32_t r = pos + static_cast<uint32_t>(__popcll(m & below));
+            if (hit && r < kSampleLocalCap) out[r] = Cand{i, v};
+            pos += static_cast<uint32_t>(__popcll(m));
+        });
+    }
+}
+
+// The slot's top1 from its chunk partials (read by one wavefront).
 __device__ __forceinline__ ArgMax slot_top1(const float *row, const ArgMax *part, uint32_t chunks, uint32_t lane) {
     ArgMax b{0.0f, kNone};
     for (uint32_t c = lane; c < chunks; c += 64) b = pick(b, part[c]);
@@ -139,83 +255,113 @@ __device__ __forceinline__ ArgMax slot_top1(const float *row, const ArgMax *part
     return b;
 }
 
-// Step 2: top1 per slot (written by chunk 0) and candidate counts per chunk.
-__global__ __launch_bounds__(256) void k_cand_count(const float *__restrict__ logits, uint32_t vocab, uint32_t chunk,
-                                                    const ArgMax *__restrict__ part, uint32_t *__restrict__ counts,
-                                                    uint32_t *__restrict__ top1_idx, float *__restrict__ top1_val) {
-    __shared__ float thr_s;
-    const uint32_t slot = blockIdx.y, c = blockIdx.x, chunks = gridDim.x;
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const float *row = logits + static_cast<uint64_t>(slot) * vocab;
-    if (wave == 0) {
-        const ArgMax t = slot_top1(row, part + static_cast<uint64_t>(slot) * chunks, chunks, lane);
-        if (lane == 0) {
-            thr_s = t.val - 0.5f;
-            if (c == 0) {
-                top1_idx[slot] = t.idx;
-                top1_val[slot] = t.val;
-            }
-        }
-    }
-    __syncthreads();
-    const float thr = thr_s;
-    const Span s = wave_span(c, chunk, vocab, wave);
-    uint32_t n = 0;
-    scan_span(row_rsrc(row, vocab), s, lane, [&](uint32_t, float v, bool in) { n += __popcll(__ballot(in && v >= thr)); });
-    if (lane == 0) counts[(static_cast<uint64_t>(slot) * chunks + c) * 4u + wave] = n;
-}
+// Pass 2: one workgroup per slot. Wavefront w takes chunks w, w + 4, ... (at
+// most kSampleMaxChunks / 4 of them): it loads their local counts and kept
+// candidates (lane j: the j-th kept one) unconditionally, from clamped
+// addresses, so they are all in flight together and the pass waits out one
+// memory latency rather than one per chunk. A chunk with more local candidates
+// than were kept is rescanned from the logits, in loops of their own (rare:
+// many logits within 0.5 of a chunk's maximum).
+constexpr uint32_t kFinishPer = kSampleMaxChunks / 4;
+static_assert(kSampleLocalCap == 64, "one kept candidate per lane");
 
-// Step 3: candidate ids in index order, the total and the overflow flag.
-__global__ __launch_bounds__(256) void k_cand_collect(const float *__restrict__ logits, uint32_t vocab, uint32_t chunk,
-                                                      const ArgMax *__restrict__ part,
-                                                      const uint32_t *__restrict__ counts, uint32_t cap,
-                                                      uint32_t *__restrict__ cand_count, uint32_t *__restrict__ overflow,
-                                                      uint32_t *__restrict__ cand_ids) {
+__global__ __launch_bounds__(256) void k_sample_finish(const float *__restrict__ logits, uint32_t vocab, uint32_t chunk,
+                                                       uint32_t chunks, SampleWs ws, uint32_t cap,
+                                                       uint32_t *__restrict__ top1_idx, float *__restrict__ top1_val,
+                                                       uint32_t *__restrict__ cand_count,
+                                                       uint32_t *__restrict__ overflow, uint32_t *__restrict__ cand_ids) {
     __shared__ float thr_s;
-    __shared__ uint32_t base_s;
-    const uint32_t slot = blockIdx.y, c = blockIdx.x, chunks = gridDim.x;
+    __shared__ uint32_t sc[kSampleMaxChunks];  // candidates of the slot per chunk, then their exclusive prefix
+    const uint32_t slot = blockIdx.x;
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const float *row = logits + static_cast<uint64_t>(slot) * vocab;
-    const uint32_t *cnts = counts + static_cast<uint64_t>(slot) * chunks * 4u;
-    if (wave == 0) {
-        const ArgMax t = slot_top1(row, part + static_cast<uint64_t>(slot) * chunks, chunks, lane);
-        uint32_t before = 0, total = 0;
-        for (uint32_t k = lane; k < chunks * 4u; k += 64) {
-            const uint32_t v = cnts[k];
-            total += v;
-            if (k < c * 4u) before += v;
-        }
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, vocab);
+    const uint64_t p0 = static_cast<uint64_t>(slot) * chunks;
+    uint32_t nl[kFinishPer];
+    Cand kc[kFinishPer];
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            before += static_cast<uint32_t>(__shfl_xor(static_cast<int>(before), m, 64));
-            total += static_cast<uint32_t>(__shfl_xor(static_cast<int>(total), m, 64));
-        }
+    for (uint32_t q = 0; q < kFinishPer; ++q) {
+        const uint32_t c = min(wave + 4u * q, chunks - 1u);
+        nl[q] = ws.nloc[p0 + c];
+        kc[q] = ws.cand[(p0 + c) * kSampleLocalCap + lane];
+    }
+    if (wave == 0) {
+        const ArgMax t = slot_top1(row, ws.part + p0, chunks, lane);
         if (lane == 0) {
             thr_s = t.val - 0.5f;
-            base_s = before;
-            if (c == 0) {
-                cand_count[slot] = total;
-                overflow[slot] = total > cap ? 1u : 0u;
-            }
+            top1_idx[slot] = t.idx;
+            top1_val[slot] = t.val;
         }
     }
-    const Span s = wave_span(c, chunk, vocab, wave);
-    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, vocab);
     __syncthreads();
     const float thr = thr_s;
-    // The quarters of this chunk before this wavefront's, from the counts of step 2.
-    uint32_t pos = base_s;
-    for (uint32_t w = 0; w < wave; ++w) pos += cnts[c * 4u + w];
-    if (pos >= cap) return;  // this quarter's candidates all fall past the capacity
-    uint32_t *out = cand_ids + static_cast<uint64_t>(slot) * cap;
     const uint64_t below = (1ull << lane) - 1ull;
-    scan_span(rs, s, lane, [&](uint32_t i, float v, bool in) {
-        const bool hit = in && v >= thr;
-        const uint64_t m = __ballot(hit);
-        const uint32_t r = pos + static_cast<uint32_t>(__popcll(m & below));
-        if (hit && r < cap) out[r] = i;
-        pos += static_cast<uint32_t>(__popcll(m));
-    });
+    // The whole chunk c, walked by one wavefront in order.
+    auto chunk_span = [&](uint32_t c) __attribute__((always_inline)) {
+        const uint32_t b = c * chunk;
+        return Span{b, b + chunk < vocab ? b + chunk : vocab};
+    };
+    uint64_t hits[kFinishPer];
+    uint32_t rescan = 0;  // bit q: chunk wave + 4 q had more local candidates than were kept
+#pragma unroll
+    for (uint32_t q = 0; q < kFinishPer; ++q) {
+        const uint32_t c = wave + 4u * q;
+        const bool kept = c < chunks && nl[q] <= kSampleLocalCap;
+        if (c < chunks && !kept) rescan |= 1u << q;
+        hits[q] = __ballot(kept && lane < nl[q] && kc[q].val >= thr);
+        if (lane == 0 && kept) sc[c] = static_cast<uint32_t>(__popcll(hits[q]));
+    }
+    rescan = __builtin_amdgcn_readfirstlane(rescan);
+#pragma nounroll
+    for (uint32_t todo = rescan; todo != 0; todo &= todo - 1u) {
+        const uint32_t c = wave + 4u * static_cast<uint32_t>(__builtin_ctz(todo));
+        uint32_t n = 0;
+        scan_span(rs, chunk_span(c), lane, [&](uint32_t, float v, bool in) {
+            n += static_cast<uint32_t>(__popcll(__ballot(in && v >= thr)));
+        });
+        if (lane == 0) sc[c] = n;
+    }
+    __syncthreads();
+    // Exclusive prefix of the chunk counts (one per lane of wavefront 0) and the total.
+    if (wave == 0) {
+        const uint32_t own = lane < chunks ? sc[lane] : 0u;
+        uint32_t v = own;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t u = static_cast<uint32_t>(__shfl_up(static_cast<int>(v), d, 64));
+            if (lane >= static_cast<uint32_t>(d)) v += u;
+        }
+        if (lane < chunks) sc[lane] = v - own;
+        if (lane == 63) {
+            cand_count[slot] = v;
+            overflow[slot] = v > cap ? 1u : 0u;
+        }
+    }
+    __syncthreads();
+    uint32_t *out = cand_ids + static_cast<uint64_t>(slot) * cap;
+#pragma unroll
+    for (uint32_t q = 0; q < kFinishPer; ++q) {
+        const uint32_t c = wave + 4u * q;
+        if (c < chunks && nl[q] <= kSampleLocalCap && hits[q] != 0) {
+            const uint32_t pos = sc[c];
+            const bool hit = (hits[q] >> lane) & 1ull;
+            const uint32_t r = pos + static_cast<uint32_t>(__popcll(hits[q] & below));
+            if (hit && r < cap) out[r] = kc[q].idx;
+        }
+    }
+#pragma nounroll
+    for (uint32_t todo = rescan; todo != 0; todo &= todo - 1u) {
+        const uint32_t c = wave + 4u * static_cast<uint32_t>(__builtin_ctz(todo));
+        uint32_t pos = sc[c];
+        if (pos >= cap) continue;
+        scan_span(rs, chunk_span(c), lane, [&](uint32_t i, float v, bool in) {
+            const bool hit = in && v >= thr;
+            const uint64_t m = __ballot(hit);
+            const uint32_t r = pos + static_cast<uint32_t>(__popcll(m & below));
+            if (hit && r < cap) out[r] = i;
+            pos += static_cast<uint32_t>(__popcll(m));
+        });
+    }
 }
 
 }  // namespace
@@ -226,13 +372,14 @@ hipError_t launch_argmax_candidates(const float *logits, uint32_t n_slots, uint3
     if (n_slots == 0 || n_slots > kMaxGridY) return hipErrorInvalidValue;
     const uint32_t chunk = sample_chunk(vocab);
     const uint32_t chunks = (vocab + chunk - 1) / chunk;
-    auto *part = static_cast<ArgMax *>(workspace);
-    auto *counts = reinterpret_cast<uint32_t *>(part + static_cast<uint64_t>(n_slots) * chunks);
+    const SampleWs ws = sample_ws(workspace, n_slots, chunks);
     const dim3 grid(chunks, n_slots), block(256);
-    hipLaunchKernelGGL(k_argmax_partial, grid, block, 0, stream, logits, vocab, chunk, part);
-    hipLaunchKernelGGL(k_cand_count, grid, block, 0, stream, logits, vocab, chunk, part, counts, top1_idx, top1_val);
-    hipLaunchKernelGGL(k_cand_collect, grid, block, 0, stream, logits, vocab, chunk, part, counts, cap, cand_count,
-                       overflow, cand_ids);
+    if (chunk / 4 <= 64 * kRound)
+        hipLaunchKernelGGL(k_sample_scan<true>, grid, block, 0, stream, logits, vocab, chunk, ws);
+    else
+        hipLaunchKernelGGL(k_sample_scan<false>, grid, block, 0, stream, logits, vocab, chunk, ws);
+    hipLaunchKernelGGL(k_sample_finish, dim3(n_slots), block, 0, stream, logits, vocab, chunk, chunks, ws, cap,
+                       top1_idx, top1_val, cand_count, overflow, cand_ids);
     return hipGetLastError();
 }
 

@@ -25,11 +25,12 @@ uint32_t sample_chunk(uint32_t vocab) {
 }
 
 uint64_t sample_workspace_bytes(uint32_t n_slots, uint32_t vocab) {
-    // Per slot and chunk: one partial maximum, then the candidate counts of
-    // the chunk's four quarters.
+    // Per slot and chunk: one partial maximum, the kept local candidates and
+    // their count.
     const uint32_t chunk = sample_chunk(vocab);
     const uint64_t chunks = (vocab + chunk - 1) / chunk;
-    return static_cast<uint64_t>(n_slots) * chunks * (kSampleArgMaxBytes + 4 * sizeof(uint32_t));
+    return static_cast<uint64_t>(n_slots) * chunks *
+           (kSampleArgMaxBytes + kSampleLocalCap * kSampleCandBytes + sizeof(uint32_t));
 }
 
 uint32_t moe_tiles_max(uint32_t routes, uint32_t n_experts) {

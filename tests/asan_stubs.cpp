@@ -157,15 +157,17 @@ hipError_t launch_argmax_candidates(const float *logits, uint32_t n_slots, uint3
                                     uint32_t *cand_ids, void *workspace, hipStream_t) {
     if (n_slots == 0 || n_slots > kMaxGridY) return hipErrorInvalidValue;
     if (reinterpret_cast<uintptr_t>(workspace) & 7u) return hipErrorInvalidValue;
-    // Workspace layout of the three launches: one 8-byte partial (value,
-    // index) per (slot, chunk), then four u32 quarter counts per (slot, chunk).
+    // Workspace layout of the two launches, per (slot, chunk): an 8-byte
+    // partial (value, index) each, then kSampleLocalCap 8-byte kept candidates
+    // each, then a u32 local candidate count each. The scan writes them all;
+    // the finish pass reads them all back.
     const uint32_t chunk = sample_chunk(vocab);
     const uint64_t chunks = (vocab + chunk - 1) / chunk;
     const uint64_t parts = static_cast<uint64_t>(n_slots) * chunks;
+    const uint64_t bytes = parts * (8 + 8ull * kSampleLocalCap + 4);
     read_bytes(logits, 4ull * n_slots * vocab);
-    write_bytes(workspace, parts * 8);
-    write_bytes(static_cast<uint8_t *>(workspace) + parts * 8, parts * 16);
-    read_bytes(workspace, parts * 24);
+    write_bytes(workspace, bytes);
+    read_bytes(workspace, bytes);
     write_bytes(top1_idx, 4ull * n_slots);
     write_bytes(top1_val, 4ull * n_slots);
     write_bytes(cand_count, 4ull * n_slots);
