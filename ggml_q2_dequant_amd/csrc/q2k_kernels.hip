@@ -69,12 +69,15 @@ __device__ __forceinline__ float4 decode_quad(const uint8_t *blk, uint32_t e0) {
 // with direct buffer-to-LDS dword loads, all in flight at once, then writes
 // block i as one 1 KiB run of 16-byte stores, lane l taking weights
 // 4l..4l+3. With one block per wavefront (84 bytes of reads in flight) the
-// dequantize mostly waited on memory latency; with runs of 64 blocks a
-// wavefront's whole input (5376 bytes) is requested before any of it is
-// needed. A wavefront only touches its own region, so there are no barriers.
-constexpr uint32_t kRunBlocks = 64;                           // blocks per dequantize wavefront
-constexpr uint32_t kRunDwords = kRunBlocks * kBlockBytes / 4;  // 1344 = 21 loads of 64 dwords
-static_assert(kRunDwords % kWave == 0, "stage_blocks fills whole loads of 64 dwords: the region must hold them");
+// dequantize mostly waited on memory latency; with runs of 32 blocks a
+// wavefront's whole input (2688 bytes) is requested before any of it is
+// needed (65536 blocks: 12.2 us, against 12.3-12.5 us with runs of 64 and
+// 12.7 us with runs of 16). A wavefront only touches its own region, so
+// there are no barriers.
+constexpr uint32_t kRunBlocks = 32;  // blocks per dequantize wavefront
+// Its region: 672 dwords of blocks, rounded up to whole loads of 64 dwords (the
+// last load reads past the run, beyond the descriptor: zeros).
+constexpr uint32_t kRunDwords = (kRunBlocks * kBlockBytes / 4 + kWave - 1) / kWave * kWave;
 
 // Copies blocks src[0 .. nb) into r (ceil(21 nb / 64) * 64 dwords, which r
 // must hold) and waits until they are in. Loads past the last block lie
