@@ -9,6 +9,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <map>
@@ -81,10 +82,18 @@ q2k_status check_matmul(const float *x, const void *w, const float *y, uint32_t 
     return Q2K_OK;
 }
 
-// One pinned, device-visible status word per device for the gather's id check.
+// Per device, for the synchronous gather: a device word the gather kernel
+// stores a bad id's marker into, and a pinned, host-coherent word that a
+// one-thread kernel queued behind it publishes the outcome to. The host polls
+// the pinned word instead of synchronizing the stream, which costs several
+// microseconds more per call. Each call tags its marker and its published
+// word with a fresh sequence number, so nothing an earlier call left behind
+// reads as this call's.
 struct StatusWord {
-    int *host = nullptr;
-    int *dev = nullptr;
+    int *host = nullptr;      // pinned, mapped, coherent
+    int *host_dev = nullptr;  // the same word's device address
+    int *dev = nullptr;       // device memory, zeroed once
+    uint32_t seq = 0;
     std::mutex mu;
 };
 
@@ -122,16 +131,21 @@ q2k_status status_word(StatusWord **out) {
     if (g_status.size() <= static_cast<size_t>(dev)) g_status.resize(dev + 1, nullptr);
     if (!g_status[dev]) {
         auto *sw = new StatusWord;
-        e = hipHostMalloc(reinterpret_cast<void **>(&sw->host), sizeof(int), hipHostMallocMapped);
+        e = hipHostMalloc(reinterpret_cast<void **>(&sw->host), sizeof(int), hipHostMallocMapped | hipHostMallocCoherent);
         if (e != hipSuccess) {
             delete sw;
             return device_error("hipHostMalloc(status word)", e);
         }
-        e = hipHostGetDevicePointer(reinterpret_cast<void **>(&sw->dev), sw->host, 0);
+        *sw->host = 0;
+        e = hipHostGetDevicePointer(reinterpret_cast<void **>(&sw->host_dev), sw->host, 0);
+        if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&sw->dev), sizeof(int));
+        if (e == hipSuccess) e = hipMemset(sw->dev, 0, sizeof(int));
+        if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) {
+            if (sw->dev) (void)hipFree(sw->dev);
             (void)hipHostFree(sw->host);
             delete sw;
-            return device_error("hipHostGetDevicePointer(status word)", e);
+            return device_error("status word set-up", e);
         }
         g_status[dev] = sw;
     }
@@ -671,19 +685,45 @@ q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *o
                                 uint32_t embed_dim, uint32_t n_tokens, void *stream) {
     q2k_status s = check_gather("q2k_embedding_gather", table, ids, out, vocab, embed_dim, n_tokens);
     if (s != Q2K_OK) return s;
+    const auto st = static_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e != hipSuccess) return device_error("hipStreamIsCapturing", e);
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(Q2K_ERR_INVALID_ARGUMENT,
+                    "q2k_embedding_gather: waits on the host, so it cannot be captured; use q2k_embedding_gather_async");
     StatusWord *sw = nullptr;
     s = status_word(&sw);
     if (s != Q2K_OK) return s;
     std::lock_guard<std::mutex> lock(sw->mu);
-    *sw->host = 0;
-    const auto st = static_cast<hipStream_t>(stream);
-    hipError_t e = q2k::launch_gather(static_cast<const uint8_t *>(table), ids, out, vocab, embed_dim / q2k::kQK,
-                                      n_tokens, sw->dev, st);
+    // Sequence numbers run over 1 .. 2^29 - 1, so (seq << 2) | 3 stays a positive int.
+    sw->seq = sw->seq % ((1u << 29) - 1) + 1;
+    const int seq = static_cast<int>(sw->seq);
+    e = q2k::launch_gather(static_cast<const uint8_t *>(table), ids, out, vocab, embed_dim / q2k::kQK, n_tokens,
+                           sw->dev, seq, st);
     if (e != hipSuccess) return device_error("q2k_embedding_gather launch", e);
-    e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return device_error("q2k_embedding_gather sync", e);
-    const int bad = __atomic_load_n(sw->host, __ATOMIC_ACQUIRE);
-    if (bad) return fail(Q2K_ERR_ID_OUT_OF_RANGE, "q2k_embedding_gather: a token id is >= vocab (%u)", vocab);
+    e = q2k::launch_gather_done(sw->dev, seq, sw->host_dev, st);
+    if (e != hipSuccess) return device_error("q2k_embedding_gather launch", e);
+    // Poll for the published word; past about 2 ms (a stream with other work
+    // queued ahead) wait on the stream instead, which also reports any fault.
+    const int want = (seq << 2) | 2;
+    int v = __atomic_load_n(sw->host, __ATOMIC_ACQUIRE);
+    if ((v & ~1) != want) {
+        const auto t0 = std::chrono::steady_clock::now();
+        for (;;) {
+            v = __atomic_load_n(sw->host, __ATOMIC_ACQUIRE);
+            if ((v & ~1) == want) break;
+            if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(2)) {
+                e = hipStreamSynchronize(st);
+                if (e != hipSuccess) return device_error("q2k_embedding_gather sync", e);
+                v = __atomic_load_n(sw->host, __ATOMIC_ACQUIRE);
+                if ((v & ~1) != want)
+                    return fail(Q2K_ERR_DEVICE, "q2k_embedding_gather: the completion word was not published");
+                break;
+            }
+        }
+    }
+    if (v & 1) return fail(Q2K_ERR_ID_OUT_OF_RANGE, "q2k_embedding_gather: a token id is >= vocab (%u)", vocab);
     return ok();
 }
 
@@ -698,7 +738,7 @@ q2k_status q2k_embedding_gather_async(const void *table, const uint32_t *ids, fl
     if (overlap(status, 4, out, ob) || overlap(status, 4, table, tb) || overlap(status, 4, ids, 4ull * n_tokens))
         return fail(Q2K_ERR_INVALID_ARGUMENT, "q2k_embedding_gather_async: status overlaps an input or out");
     hipError_t e = q2k::launch_gather(static_cast<const uint8_t *>(table), ids, out, vocab, embed_dim / q2k::kQK,
-                                      n_tokens, status, static_cast<hipStream_t>(stream));
+                                      n_tokens, status, 1, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_error("q2k_embedding_gather_async launch", e);
     return ok();
 }

@@ -115,7 +115,7 @@ constexpr uint32_t kGatherDwords = (kGatherRun * kBlockBytes / 4 + kWave - 1) / 
 
 __global__ __launch_bounds__(256) void k_gather(const uint8_t *__restrict__ table, const uint32_t *__restrict__ ids,
                                                 float4 *__restrict__ out, uint32_t vocab, uint32_t blocks_per_row,
-                                                uint32_t n_tokens, int *status) {
+                                                uint32_t n_tokens, int *status, int bad_value) {
     __shared__ __attribute__((aligned(16))) uint32_t raw[4][kGatherDwords];
     const uint32_t lane = threadIdx.x & (kWave - 1u);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void k_gather(const uint8_t *__restrict__ tabl
     const uint32_t t = static_cast<uint32_t>(u / runs), c = static_cast<uint32_t>(u % runs);
     const uint32_t id = ids[t];
     if (id >= vocab) {
-        if (c == 0 && lane == 0) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (c == 0 && lane == 0) __hip_atomic_store(status, bad_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         return;
     }
     const uint32_t kb0 = c * kGatherRun, nb = min(kGatherRun, blocks_per_row - kb0);
@@ -134,6 +134,21 @@ __global__ __launch_bounds__(256) void k_gather(const uint8_t *__restrict__ tabl
     const uint8_t *rb = reinterpret_cast<const uint8_t *>(raw[wave]);
     float4 *orow = out + (static_cast<uint64_t>(t) * blocks_per_row + kb0) * 64u;
     for (uint32_t i = 0; i < nb; ++i) orow[i * 64u + lane] = decode_quad(rb + i * kBlockBytes, 4u * lane);
+}
+
+// The end of a synchronous gather, for a host that polls memory instead of
+// synchronizing the stream (which costs several microseconds more): this
+// kernel starts only after the gather kernel before it on the stream has
+// ended, and its one store to host-visible memory carries both the call's
+// sequence number and whether that gather saw a bad id (the gather stores the
+// number itself into *status, so a value left by an earlier call never reads
+// as this call's). Folding this into the gather (the last workgroup to finish
+// publishing) costs more: every workgroup then needs an agent-scope release,
+// an L2 write-back, before it counts itself.
+__global__ __launch_bounds__(64) void k_gather_done(const int *__restrict__ status, int seq, int *host_word) {
+    if (threadIdx.x != 0) return;
+    const int v = __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(host_word, (seq << 2) | 2 | (v == seq ? 1 : 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // ---------------------------------------------------------------------------
@@ -1777,12 +1792,17 @@ hipError_t launch_dequantize(const uint8_t *blocks, uint64_t nblocks, float *out
 }
 
 hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, uint32_t vocab,
-                         uint32_t blocks_per_row, uint32_t n_tokens, int *status, hipStream_t stream) {
+                         uint32_t blocks_per_row, uint32_t n_tokens, int *status, int bad_value, hipStream_t stream) {
     const uint64_t runs = (blocks_per_row + kGatherRun - 1) / kGatherRun;
     const uint64_t grid = (static_cast<uint64_t>(n_tokens) * runs + 3) / 4;
     if (grid > 0x7fffffffu) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_gather, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, table, ids,
-                       reinterpret_cast<float4 *>(out), vocab, blocks_per_row, n_tokens, status);
+                       reinterpret_cast<float4 *>(out), vocab, blocks_per_row, n_tokens, status, bad_value);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_done(const int *status, int seq, int *host_word, hipStream_t stream) {
+    hipLaunchKernelGGL(k_gather_done, dim3(1), dim3(64), 0, stream, status, seq, host_word);
     return hipGetLastError();
 }
 

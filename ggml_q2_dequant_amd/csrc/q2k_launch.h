@@ -19,8 +19,15 @@ constexpr uint32_t kMaxGridY = 65535;  // largest batch count one GEMV launch ta
 
 hipError_t launch_dequantize(const uint8_t *blocks, uint64_t nblocks, float *out, hipStream_t stream);
 
+// A bad id (>= vocab) makes the kernel store bad_value into *status.
 hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, uint32_t vocab,
-                         uint32_t blocks_per_row, uint32_t n_tokens, int *status, hipStream_t stream);
+                         uint32_t blocks_per_row, uint32_t n_tokens, int *status, int bad_value, hipStream_t stream);
+
+// Queued after launch_gather on the same stream, so it starts once the gather
+// kernel has ended: one thread stores (seq << 2) | 2 | (*status == seq) into
+// *host_word (host-visible memory, system scope), which the host can poll for
+// the end of the gather and its id check.
+hipError_t launch_gather_done(const int *status, int seq, int *host_word, hipStream_t stream);
 
 // 1 <= M <= 8; batches problems laid out batch-major (x [batches, M, K],
 // w [batches, N, K/256 blocks], y [batches, M, N]), 1 <= batches <= kMaxGridY.

@@ -297,11 +297,16 @@ q2k_status q2k_matmul_id_pooled_slotted(const float *x, const void *w, const uin
  *   vocab, n_tokens >= 1; embed_dim >= 256 and a multiple of 256.
  * Rows are bit-identical to q2k_dequantize of the same blocks. The kernel
  * checks every id on the GPU and never reads a row at or beyond vocab; the
- * call then waits for `stream` and returns Q2K_ERR_ID_OUT_OF_RANGE if any id
+ * call then waits for the kernel and returns Q2K_ERR_ID_OUT_OF_RANGE if any id
  * was >= vocab. In that case rows of valid ids hold their values and rows of
- * bad ids are left unwritten. Synchronous: it returns after the kernel ends.
- * Uses one small pinned status word per device, created on first use; calls
- * from several host threads are serialised on it.
+ * bad ids are left unwritten. Synchronous: it returns after the kernel, and
+ * so all work queued on `stream` before it, has ended. The wait polls a
+ * pinned word that a one-thread kernel queued behind the gather writes; past
+ * about 2 ms it waits on `stream` instead (which also reports a fault in work
+ * queued earlier). Not allowed while `stream` is capturing a graph
+ * (Q2K_ERR_INVALID_ARGUMENT; use q2k_embedding_gather_async). Uses one pinned
+ * and one device word per device, created on first use; calls from several
+ * host threads are serialised on them.
  */
 q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *out, uint32_t vocab,
                                 uint32_t embed_dim, uint32_t n_tokens, void *stream);

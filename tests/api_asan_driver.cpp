@@ -215,6 +215,10 @@ void capture_cases() {
            "growth during capture must be refused");
     EXPECT(q2k_matmul(x.as<float>(), w.p, y.as<float>(), 1, 8, 512, stream(7)) == Q2K_OK,
            "a GEMV call needs no workspace during capture");
+    Buf table(wbytes(4, 256)), ids(4 * 2), emb(4ull * 2 * 256);
+    EXPECT(q2k_embedding_gather(table.p, ids.as<uint32_t>(), emb.as<float>(), 4, 256, 2, stream(7)) ==
+               Q2K_ERR_INVALID_ARGUMENT,
+           "the synchronous gather must be refused during capture");
     stub_set_capturing(0);
     EXPECT(stub_mallocs() == before, "no allocation during capture");
     EXPECT(stub_launches() == launches + 2, "the refused call enqueued nothing");

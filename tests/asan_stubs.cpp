@@ -84,6 +84,18 @@ hipError_t hipHostGetDevicePointer(void **devPtr, void *hstPtr, unsigned int) {
     return hipSuccess;
 }
 
+hipError_t hipFree(void *ptr) {
+    std::free(ptr);
+    return hipSuccess;
+}
+
+hipError_t hipMemset(void *dst, int value, size_t sizeBytes) {
+    std::memset(dst, value, sizeBytes);
+    return hipSuccess;
+}
+
+hipError_t hipDeviceSynchronize(void) { return hipSuccess; }
+
 hipError_t hipHostFree(void *ptr) {
     std::free(ptr);
     return hipSuccess;
@@ -107,7 +119,7 @@ hipError_t launch_dequantize(const uint8_t *blocks, uint64_t nblocks, float *out
 }
 
 hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, uint32_t vocab,
-                         uint32_t blocks_per_row, uint32_t n_tokens, int *status, hipStream_t) {
+                         uint32_t blocks_per_row, uint32_t n_tokens, int *status, int bad_value, hipStream_t) {
     // Each token's row of blocks_per_row blocks, or a NaN row and the status
     // word for an id >= vocab.
     const uint64_t rb = static_cast<uint64_t>(blocks_per_row) * kBlockBytes;
@@ -116,9 +128,16 @@ hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, 
         if (id < vocab)
             read_bytes(table + id * rb, rb);
         else
-            *status = 1;
+            *status = bad_value;
         write_bytes(out + static_cast<uint64_t>(t) * blocks_per_row * kQK, 4ull * blocks_per_row * kQK);
     }
+    return launched();
+}
+
+hipError_t launch_gather_done(const int *status, int seq, int *host_word, hipStream_t) {
+    // Stands in for the one-thread kernel: publishes the outcome at once.
+    const int v = __atomic_load_n(status, __ATOMIC_RELAXED);
+    __atomic_store_n(host_word, (seq << 2) | 2 | (v == seq ? 1 : 0), __ATOMIC_RELEASE);
     return launched();
 }
 

@@ -169,6 +169,39 @@ def test_gather_page_fixture_and_bad_id():
     assert bits_equal(gpu_gather(table, [1, 1], vocab, QK_K, 2), oracle.gather(table, [1, 1], vocab, QK_K, 2))
 
 
+def test_gather_returns_after_work_queued_ahead_of_it():
+    # The call returns only once everything queued on its stream before it has
+    # ended: with a short queue (it polls the word its completion kernel
+    # publishes) and behind a spin of many milliseconds (past the poll bound it
+    # waits on the stream). A rejected id between good calls must not leak into
+    # the next call's verdict.
+    vocab = 3
+    table = np.concatenate([synth.page_block(r + 2) for r in range(vocab)])
+    tbl = dev(table)
+    s = torch.cuda.current_stream()
+    marker = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    cases = [(0, [2, 0]), (20_000_000, [1, 2]), (0, [0, 0]), (0, [2, vocab]), (20_000_000, [1, 0]), (0, [vocab + 7, 1]),
+             (0, [1, 1])]
+    for k, (cycles, ids) in enumerate(cases):
+        out = torch.full((2, QK_K), float("nan"), dtype=torch.float32, device="cuda:0")
+        idd = dev(np.asarray(ids, dtype=np.uint32))
+        torch.cuda.synchronize()
+        if cycles:
+            torch.cuda._sleep(cycles)
+        marker.fill_(float(k + 1))
+        ev = torch.cuda.Event()
+        ev.record(s)
+        if max(ids) >= vocab:
+            with pytest.raises(q2k.Q2KIdOutOfRange):
+                q2k.q2k_embedding_gather(tbl, idd, out, vocab, QK_K, 2, stream=s)
+            assert ev.query(), "returned before the work queued ahead ended"
+            continue
+        q2k.q2k_embedding_gather(tbl, idd, out, vocab, QK_K, 2, stream=s)
+        assert ev.query(), "returned before the work queued ahead ended"
+        assert float(marker.item()) == float(k + 1)
+        assert bits_equal(out.cpu().numpy(), oracle.gather(table, ids, vocab, QK_K, 2))
+
+
 def test_gather_ragged_multi_block_rows_with_duplicates():
     rng = np.random.Generator(np.random.PCG64(34))
     vocab, dim = 5, 768
