@@ -28,7 +28,7 @@
 // and writes the first cap candidate ids in index order, the total and the
 // overflow flag. Within a chunk each wavefront walks its quarter 64 columns
 // at a time (coalesced); ballots and lane masks rank candidates inside a
-// wavefront. For 8 x 262144 Gaussian logits the two take 12.7 us per call,
+// wavefront. For 8 x 262144 Gaussian logits the two take 12.2 us per call,
 // against 14.7 us for three passes (maximum, count, collect) that each read
 // the logits.
 #include <hip/hip_runtime.h>
@@ -57,18 +57,6 @@ __device__ __forceinline__ ArgMax pick(ArgMax a, ArgMax b) {
     return b.idx < a.idx ? b : a;
 }
 
-__device__ __forceinline__ ArgMax shfl_xor(ArgMax a, int mask) {
-    ArgMax r;
-    r.val = __shfl_xor(a.val, mask, 64);
-    r.idx = static_cast<uint32_t>(__shfl_xor(static_cast<int>(a.idx), mask, 64));
-    return r;
-}
-
-__device__ __forceinline__ ArgMax wave_pick(ArgMax a) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) a = pick(a, shfl_xor(a, m));
-    return a;
-}
 
 // Columns of chunk c of a slot: [c * chunk, min((c + 1) * chunk, vocab)); wave w
 // of the workgroup takes the w-th quarter of them.
@@ -141,6 +129,66 @@ inline SampleWs sample_ws(void *ws, uint32_t n_slots, uint32_t chunks) {
     return w;
 }
 
+// Wavefront reductions without a trip through LDS: within each row of 16
+// lanes by DPP moves (quad xor 1, quad xor 2, row rotations by 4 and 8), then
+// across rows by the gfx950 lane swaps (rows 0/1 and 2/3, then the halves),
+// which hand every lane of a pair both partners' values.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ ArgMax dpp_move(ArgMax a) {
+    return ArgMax{dpp_move<CTRL>(a.val),
+                  static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(a.idx), CTRL, 0xF, 0xF, false))};
+}
+
+// The values of the two rows (16 lanes) or halves (32 lanes) that a lane swap
+// pairs, at the lane's position, in every lane of either.
+__device__ __forceinline__ void swap16(uint32_t v, uint32_t *even, uint32_t *odd) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    *even = r[0];
+    *odd = r[1];
+}
+
+__device__ __forceinline__ void swap32(uint32_t v, uint32_t *lo, uint32_t *hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    *lo = r[0];
+    *hi = r[1];
+}
+
+// The wavefront's first maximum (pick over all 64 lanes) in every lane, by the
+// same moves as wave_fmax; pick is a maximum under a total order, so the
+// order of combination does not matter.
+__device__ __forceinline__ ArgMax wave_pick(ArgMax a) {
+    a = pick(a, dpp_move<0xB1>(a));
+    a = pick(a, dpp_move<0x4E>(a));
+    a = pick(a, dpp_move<0x124>(a));
+    a = pick(a, dpp_move<0x128>(a));
+    uint32_t v0, v1, i0, i1;
+    swap16(__builtin_bit_cast(uint32_t, a.val), &v0, &v1);
+    swap16(a.idx, &i0, &i1);
+    a = pick(ArgMax{__builtin_bit_cast(float, v0), i0}, ArgMax{__builtin_bit_cast(float, v1), i1});
+    swap32(__builtin_bit_cast(uint32_t, a.val), &v0, &v1);
+    swap32(a.idx, &i0, &i1);
+    return pick(ArgMax{__builtin_bit_cast(float, v0), i0}, ArgMax{__builtin_bit_cast(float, v1), i1});
+}
+
+// The largest non-NaN value over the wavefront in every lane (NaN if all are
+// NaN; max ignores NaN).
+__device__ __forceinline__ float wave_fmax(float m) {
+    m = __builtin_fmaxf(m, dpp_move<0xB1>(m));   // quad_perm [1,0,3,2]
+    m = __builtin_fmaxf(m, dpp_move<0x4E>(m));   // quad_perm [2,3,0,1]
+    m = __builtin_fmaxf(m, dpp_move<0x124>(m));  // row_ror 4
+    m = __builtin_fmaxf(m, dpp_move<0x128>(m));  // row_ror 8
+    uint32_t e, o;
+    swap16(__builtin_bit_cast(uint32_t, m), &e, &o);
+    m = __builtin_fmaxf(__builtin_bit_cast(float, e), __builtin_bit_cast(float, o));
+    swap32(__builtin_bit_cast(uint32_t, m), &e, &o);
+    return __builtin_fmaxf(__builtin_bit_cast(float, e), __builtin_bit_cast(float, o));
+}
+
 // The wavefront's first maximum over its quarter when the quarter is one
 // round held in registers (v[u] is column begin + 64 u + lane, NaN past the
 // row): the largest non-NaN value M (max ignores NaN), then the lowest
@@ -150,8 +198,7 @@ __device__ __forceinline__ ArgMax round_first_max(const float (&v)[kRound], uint
     float m = v[0];
 #pragma unroll
     for (uint32_t u = 1; u < kRound; ++u) m = __builtin_fmaxf(m, v[u]);
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, d, 64));
+    m = wave_fmax(m);
     if (m != m) return ArgMax{0.0f, kNone};  // no non-NaN value in the quarter
     // Steps in column order; the first whose ballot finds M holds the answer in its lowest such lane.
 #pragma unroll
@@ -187,12 +234,16 @@ __global__ __launch_bounds__(256) void k_sample_scan(const float *__restrict__ l
     if constexpr (kOneRound) {
         // Column begin + 64 u + lane at byte offset 4 (begin + lane) + 256 u (the step in the scalar offset);
         // past the quarter it is another wavefront's logit or, past the row, zero: NaN either way here.
+        // All 32 loads are issued before the first is used (left free, the scheduler starts the maximum
+        // after 24 of them and issues the rest a memory latency later).
         const uint32_t len = s.end - s.begin;
+        uint32_t e[kRound];
 #pragma unroll
-        for (uint32_t u = 0; u < kRound; ++u) {
-            const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(rs, 4u * (s.begin + lane), 256u * u, 0);
-            v1[u] = 64u * u + lane < len ? __builtin_bit_cast(float, e) : __builtin_nanf("");
-        }
+        for (uint32_t u = 0; u < kRound; ++u)
+            e[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4u * (s.begin + lane), 256u * u, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (uint32_t u = 0; u < kRound; ++u) v1[u] = 64u * u + lane < len ? __builtin_bit_cast(float, e[u]) : __builtin_nanf("");
         best = round_first_max(v1, s.begin, lane);
     } else {
         scan_span(rs, s, lane, [&](uint32_t i, float v, bool in) {
@@ -244,12 +295,10 @@ __global__ __launch_bounds__(256) void k_sample_scan(const float *__restrict__ l
     }
 }
 
-// The slot's top1 from its chunk partials (read by one wavefront).
-__device__ __forceinline__ ArgMax slot_top1(const float *row, const ArgMax *part, uint32_t chunks, uint32_t lane) {
-    ArgMax b{0.0f, kNone};
-    for (uint32_t c = lane; c < chunks; c += 64) b = pick(b, part[c]);
+// The slot's top1 from its chunk partials, lane c holding chunk c's (c < chunks <= 64), and column 0.
+__device__ __forceinline__ ArgMax slot_top1(ArgMax own, float x0, uint32_t chunks, uint32_t lane) {
+    ArgMax b = lane < chunks ? own : ArgMax{0.0f, kNone};
     b = wave_pick(b);
-    const float x0 = row[0];
     if (x0 != x0) b = ArgMax{x0, 0};     // the scan starts at column 0 and NaN is never beaten
     if (b.idx == kNone) b = ArgMax{x0, 0};  // unreachable unless column 0 is NaN
     return b;
@@ -279,6 +328,11 @@ __global__ __launch_bounds__(256) void k_sample_finish(const float *__restrict__
     const uint64_t p0 = static_cast<uint64_t>(slot) * chunks;
     uint32_t nl[kFinishPer];
     Cand kc[kFinishPer];
+    // Every load of the pass up front (clamped addresses, nothing conditional), so it waits out one memory
+    // latency: the partials (one chunk per lane), column 0, the counts and kept candidates.
+    static_assert(kSampleMaxChunks <= 64, "one chunk partial per lane");
+    const ArgMax own = ws.part[p0 + min(lane, chunks - 1u)];
+    const float x0 = row[0];
 #pragma unroll
     for (uint32_t q = 0; q < kFinishPer; ++q) {
         const uint32_t c = min(wave + 4u * q, chunks - 1u);
@@ -286,7 +340,7 @@ __global__ __launch_bounds__(256) void k_sample_finish(const float *__restrict__
         kc[q] = ws.cand[(p0 + c) * kSampleLocalCap + lane];
     }
     if (wave == 0) {
-        const ArgMax t = slot_top1(row, ws.part + p0, chunks, lane);
+        const ArgMax t = slot_top1(own, x0, chunks, lane);
         if (lane == 0) {
             thr_s = t.val - 0.5f;
             top1_idx[slot] = t.idx;
