@@ -28,7 +28,7 @@
 // and writes the first cap candidate ids in index order, the total and the
 // overflow flag. Within a chunk each wavefront walks its quarter 64 columns
 // at a time (coalesced); ballots and lane masks rank candidates inside a
-// wavefront. For 8 x 262144 Gaussian logits the two take 12.2 us per call,
+// wavefront. For 8 x 262144 Gaussian logits the two take 10.9 us per call,
 // against 14.7 us for three passes (maximum, count, collect) that each read
 // the logits.
 #include <hip/hip_runtime.h>
@@ -73,32 +73,42 @@ __device__ __forceinline__ Span wave_span(uint32_t c, uint32_t chunk, uint32_t v
     return s;
 }
 
-// Walks a wavefront's span 64 columns at a time, 32 steps per round: all 32
+// Walks a wavefront's span 64 columns at a time, R steps per round: all R
 // loads of a round are issued before any is used (buffer loads past the row
 // return 0 and are flagged out of range), then f(column, value, in_range) runs
-// in increasing column order. A quarter of an 8192-column chunk is one round,
-// so each pass over the logits waits out one memory latency per wavefront (in
-// an earlier three-pass form of this call, rounds of 8 took 18.8 us for
-// 8 x 262144 logits and rounds of 32 16.2 us). With one round the scan keeps
-// the values in registers for all its walks (round_first_max and below).
+// in increasing column order, so each pass over the logits waits out one
+// memory latency per round (in an earlier three-pass form of this call,
+// rounds of 8 took 18.8 us for 8 x 262144 logits and rounds of 32 16.2 us).
+// The scan walks chunks longer than 4096 logits (vocabularies above 2^18) in
+// rounds of 32.
 constexpr uint32_t kRound = 32;
+
+// Chunks of 4096 logits (the minimum) take the one-round form instead: a
+// wavefront's quarter is 16 steps, all loaded up front and held in registers
+// for every walk (round_first_max and below). 4096-logit chunks give 512
+// workgroups for 8 x 262144 logits: 10.9 us per call, against 12.2 us with
+// 8192-logit chunks (256 workgroups, 32 steps) and 13.8 us with 2048 (the
+// finish pass then holds twice the chunks). The finish pass's rare rescans
+// of whole chunks also go in rounds of 16: rounds of 32 there cost its
+// common path registers and 0.6 us per call.
+constexpr uint32_t kOneRoundSteps = 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float *row, uint32_t vocab) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(row), 0, static_cast<int>(vocab * 4u), 0x00020000);
 }
 
-template <typename F>
+template <uint32_t R, typename F>
 __device__ __forceinline__ void scan_span(__amdgpu_buffer_rsrc_t rs, Span s, uint32_t lane, F f) {
-    for (uint32_t i0 = s.begin; i0 < s.end; i0 += 64 * kRound) {
-        float v[kRound];
+    for (uint32_t i0 = s.begin; i0 < s.end; i0 += 64 * R) {
+        float v[R];
 #pragma unroll
-        for (uint32_t u = 0; u < kRound; ++u) {
+        for (uint32_t u = 0; u < R; ++u) {
             const uint32_t i = i0 + 64 * u + lane;
             const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(rs, i < s.end ? 4u * i : 0x80000000u, 0, 0);
             v[u] = __builtin_bit_cast(float, e);
         }
 #pragma unroll
-        for (uint32_t u = 0; u < kRound; ++u) {
+        for (uint32_t u = 0; u < R; ++u) {
             const uint32_t i = i0 + 64 * u + lane;
             f(i, v[u], i < s.end);
         }
@@ -194,15 +204,15 @@ __device__ __forceinline__ float wave_fmax(float m) {
 // row): the largest non-NaN value M (max ignores NaN), then the lowest
 // column holding a value equal to M, and that column's own value (so +0 and
 // -0 keep their bits).
-__device__ __forceinline__ ArgMax round_first_max(const float (&v)[kRound], uint32_t begin, uint32_t lane) {
+__device__ __forceinline__ ArgMax round_first_max(const float (&v)[kOneRoundSteps], uint32_t begin, uint32_t lane) {
     float m = v[0];
 #pragma unroll
-    for (uint32_t u = 1; u < kRound; ++u) m = __builtin_fmaxf(m, v[u]);
+    for (uint32_t u = 1; u < kOneRoundSteps; ++u) m = __builtin_fmaxf(m, v[u]);
     m = wave_fmax(m);
     if (m != m) return ArgMax{0.0f, kNone};  // no non-NaN value in the quarter
     // Steps in column order; the first whose ballot finds M holds the answer in its lowest such lane.
 #pragma unroll
-    for (uint32_t u = 0; u < kRound; ++u) {
+    for (uint32_t u = 0; u < kOneRoundSteps; ++u) {
         const uint64_t b = __ballot(v[u] == m);
         if (b != 0) {
             const uint32_t l = static_cast<uint32_t>(__builtin_ctzll(b));
@@ -229,24 +239,24 @@ __global__ __launch_bounds__(256) void k_sample_scan(const float *__restrict__ l
     const uint64_t below = (1ull << lane) - 1ull;
     const uint64_t pc = static_cast<uint64_t>(slot) * chunks + c;
     Cand *out = ws.cand + pc * kSampleLocalCap;
-    float v1[kRound];  // kOneRound: the wavefront's whole quarter, NaN past the row
+    float v1[kOneRoundSteps];  // kOneRound: the wavefront's whole quarter, NaN past the row
     ArgMax best{0.0f, kNone};
     if constexpr (kOneRound) {
         // Column begin + 64 u + lane at byte offset 4 (begin + lane) + 256 u (the step in the scalar offset);
         // past the quarter it is another wavefront's logit or, past the row, zero: NaN either way here.
-        // All 32 loads are issued before the first is used (left free, the scheduler starts the maximum
-        // after 24 of them and issues the rest a memory latency later).
+        // All loads are issued before the first is used (left free, the scheduler may start the maximum
+        // after some of them and issue the rest a memory latency later).
         const uint32_t len = s.end - s.begin;
-        uint32_t e[kRound];
+        uint32_t e[kOneRoundSteps];
 #pragma unroll
-        for (uint32_t u = 0; u < kRound; ++u)
+        for (uint32_t u = 0; u < kOneRoundSteps; ++u)
             e[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4u * (s.begin + lane), 256u * u, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (uint32_t u = 0; u < kRound; ++u) v1[u] = 64u * u + lane < len ? __builtin_bit_cast(float, e[u]) : __builtin_nanf("");
+        for (uint32_t u = 0; u < kOneRoundSteps; ++u) v1[u] = 64u * u + lane < len ? __builtin_bit_cast(float, e[u]) : __builtin_nanf("");
         best = round_first_max(v1, s.begin, lane);
     } else {
-        scan_span(rs, s, lane, [&](uint32_t i, float v, bool in) {
+        scan_span<kRound>(rs, s, lane, [&](uint32_t i, float v, bool in) {
             if (in && v == v && (best.idx == kNone || v > best.val)) best = ArgMax{v, i};
         });
         best = wave_pick(best);
@@ -263,9 +273,9 @@ __global__ __launch_bounds__(256) void k_sample_scan(const float *__restrict__ l
     uint32_t n = 0;
     if constexpr (kOneRound) {
 #pragma unroll
-        for (uint32_t u = 0; u < kRound; ++u) n += static_cast<uint32_t>(__popcll(__ballot(v1[u] >= thr)));
+        for (uint32_t u = 0; u < kOneRoundSteps; ++u) n += static_cast<uint32_t>(__popcll(__ballot(v1[u] >= thr)));
     } else {
-        scan_span(rs, s, lane, [&](uint32_t, float v, bool in) { n += static_cast<uint32_t>(__popcll(__ballot(in && v >= thr))); });
+        scan_span<kRound>(rs, s, lane, [&](uint32_t, float v, bool in) { n += static_cast<uint32_t>(__popcll(__ballot(in && v >= thr))); });
     }
     if (lane == 0) cnt[wave] = n;
     __syncthreads();
@@ -275,7 +285,7 @@ __global__ __launch_bounds__(256) void k_sample_scan(const float *__restrict__ l
     if (pos >= kSampleLocalCap || n == 0) return;
     if constexpr (kOneRound) {
 #pragma unroll
-        for (uint32_t u = 0; u < kRound; ++u) {
+        for (uint32_t u = 0; u < kOneRoundSteps; ++u) {
             const uint64_t mk = __ballot(v1[u] >= thr);
             if (mk != 0) {  // uniform: most steps of a quarter hold no candidate
                 const bool hit = (mk >> lane) & 1ull;
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(256) void k_sample_scan(const float *__restrict__ l
             }
         }
     } else {
-        scan_span(rs, s, lane, [&](uint32_t i, float v, bool in) {
+        scan_span<kRound>(rs, s, lane, [&](uint32_t i, float v, bool in) {
             const bool hit = in && v >= thr;
             const uint64_t m = __ballot(hit);
             const uint32_t r = pos + static_cast<uint32_t>(__popcll(m & below));
@@ -370,7 +380,7 @@ __global__ __launch_bounds__(256) void k_sample_finish(const float *__restrict__
     for (uint32_t todo = rescan; todo != 0; todo &= todo - 1u) {
         const uint32_t c = wave + 4u * static_cast<uint32_t>(__builtin_ctz(todo));
         uint32_t n = 0;
-        scan_span(rs, chunk_span(c), lane, [&](uint32_t, float v, bool in) {
+        scan_span<kOneRoundSteps>(rs, chunk_span(c), lane, [&](uint32_t, float v, bool in) {
             n += static_cast<uint32_t>(__popcll(__ballot(in && v >= thr)));
         });
         if (lane == 0) sc[c] = n;
@@ -408,7 +418,7 @@ __global__ __launch_bounds__(256) void k_sample_finish(const float *__restrict__
         const uint32_t c = wave + 4u * static_cast<uint32_t>(__builtin_ctz(todo));
         uint32_t pos = sc[c];
         if (pos >= cap) continue;
-        scan_span(rs, chunk_span(c), lane, [&](uint32_t i, float v, bool in) {
+        scan_span<kOneRoundSteps>(rs, chunk_span(c), lane, [&](uint32_t i, float v, bool in) {
             const bool hit = in && v >= thr;
             const uint64_t m = __ballot(hit);
             const uint32_t r = pos + static_cast<uint32_t>(__popcll(m & below));
@@ -428,7 +438,7 @@ hipError_t launch_argmax_candidates(const float *logits, uint32_t n_slots, uint3
     const uint32_t chunks = (vocab + chunk - 1) / chunk;
     const SampleWs ws = sample_ws(workspace, n_slots, chunks);
     const dim3 grid(chunks, n_slots), block(256);
-    if (chunk / 4 <= 64 * kRound)
+    if (chunk / 4 <= 64 * kOneRoundSteps)
         hipLaunchKernelGGL(k_sample_scan<true>, grid, block, 0, stream, logits, vocab, chunk, ws);
     else
         hipLaunchKernelGGL(k_sample_scan<false>, grid, block, 0, stream, logits, vocab, chunk, ws);

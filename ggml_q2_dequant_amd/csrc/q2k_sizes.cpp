@@ -15,11 +15,11 @@ constexpr uint64_t align256(uint64_t v) { return (v + 255u) & ~uint64_t{255u}; }
 }  // namespace
 
 uint32_t sample_chunk(uint32_t vocab) {
-    // 256 threads x at least 32 columns each, and at most kSampleMaxChunks
+    // 256 threads x at least 16 columns each, and at most kSampleMaxChunks
     // chunks per slot; a multiple of 256 so each wavefront's quarter is whole
     // 64-column steps.
     uint64_t chunk = (static_cast<uint64_t>(vocab) + kSampleMaxChunks - 1) / kSampleMaxChunks;
-    if (chunk < 8192) chunk = 8192;
+    if (chunk < 4096) chunk = 4096;
     chunk = (chunk + 255) / 256 * 256;
     return static_cast<uint32_t>(chunk);
 }

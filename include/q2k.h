@@ -349,7 +349,7 @@ q2k_status q2k_embedding_gather_async(const void *table, const uint32_t *ids, fl
  *               candidate indices in increasing order; entries past them are
  *               left unwritten.
  * 1 <= vocab <= 2^29. Outputs may not overlap the logits or each other. Uses the stream's
- * workspace (about 530 bytes per 8192 logits; conventions above). Asynchronous on `stream`.
+ * workspace (about 530 bytes per 4096 logits; conventions above). Asynchronous on `stream`.
  */
 q2k_status q2k_argmax_candidates(const float *logits, uint32_t n_slots, uint32_t vocab, uint32_t cap,
                                  uint32_t *top1_idx, float *top1_val, uint32_t *cand_count, uint32_t *overflow,

@@ -70,8 +70,11 @@ def test_page_scale_vocab_with_planted_candidates():
     assert np.all(gc == 9)
 
 
-@pytest.mark.parametrize("n_slots,vocab,cap", [(1, 1, 1), (3, 7, 2), (2, 300, 512), (4, 8192, 5), (2, 8193, 64),
-                                               (3, 65537, 9), (1, 600001, 100)])
+# Chunks are 4096 logits up to a 2^18 vocabulary (one round of 16 steps per wavefront), longer beyond
+# it (rounds of 32 steps, the last one partial).
+@pytest.mark.parametrize("n_slots,vocab,cap", [(1, 1, 1), (3, 7, 2), (2, 300, 512), (4, 4096, 5), (2, 4097, 64),
+                                               (4, 8192, 5), (2, 8193, 64), (3, 65537, 9), (2, 262145, 33),
+                                               (1, 600001, 100)])
 def test_ragged_sizes_and_chunk_edges(n_slots, vocab, cap):
     rng = np.random.Generator(np.random.PCG64(n_slots * 7 + vocab))
     x = (rng.integers(0, 6, (n_slots, vocab)).astype(np.float32) * np.float32(0.25))  # many ties and candidates
@@ -80,11 +83,12 @@ def test_ragged_sizes_and_chunk_edges(n_slots, vocab, cap):
 
 def test_ties_across_chunks_take_the_lowest_index():
     vocab = 3 * 8192 + 17
-    x = np.zeros((2, vocab), np.float32)
+    x = np.zeros((3, vocab), np.float32)
     x[0, [9000, 20000, vocab - 1]] = 1.0
     x[1, [vocab - 1, 5]] = 1.0
-    gi, _ = check(x, 2, vocab, 4)
-    assert gi.tolist() == [9000, 5]
+    x[2, [4096, 4095 + 4096, 4095]] = 1.0  # first and last column of neighbouring 4096-logit chunks
+    gi, _ = check(x, 3, vocab, 4)
+    assert gi.tolist() == [9000, 5, 4095]
 
 
 def test_nan_and_infinity_rows():
