@@ -88,12 +88,15 @@ q2k_status check_matmul(const float *x, const void *w, const float *y, uint32_t 
 // the pinned word instead of synchronizing the stream, which costs several
 // microseconds more per call. Each call tags its marker and its published
 // word with a fresh sequence number, so nothing an earlier call left behind
-// reads as this call's.
+// reads as this call's; the completion kernel also clears the device word. A
+// call that launched the gather but not its completion kernel marks the word
+// for clearing before the next call.
 struct StatusWord {
     int *host = nullptr;      // pinned, mapped, coherent
     int *host_dev = nullptr;  // the same word's device address
-    int *dev = nullptr;       // device memory, zeroed once
+    int *dev = nullptr;       // device memory, zero between calls
     uint32_t seq = 0;
+    bool stale = false;
     std::mutex mu;
 };
 
@@ -696,6 +699,12 @@ q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *o
     s = status_word(&sw);
     if (s != Q2K_OK) return s;
     std::lock_guard<std::mutex> lock(sw->mu);
+    if (sw->stale) {
+        e = hipMemset(sw->dev, 0, sizeof(int));
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) return device_error("q2k_embedding_gather: status word reset", e);
+        sw->stale = false;
+    }
     // Sequence numbers run over 1 .. 2^29 - 1, so (seq << 2) | 3 stays a positive int.
     sw->seq = sw->seq % ((1u << 29) - 1) + 1;
     const int seq = static_cast<int>(sw->seq);
@@ -703,7 +712,10 @@ q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *o
                            sw->dev, seq, st);
     if (e != hipSuccess) return device_error("q2k_embedding_gather launch", e);
     e = q2k::launch_gather_done(sw->dev, seq, sw->host_dev, st);
-    if (e != hipSuccess) return device_error("q2k_embedding_gather launch", e);
+    if (e != hipSuccess) {
+        sw->stale = true;
+        return device_error("q2k_embedding_gather launch", e);
+    }
     // Poll for the published word; past about 2 ms (a stream with other work
     // queued ahead) wait on the stream instead, which also reports any fault.
     const int want = (seq << 2) | 2;

@@ -142,13 +142,16 @@ __global__ __launch_bounds__(256) void k_gather(const uint8_t *__restrict__ tabl
 // ended, and its one store to host-visible memory carries both the call's
 // sequence number and whether that gather saw a bad id (the gather stores the
 // number itself into *status, so a value left by an earlier call never reads
-// as this call's). Folding this into the gather (the last workgroup to finish
-// publishing) costs more: every workgroup then needs an agent-scope release,
-// an L2 write-back, before it counts itself.
-__global__ __launch_bounds__(64) void k_gather_done(const int *__restrict__ status, int seq, int *host_word) {
+// as this call's). It clears *status before that store (release order), so a
+// marker does not outlive its call and cannot meet a reused sequence number
+// after the numbers wrap. Folding this into the gather (the last workgroup
+// to finish publishing) costs more: every workgroup then needs an
+// agent-scope release, an L2 write-back, before it counts itself.
+__global__ __launch_bounds__(64) void k_gather_done(int *__restrict__ status, int seq, int *host_word) {
     if (threadIdx.x != 0) return;
     const int v = __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __hip_atomic_store(host_word, (seq << 2) | 2 | (v == seq ? 1 : 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (v != 0) __hip_atomic_store(status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(host_word, (seq << 2) | 2 | (v == seq ? 1 : 0), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // ---------------------------------------------------------------------------
@@ -1801,7 +1804,7 @@ hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, 
     return hipGetLastError();
 }
 
-hipError_t launch_gather_done(const int *status, int seq, int *host_word, hipStream_t stream) {
+hipError_t launch_gather_done(int *status, int seq, int *host_word, hipStream_t stream) {
     hipLaunchKernelGGL(k_gather_done, dim3(1), dim3(64), 0, stream, status, seq, host_word);
     return hipGetLastError();
 }

@@ -24,10 +24,11 @@ hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, 
                          uint32_t blocks_per_row, uint32_t n_tokens, int *status, int bad_value, hipStream_t stream);
 
 // Queued after launch_gather on the same stream, so it starts once the gather
-// kernel has ended: one thread stores (seq << 2) | 2 | (*status == seq) into
-// *host_word (host-visible memory, system scope), which the host can poll for
-// the end of the gather and its id check.
-hipError_t launch_gather_done(const int *status, int seq, int *host_word, hipStream_t stream);
+// kernel has ended: one thread clears *status and then stores
+// (seq << 2) | 2 | (*status was seq) into *host_word (host-visible memory,
+// system scope, release), which the host can poll for the end of the gather
+// and its id check.
+hipError_t launch_gather_done(int *status, int seq, int *host_word, hipStream_t stream);
 
 // 1 <= M <= 8; batches problems laid out batch-major (x [batches, M, K],
 // w [batches, N, K/256 blocks], y [batches, M, N]), 1 <= batches <= kMaxGridY.

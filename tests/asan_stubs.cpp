@@ -134,9 +134,10 @@ hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, 
     return launched();
 }
 
-hipError_t launch_gather_done(const int *status, int seq, int *host_word, hipStream_t) {
-    // Stands in for the one-thread kernel: publishes the outcome at once.
+hipError_t launch_gather_done(int *status, int seq, int *host_word, hipStream_t) {
+    // Stands in for the one-thread kernel: clears the marker and publishes the outcome at once.
     const int v = __atomic_load_n(status, __ATOMIC_RELAXED);
+    __atomic_store_n(status, 0, __ATOMIC_RELAXED);
     __atomic_store_n(host_word, (seq << 2) | 2 | (v == seq ? 1 : 0), __ATOMIC_RELEASE);
     return launched();
 }
