@@ -208,8 +208,7 @@ struct GemvRoute {
 // Partial sums are reduced over the 4 BW lanes of a row with DPP and over the
 // wavefronts through LDS, in a fixed order: the four segments of a block
 // pairwise, then blocks pairwise up to four, then the four quarters of the
-// chunk left to right. That is the order k_gemv_rows uses, so the two kernels
-// (and both shapes below) give bit-identical rows.
+// chunk left to right, so both shapes below give bit-identical rows.
 //
 // Error bound (first order, u = 2^-24): every term of the result passes
 // through at most 16 roundings in T (the first FMA adds to +0), 4 in the sc
@@ -553,204 +552,6 @@ __global__ __launch_bounds__(64 * 16 / BW) void k_gemv_seg(const float *__restri
         };
         const float v = ((quarter(0) + quarter(1)) + quarter(2)) + quarter(3);
         if (n < N) y[static_cast<uint64_t>(m) * N + n] = v;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// fp32 GEMV for M <= 2 and K <= 4096: persistent wavefronts that stream rows.
-//
-// Lane l of a wavefront owns block l / 4 of a row (K <= 4096 is at most 16
-// blocks) and code segment g = l % 4 of it: the 16 code bytes qs[32h + 16s ..]
-// with h = g / 2, s = g % 2, at all four 2-bit positions p, that is sub-blocks
-// 8h + 2p + s (64 weights). A wavefront therefore covers whole rows and sums
-// each one within itself (DPP), with no barrier between wavefronts. The
-// lane's 64 activations and its four sub-block sums S are the same for every
-// row: they come once from x staged in LDS by the workgroup and stay in
-// registers while the wavefront walks its row groups (kRowsPerGroup rows;
-// group i, i + W, i + 2W, ... for the W wavefronts of the problem), loading
-// the next group's weights while it computes the current one. The host sizes
-// the grid to the workgroups the chip holds at once.
-//
-// Per row the lane adds segment_value, the same arithmetic as k_gemv_seg, and
-// the 64-lane sum follows k_gemv_seg's association (segments pairwise, block
-// pairs, four-block quarters, then the quarters in order), so the two kernels
-// give bit-identical rows and the same error bound, |y - exact| <= 29 u * B
-// (K <= 4096).
-constexpr uint32_t kRowsPerGroup = 4;
-
-template <int M, bool kRouted>
-__global__ __launch_bounds__(256) void k_gemv_rows(const float *__restrict__ x, const uint8_t *__restrict__ w,
-                                                   float *__restrict__ y, uint32_t N, uint32_t K, GemvBatch bt,
-                                                   GemvRoute rt) {
-    constexpr uint32_t R = kRowsPerGroup;
-    // Block b's 256 activations at float 260 b: a 16-byte read by the lanes of all 16 blocks then spreads
-    // over the 16 groups of four banks (256 apart they would all share one group per segment parity).
-    constexpr uint32_t kXB = 260;
-    __shared__ __attribute__((aligned(16))) float xl[M][16 * kXB];
-    // Per wavefront: each lane's partial sums of a group's R rows, lane-major (the row reduction's transpose).
-    static_assert(R == 4, "a lane's group partials are one 16-byte LDS store");
-    __shared__ __attribute__((aligned(16))) float gsum[4][M][64 * R];
-    const uint32_t tid = threadIdx.x, lane = tid & 63u;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if constexpr (kRouted) {
-        static_assert(M == 1, "routes are single activation rows");
-        const uint32_t r = rt.route0 + blockIdx.y;
-        const uint32_t e = rt.ids[r];
-        y += static_cast<uint64_t>(r) * N;
-        if (e >= rt.n_experts) {
-            for (uint32_t n = blockIdx.x * 256u + tid; n < N; n += gridDim.x * 256u) y[n] = __builtin_nanf("");
-            if (blockIdx.x == 0 && tid == 0 && rt.status)
-                __hip_atomic_store(rt.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            return;
-        }
-        x += static_cast<uint64_t>(r / rt.x_div) * K;
-        w += e * rt.expert_stride;
-    } else {
-        x += blockIdx.y * bt.x_elems;
-        w += blockIdx.y * bt.w_bytes;
-        y += blockIdx.y * bt.y_elems;
-    }
-    const uint32_t nb = K >> 8, row_bytes = nb * kBlockBytes;
-    const uint32_t groups = (N + R - 1) / R;
-    const uint32_t b = lane >> 2, g = lane & 3u, h = g >> 1, s = g & 1u;
-    // Lanes past the row's last block aim their loads beyond every descriptor (they read zeros).
-    const uint32_t loff = b < nb ? b * kBlockBytes : 0x80000000u;
-
-    // x of the whole row (16 blocks of 256 floats per activation row, zeros past K) into LDS: each wavefront
-    // copies blocks wave, wave + 4, wave + 8, wave + 12 (one 1 KiB load each), issued before any weight load.
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x + static_cast<uint64_t>(m) * K, K * 4u);
-#pragma unroll
-        for (uint32_t j = 0; j < 4; ++j) {
-            const uint32_t blk = 4u * j + wave;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void *)(xl[m] + kXB * blk),
-                                                     16, static_cast<int>(1024u * blk + 16u * lane), 0, 0, 0);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // Group i holds rows R i .. R i + R - 1; one descriptor spans them (rows past N read zeros).
-    auto load_group = [&](SegLoads (&L)[R], uint32_t grp) __attribute__((always_inline)) {
-        const uint32_t n0 = grp * R;
-        const uint32_t nrows = N - n0 < R ? N - n0 : R;
-        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w + static_cast<uint64_t>(n0) * row_bytes, nrows * row_bytes);
-#pragma unroll
-        for (uint32_t r = 0; r < R; ++r) L[r] = load_seg(rs, r * row_bytes + loff, g, h);
-    };
-
-    const uint32_t W = gridDim.x * 4u;
-    uint32_t grp = blockIdx.x * 4u + wave;
-    SegLoads A[R], B[R];
-    if (grp < groups) load_group(A, grp);
-    __builtin_amdgcn_sched_barrier(0);
-    // Loads complete in issue order: the x copies are in once the group's weight loads alone are in flight.
-    // A plain barrier then (__syncthreads would also wait for those weight loads).
-    if (grp < groups) vm_wait<3 * R>();
-    else vm_wait<0>();
-    asm volatile("s_barrier" ::: "memory");
-
-    // The lane's activations: element i of sub-block p is x[256 b + 128 h + 32 p + 16 s + i].
-    float xv[M][4][16], xs[M][4];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4v v = *reinterpret_cast<const f32x4v *>(xl[m] + kXB * b + 128u * h + 32u * p + 16u * s +
-                                                                  4u * i);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) xv[m][p][4 * i + c] = v[c];
-            }
-            float s2[8], s4[4];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) s2[i] = xv[m][p][2 * i] + xv[m][p][2 * i + 1];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s4[i] = s2[2 * i] + s2[2 * i + 1];
-            xs[m][p] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-        }
-    const uint32_t scsel = 0x06040200u + 0x01010101u * s;
-
-    // Sum of a group's rows over the 64 lanes, in k_gemv_seg's association: per block the four segments
-    // (g0 + g1) + (g2 + g3); per four blocks (two chunked-kernel wavefronts) (b0 + b1) + (b2 + b3); then the
-    // four of those in order, ((G0 + G1) + G2) + G3. The R rows are reduced together: each lane stores its
-    // R partials, then lane l reads the four segments of block l % 16 of row l / 16, so a 16-lane DPP row
-    // holds one row's 16 blocks: two quad steps form the G's, and three row_shr:4 steps limited to one
-    // bank (four lanes) each chain them in order (the disabled lanes add +0; no lane value is -0).
-    // Lanes 15, 31, 47 and 63 end with the totals of rows 0..3.
-    const uint32_t srow = lane >> 4, sblk = lane & 15u;
-    auto group_sums = [&](float (&v)[R][M], float (&out)[M]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-            *reinterpret_cast<f32x4v *>(&gsum[wave][m][R * lane]) = f32x4v{v[0][m], v[1][m], v[2][m], v[3][m]};
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float *src = &gsum[wave][m][R * 4u * sblk + srow];
-            float t = (src[0] + src[R]) + (src[2 * R] + src[3 * R]);
-            t += dpp<kDppQuadXor1>(t);
-            t += dpp<kDppQuadXor2>(t);
-            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x114, 0xF, 0x2, false));
-            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x114, 0xF, 0x4, false));
-            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x114, 0xF, 0x8, false));
-            out[m] = t;
-        }
-    };
-
-    // Row r of a group is computed once its three loads are in. Loads and stores
-    // complete in issue order; the group's own later rows and, when a next
-    // group was requested after it, that group's 3R loads may still be in
-    // flight (stores of the previous group, issued in between, are waited for
-    // too: the count leaves them out, which only waits longer).
-    auto compute_group = [&](const SegLoads (&L)[R], uint32_t gi, auto next_in_flight)
-        __attribute__((always_inline)) {
-        constexpr uint32_t kNext = decltype(next_in_flight)::value ? 3 * R : 0;
-        float tot[R][M];
-#pragma unroll
-        for (uint32_t r = 0; r < R; ++r) {
-            __builtin_amdgcn_sched_barrier(0);
-            vm_wait_n<3 * R + kNext>(3 * (R - 1 - r) + kNext);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int m = 0; m < M; ++m) tot[r][m] = 0.0f;
-            // The row's words enter the arithmetic only here, after its wait: the compiler otherwise hoists
-            // the code masks of both loop branches above the wait and holds them in registers.
-            SegLoads Lr = L[r];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(Lr.q[j]));
-            segment_value<M>(Lr, xv, xs, scsel, tot[r]);
-        }
-        float sum[M];
-        group_sums(tot, sum);
-        const uint32_t n = gi * R + srow;
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-            if (sblk == 15u && n < N) y[static_cast<uint64_t>(m) * N + n] = sum[m];
-    };
-
-    typedef std::integral_constant<bool, true> InFlight;
-    typedef std::integral_constant<bool, false> Drained;
-    while (grp < groups) {
-        const uint32_t g1 = grp + W;
-        if (g1 < groups) {
-            load_group(B, g1);
-            compute_group(A, grp, InFlight{});
-        } else {
-            compute_group(A, grp, Drained{});
-            break;
-        }
-        const uint32_t g2 = g1 + W;
-        if (g2 < groups) {
-            load_group(A, g2);
-            compute_group(B, g1, InFlight{});
-        } else {
-            compute_group(B, g1, Drained{});
-            break;
-        }
-        grp = g2;
     }
 }
 
@@ -1737,45 +1538,9 @@ void launch_seg(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t
                        stream, x, w, y, N, K, bt, rt);
 }
 
-// Workgroups of k_gemv_rows per problem: enough for every wavefront to take at
-// least one row group, at most what the chip holds at once (occupancy times
-// compute units) shared among the problems of the launch. Returns 0 when the
-// launch is too small for every wavefront to stream two or more groups: then
-// the per-wavefront setup (activations, sub-block sums, the workgroup barrier)
-// is not amortized and k_gemv_seg, which splits K over the wavefronts of a
-// workgroup instead, is faster (decode M = 1, N = K = 4096: 4.1 us against
-// 4.7 us; M = 1, N = 65536: 24.4 us against 22.9 us the other way).
-template <int M, bool kRouted>
-uint32_t rows_grid(uint32_t N, uint32_t problems) {
-    static const int per_cu = [] {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(k_gemv_rows<M, kRouted>),
-                                                         256, 0) != hipSuccess || n < 1)
-            n = 1;
-        return n;
-    }();
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || cus < 1)
-        cus = 256;
-    const uint64_t groups = (N + kRowsPerGroup - 1) / kRowsPerGroup;
-    const uint64_t want = (groups + 3) / 4;
-    const uint64_t cap = static_cast<uint64_t>(per_cu) * static_cast<uint64_t>(cus);
-    if (groups * problems < 2 * 4 * cap) return 0;
-    const uint64_t per = cap / problems;
-    const uint64_t g = want < per ? want : per;
-    return static_cast<uint32_t>(g > 0 ? g : 1);
-}
-
 template <int M>
 hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, uint32_t batches,
                            GemvBatch bt, hipStream_t stream) {
-    const uint32_t rg = K <= 4096u ? rows_grid<M, false>(N, batches) : 0;
-    if (rg > 0) {
-        hipLaunchKernelGGL((k_gemv_rows<M, false>), dim3(rg, batches), dim3(256), 0, stream, x, w, y, N, K, bt,
-                           GemvRoute{});
-        return hipGetLastError();
-    }
     if (seg_iters_large<M>(N, batches))
         launch_seg<M, kSegLargeBW, kSegLargeNI<M>, false>(x, w, y, N, K, batches, bt, GemvRoute{}, stream);
     else
@@ -1852,21 +1617,6 @@ hipError_t launch_gemm_mfma(const float *x, const uint8_t *w, float *y, uint32_t
 hipError_t launch_moe_gemv(const float *x, const uint8_t *w, const uint32_t *ids, float *y, uint32_t routes,
                            uint32_t x_div, uint32_t N, uint32_t K, uint32_t n_experts, uint64_t expert_stride,
                            int *status, hipStream_t stream) {
-    if (K <= 4096u && rows_grid<1, true>(N, routes < kMaxGridY ? routes : kMaxGridY) > 0) {
-        for (uint32_t r0 = 0; r0 < routes; r0 += kMaxGridY) {
-            const uint32_t nr = routes - r0 < kMaxGridY ? routes - r0 : kMaxGridY;
-            const uint32_t rg = rows_grid<1, true>(N, nr);
-            const GemvRoute rt{ids, status, expert_stride, r0, x_div, n_experts};
-            if (rg > 0)
-                hipLaunchKernelGGL((k_gemv_rows<1, true>), dim3(rg, nr), dim3(256), 0, stream, x, w, y, N, K,
-                                   GemvBatch{}, rt);
-            else
-                launch_seg<1, kSegSmallBW, kSegSmallNI, true>(x, w, y, N, K, nr, GemvBatch{}, rt, stream);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
-        return hipSuccess;
-    }
     const bool large = seg_iters_large<1>(N, routes);
     for (uint32_t r0 = 0; r0 < routes; r0 += kMaxGridY) {
         const uint32_t nr = routes - r0 < kMaxGridY ? routes - r0 : kMaxGridY;

@@ -315,10 +315,10 @@ def test_gemv_ragged_shapes(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(1, 40001, 1024), (2, 33333, 768), (1, 70003, 4096), (2, 9999, 3840),
                                    (1, 5, 256), (2, 4, 512)])
-def test_gemv_streaming_rows_many_groups_per_wavefront(M, N, K):
-    # M <= 2 with K <= 4096 runs wavefronts that each stream several 4-row groups
-    # (the grid is capped at what the chip holds): large ragged N walks that loop
-    # and its last partial group; K below 4096 leaves lanes without a block.
+def test_gemv_large_ragged_launches(M, N, K):
+    # M <= 2 launches with many rows take the large chunked shape (32 rows per
+    # workgroup for M = 1, 24 for M = 2, in row groups of 4): large ragged N
+    # leaves a partial last workgroup and group; K below 4096 a partial chunk.
     rng = np.random.Generator(np.random.PCG64(M * 7 + N + K))
     blocks = synth.random_blocks(rng, N * K // QK_K)
     x = rng.standard_normal((M, K), dtype=np.float32)
@@ -330,11 +330,12 @@ def test_gemv_streaming_rows_many_groups_per_wavefront(M, N, K):
 
 
 @pytest.mark.parametrize("M", [1, 2])
-def test_gemv_streaming_and_chunked_kernels_agree_bitwise(M):
-    # A large launch streams rows through persistent wavefronts; a 4096-row call
-    # splits K over the wavefronts of a workgroup. Both run the same per-lane
-    # arithmetic and summation order, so the shared rows must match bit for bit
-    # (that is what keeps routed and batched rows equal to single calls).
+def test_gemv_large_and_small_shapes_agree_bitwise(M):
+    # A large launch runs the chunked kernel's large shape (four wavefronts of
+    # four blocks); a 4096-row call the small one (eight wavefronts of two).
+    # Both run the same per-lane arithmetic and summation order, so the shared
+    # rows must match bit for bit (that is what keeps routed and batched rows
+    # equal to single calls).
     N, K, n_small = 40000, 4096, 4096
     rng = np.random.Generator(np.random.PCG64(4200 + M))
     blocks = synth.random_blocks(rng, N * K // QK_K)
