@@ -228,25 +228,25 @@ struct GemvRoute {
 // sooner, with the same activation traffic (M = 1: 3.74 us against 3.87 us).
 // Once a launch has at least two workgroups of the large shape per CU, the
 // memory system is busy anyway and per-lane setup (activations, sub-block
-// sums, reduction) is what to amortize: 4 wavefronts of four blocks and row
-// groups of 4, eight of them (32 rows) for M = 1 and six (24 rows) for M = 2,
-// whose registers would not hold eight (M = 1, N = 16384: 7.6 us against
-// 8.4 us in the small shape's layout). A row's arithmetic does not depend on
-// the shape.
+// sums, reduction) is what to amortize: 4 wavefronts of four blocks and eight
+// row groups of 4 (32 rows; M = 1, N = 16384: 7.5 us against 8.4 us in the
+// small shape's layout). Eight groups measured best for both M (M = 1: 6, 10,
+// 12 and 16 slower by 0-15 %; M = 2: 248 VGPRs, two wavefronts per SIMD, and
+// still 4-7 % faster than six). A row's arithmetic does not depend on the
+// shape.
 constexpr uint32_t kSegSmallBW = 2;
 constexpr int kSegSmallNI = 2;
 constexpr uint32_t kSegLargeBW = 4;
-template <int M>
-constexpr int kSegLargeNI = M == 1 ? 8 : 6;
+constexpr int kSegLargeNI = 8;
 constexpr uint32_t seg_rows(uint32_t bw, int ni) { return 16 / bw * static_cast<uint32_t>(ni); }
 constexpr uint64_t kSegLargeMinWorkgroups = 512;
-static_assert(seg_rows(kSegLargeBW, kSegLargeNI<1>) * (kMaxK / 256) * 84 < (1ull << 31) &&
+static_assert(seg_rows(kSegLargeBW, kSegLargeNI) * (kMaxK / 256) * 84 < (1ull << 31) &&
                   seg_rows(kSegSmallBW, kSegSmallNI) * (kMaxK / 256) * 84 < (1ull << 31),
               "a workgroup's rows fit a 31-bit offset");
 
 template <int M>
 inline bool seg_iters_large(uint32_t N, uint64_t problems) {
-    constexpr uint32_t rows = seg_rows(kSegLargeBW, kSegLargeNI<M>);
+    constexpr uint32_t rows = seg_rows(kSegLargeBW, kSegLargeNI);
     return static_cast<uint64_t>((N + rows - 1) / rows) * problems >= kSegLargeMinWorkgroups;
 }
 
@@ -1542,7 +1542,7 @@ template <int M>
 hipError_t launch_gemv_seg(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t K, uint32_t batches,
                            GemvBatch bt, hipStream_t stream) {
     if (seg_iters_large<M>(N, batches))
-        launch_seg<M, kSegLargeBW, kSegLargeNI<M>, false>(x, w, y, N, K, batches, bt, GemvRoute{}, stream);
+        launch_seg<M, kSegLargeBW, kSegLargeNI, false>(x, w, y, N, K, batches, bt, GemvRoute{}, stream);
     else
         launch_seg<M, kSegSmallBW, kSegSmallNI, false>(x, w, y, N, K, batches, bt, GemvRoute{}, stream);
     return hipGetLastError();
@@ -1622,7 +1622,7 @@ hipError_t launch_moe_gemv(const float *x, const uint8_t *w, const uint32_t *ids
         const uint32_t nr = routes - r0 < kMaxGridY ? routes - r0 : kMaxGridY;
         const GemvRoute rt{ids, status, expert_stride, r0, x_div, n_experts};
         if (large)
-            launch_seg<1, kSegLargeBW, kSegLargeNI<1>, true>(x, w, y, N, K, nr, GemvBatch{}, rt, stream);
+            launch_seg<1, kSegLargeBW, kSegLargeNI, true>(x, w, y, N, K, nr, GemvBatch{}, rt, stream);
         else
             launch_seg<1, kSegSmallBW, kSegSmallNI, true>(x, w, y, N, K, nr, GemvBatch{}, rt, stream);
         const hipError_t e = hipGetLastError();

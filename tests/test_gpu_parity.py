@@ -317,7 +317,7 @@ def test_gemv_ragged_shapes(M, N, K):
                                    (1, 5, 256), (2, 4, 512)])
 def test_gemv_large_ragged_launches(M, N, K):
     # M <= 2 launches with many rows take the large chunked shape (32 rows per
-    # workgroup for M = 1, 24 for M = 2, in row groups of 4): large ragged N
+    # workgroup, in row groups of 4): large ragged N
     # leaves a partial last workgroup and group; K below 4096 a partial chunk.
     rng = np.random.Generator(np.random.PCG64(M * 7 + N + K))
     blocks = synth.random_blocks(rng, N * K // QK_K)
