@@ -226,9 +226,10 @@ struct GemvRoute {
 // blocks per workgroup and two row groups of 8 (16 rows: 256 workgroups, one
 // per CU): twice the wavefronts of the four-block form issue a chunk's loads
 // sooner, with the same activation traffic (M = 1: 3.74 us against 3.87 us).
-// Once a launch has at least two workgroups of the large shape per CU, the
-// memory system is busy anyway and per-lane setup (activations, sub-block
-// sums, reduction) is what to amortize: 4 wavefronts of four blocks and eight
+// Once a launch would need more than about one and a half rounds of the
+// small shape's resident workgroups (seg_iters_large), the memory system is busy
+// anyway and per-lane setup (activations, sub-block sums, reduction) is what
+// to amortize: 4 wavefronts of four blocks and eight
 // row groups of 4 (32 rows; M = 1, N = 16384: 7.5 us against 8.4 us in the
 // small shape's layout). Eight groups measured best for both M (M = 1: 6, 10,
 // 12 and 16 slower by 0-15 %; M = 2: 248 VGPRs, two wavefronts per SIMD, and
@@ -239,16 +240,9 @@ constexpr int kSegSmallNI = 2;
 constexpr uint32_t kSegLargeBW = 4;
 constexpr int kSegLargeNI = 8;
 constexpr uint32_t seg_rows(uint32_t bw, int ni) { return 16 / bw * static_cast<uint32_t>(ni); }
-constexpr uint64_t kSegLargeMinWorkgroups = 512;
 static_assert(seg_rows(kSegLargeBW, kSegLargeNI) * (kMaxK / 256) * 84 < (1ull << 31) &&
                   seg_rows(kSegSmallBW, kSegSmallNI) * (kMaxK / 256) * 84 < (1ull << 31),
               "a workgroup's rows fit a 31-bit offset");
-
-template <int M>
-inline bool seg_iters_large(uint32_t N, uint64_t problems) {
-    constexpr uint32_t rows = seg_rows(kSegLargeBW, kSegLargeNI);
-    return static_cast<uint64_t>((N + rows - 1) / rows) * problems >= kSegLargeMinWorkgroups;
-}
 
 // Bytes 0, 1 (W = false) or 2, 3 (W = true) of v, each below 16, as exact integers.
 template <bool W>
@@ -1536,6 +1530,33 @@ void launch_seg(const float *x, const uint8_t *w, float *y, uint32_t N, uint32_t
     constexpr uint32_t rows = seg_rows(BW, NI);
     hipLaunchKernelGGL((k_gemv_seg<M, BW, NI, kRouted>), dim3((N + rows - 1) / rows, problems), dim3(64 * 16 / BW), 0,
                        stream, x, w, y, N, K, bt, rt);
+}
+
+// The large shape takes a launch once the small one would need more than one
+// and a half rounds of workgroups on the chip for M = 1, more than one round
+// for M = 2 (a round: the small shape's resident workgroups per CU, two for
+// M = 1 and one for M = 2 at 113 and 186 VGPRs, times the CUs). Measured on
+// one box, small against large shape (K = 4096 unless noted): M = 1 N = 8192
+// 4.85 / 5.38 us, N = 12288 (1.5 rounds) 6.64 / 7.21, N = 14336 7.97 / 7.28,
+// K = 8192 N = 8192 7.86 / 8.79, K = 2048 N = 14336 7.40 / 6.75, 3 x N = 4096
+// 6.59 / 7.21; M = 2 N = 4096 (one round) 4.71 / 6.90, N = 6144 7.43 / 7.07,
+// N = 8192 7.75 / 7.25, 2 x N = 4096 7.74 / 7.28.
+template <int M>
+bool seg_iters_large(uint32_t N, uint64_t problems) {
+    static const uint64_t resident = [] {
+        int n = 0, dev = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &n, reinterpret_cast<const void *>(k_gemv_seg<M, kSegSmallBW, kSegSmallNI, false>),
+                64 * 16 / kSegSmallBW, 0) != hipSuccess || n < 1)
+            n = 1;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+        return static_cast<uint64_t>(n) * static_cast<uint64_t>(cus);
+    }();
+    constexpr uint32_t rows = seg_rows(kSegSmallBW, kSegSmallNI);
+    const uint64_t wgs = static_cast<uint64_t>((N + rows - 1) / rows) * problems;
+    return M == 1 ? 2 * wgs > 3 * resident : wgs > resident;
 }
 
 template <int M>
