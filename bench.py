@@ -67,7 +67,7 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 TRAFFIC_ROWS = {
     "k_gemv_m1": ("gemv1", "k_gemv_seg<1", 5537792),
     "k_dequantize": ("dequant", "k_dequantize", 65536 * 84 + 65536 * 1024),
-    "k_gather": ("gather", "k_gather", 9078784),
+    "k_gather": ("gather", "k_gather(", 9078784),  # not k_gather_done
     "k_gemv_m8": ("gemv8", "k_gemv_mfma", 19857408),
 }
 ROWS = ("gemv1", "dequant", "gather", "gemv1_wide", "gemv8", "mfma", "mfma_context", "batched", "sample",
