@@ -7,6 +7,8 @@
   a graph captured with an M > 8 call still replays correctly after an eager call
   with a larger M on the same stream (the buffer it captured was retired, not freed).
 * Growth during capture is refused with an error and enqueues nothing.
+* The synchronous gather (it waits on the host) is refused during capture; the
+  asynchronous gather captures and replays.
 The page behind the pooled forms is the docs.rs source page of mlx-native 0.10.8,
 tests/deepseek_q2_k.rs (caller-held IdMmScratch for the pooled expert-routed calls)
 and the op helpers of mlx-native 0.21.1, src/ops/dflash2_selector.rs (caller-owned,
@@ -156,4 +158,36 @@ def test_workspace_growth_is_refused_during_capture():
         g2.replay()
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int32), want.view(torch.int32))
+    del g, g2
+
+
+def test_synchronous_gather_is_refused_during_capture_and_the_asynchronous_one_replays():
+    # The synchronous gather waits on the host for its kernel, which a capture
+    # cannot hold: it must be refused before anything is enqueued. The
+    # asynchronous form captures; every replay must match the eager result.
+    vocab, dim = 3, QK_K
+    table_h = np.concatenate([synth.page_block(r + 2) for r in range(vocab)])
+    table, ids = dev(table_h), dev(np.array([2, 0, 1, 2], dtype=np.uint32))
+    want = oracle.gather(table_h, [2, 0, 1, 2], vocab, dim, 4)
+    out = torch.full((4, dim), float("nan"), device="cuda:0")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with pytest.raises(q2k.Q2KInvalidArgument, match="cannot be captured"):
+            with torch.cuda.graph(g, stream=s):
+                q2k.q2k_embedding_gather(table, ids, out, vocab, dim, 4, stream=s)
+        torch.cuda.synchronize()
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2, stream=s):
+            q2k.q2k_embedding_gather_async(table, ids, out, vocab, dim, 4, status, stream=s)
+        for r in range(3):
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g2.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32)), "replay %d differs" % r
+            assert int(status.item()) == 0
+            q2k.q2k_embedding_gather(table, ids, out, vocab, dim, 4, stream=s)   # eager work between replays
+            torch.cuda.synchronize()
     del g, g2
