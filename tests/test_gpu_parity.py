@@ -314,7 +314,7 @@ def test_gemv_ragged_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 40001, 1024), (2, 33333, 768), (1, 70003, 4096), (2, 9999, 3840),
-                                   (1, 5, 256), (2, 4, 512)])
+                                   (1, 5, 256), (2, 4, 512), (1, 14336, 4096), (2, 16384, 4096), (2, 6144, 4096)])
 def test_gemv_large_ragged_launches(M, N, K):
     # M <= 2 launches with many rows take the large chunked shape (32 rows per
     # workgroup, in row groups of 4): large ragged N
@@ -443,8 +443,10 @@ def test_batched_page_fixture_equals_independent_calls_bytewise():
         assert np.all(np.abs(yb[b] - oracle.matmul_f32seq(x[b], blocks[b * per:(b + 1) * per], 1, n, QK_K)) <= 2e-4)
 
 
+# The last two stacks are large enough for the large chunked shape, while each single call runs the small
+# one: the batched rows must still equal the single calls bit for bit.
 @pytest.mark.parametrize("batches,M,N,K", [(2, 1, 130, 768), (5, 2, 33, 256), (3, 3, 70, 1280), (4, 8, 257, 512),
-                                           (1, 5, 4097, 256), (6, 7, 9, 4352)])
+                                           (1, 5, 4097, 256), (6, 7, 9, 4352), (8, 1, 4096, 512), (4, 2, 2048, 512)])
 def test_batched_equals_independent_calls_and_oracle(batches, M, N, K):
     rng = np.random.Generator(np.random.PCG64(batches * 100003 + M * 1009 + N * 31 + K))
     blocks = synth.random_blocks(rng, batches * N * K // QK_K)
