@@ -700,7 +700,9 @@ q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *o
     if (s != Q2K_OK) return s;
     std::lock_guard<std::mutex> lock(sw->mu);
     if (sw->stale) {
-        e = hipMemset(sw->dev, 0, sizeof(int));
+        // A gather launched by the failed call may still be running (on any stream): let it end first.
+        e = hipDeviceSynchronize();
+        if (e == hipSuccess) e = hipMemset(sw->dev, 0, sizeof(int));
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) return device_error("q2k_embedding_gather: status word reset", e);
         sw->stale = false;
@@ -729,8 +731,10 @@ q2k_status q2k_embedding_gather(const void *table, const uint32_t *ids, float *o
                 e = hipStreamSynchronize(st);
                 if (e != hipSuccess) return device_error("q2k_embedding_gather sync", e);
                 v = __atomic_load_n(sw->host, __ATOMIC_ACQUIRE);
-                if ((v & ~1) != want)
+                if ((v & ~1) != want) {
+                    sw->stale = true;
                     return fail(Q2K_ERR_DEVICE, "q2k_embedding_gather: the completion word was not published");
+                }
                 break;
             }
         }

@@ -25,6 +25,7 @@
 
 extern "C" {
 void stub_set_capturing(int on);
+void stub_fail_gather_done(int on);
 unsigned long long stub_launches(void);
 unsigned long long stub_mallocs(void);
 }
@@ -126,6 +127,17 @@ void dequant_and_gather_cases() {
     ids.as<uint32_t>()[3] = 0;
     EXPECT(q2k_embedding_gather(table.p, ids.as<uint32_t>(), emb.as<float>(), vocab, dim, nt, stream(1)) == Q2K_OK,
            "gather after a failed call starts from a clear status word");
+    // A failed completion launch after a gather that saw a bad id: the next call clears the status word
+    // first and succeeds.
+    ids.as<uint32_t>()[2] = vocab + 5;
+    stub_fail_gather_done(1);
+    EXPECT(q2k_embedding_gather(table.p, ids.as<uint32_t>(), emb.as<float>(), vocab, dim, nt, stream(1)) ==
+               Q2K_ERR_DEVICE,
+           "gather whose completion launch fails");
+    stub_fail_gather_done(0);
+    ids.as<uint32_t>()[2] = 1;
+    EXPECT(q2k_embedding_gather(table.p, ids.as<uint32_t>(), emb.as<float>(), vocab, dim, nt, stream(1)) == Q2K_OK,
+           "gather after a failed completion launch");
     ids.as<uint32_t>()[0] = 0xFFFFFFFFu;
     EXPECT(q2k_embedding_gather_async(table.p, ids.as<uint32_t>(), emb.as<float>(), vocab, dim, nt,
                                       status.as<int>(), stream(1)) == Q2K_OK &&

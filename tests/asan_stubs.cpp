@@ -14,6 +14,7 @@
 //
 // Also exported for drivers (extern "C"):
 //   stub_set_capturing(int)   makes hipStreamIsCapturing report an active capture
+//   stub_fail_gather_done(int) makes the gather's completion launch fail
 //   stub_launches()           number of launch stubs run so far
 //   stub_mallocs()            number of hipMalloc calls so far
 #include <hip/hip_runtime_api.h>
@@ -29,6 +30,7 @@
 namespace {
 
 std::atomic<int> g_capturing{0};
+std::atomic<int> g_fail_done{0};
 std::atomic<unsigned long long> g_launches{0};
 std::atomic<unsigned long long> g_mallocs{0};
 
@@ -58,6 +60,7 @@ hipError_t launched() {
 extern "C" {
 
 void stub_set_capturing(int on) { g_capturing = on; }
+void stub_fail_gather_done(int on) { g_fail_done = on; }
 unsigned long long stub_launches(void) { return g_launches; }
 unsigned long long stub_mallocs(void) { return g_mallocs; }
 
@@ -135,6 +138,7 @@ hipError_t launch_gather(const uint8_t *table, const uint32_t *ids, float *out, 
 }
 
 hipError_t launch_gather_done(int *status, int seq, int *host_word, hipStream_t) {
+    if (g_fail_done) return hipErrorLaunchFailure;
     // Stands in for the one-thread kernel: clears the marker and publishes the outcome at once.
     const int v = __atomic_load_n(status, __ATOMIC_RELAXED);
     __atomic_store_n(status, 0, __ATOMIC_RELAXED);
