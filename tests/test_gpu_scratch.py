@@ -176,6 +176,7 @@ def test_synchronous_gather_is_refused_during_capture_and_the_asynchronous_one_r
     with torch.cuda.stream(s):
         with pytest.raises(q2k.Q2KInvalidArgument, match="cannot be captured"):
             with torch.cuda.graph(g, stream=s):
+                out.fill_(0.0)   # something captured besides the refused call
                 q2k.q2k_embedding_gather(table, ids, out, vocab, dim, 4, stream=s)
         torch.cuda.synchronize()
         g2 = torch.cuda.CUDAGraph()
