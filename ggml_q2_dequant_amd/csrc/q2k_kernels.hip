@@ -105,12 +105,13 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
 }
 
 // Embedding gather: wavefront u takes run u % runs of token u / runs, where a
-// row of blocks_per_row blocks splits into runs = ceil(blocks_per_row / 4)
-// runs of 4 blocks. A gather moves few bytes per row, so shorter runs keep
-// more wavefronts busy (512 rows of 16 blocks: 4.5 us with 4-block runs,
-// 5.3 us with 64-block runs). A token whose id is >= vocab raises the status
-// word and its row is neither read nor written.
-constexpr uint32_t kGatherRun = 4;
+// row of blocks_per_row blocks splits into runs = ceil(blocks_per_row / 2)
+// runs of 2 blocks. A gather moves few bytes per row, so short runs keep more
+// wavefronts busy (512 rows of 16 blocks, back to back: 3.68 us with 2-block
+// runs, 3.76 us with 4, 3.85 us with 1, 3.88 us with 8; 5.3 us with 64 in an
+// earlier form). A token whose id is >= vocab raises the status word and its
+// row is neither read nor written.
+constexpr uint32_t kGatherRun = 2;
 constexpr uint32_t kGatherDwords = (kGatherRun * kBlockBytes / 4 + kWave - 1) / kWave * kWave;
 
 __global__ __launch_bounds__(256) void k_gather(const uint8_t *__restrict__ table, const uint32_t *__restrict__ ids,
